@@ -1,0 +1,24 @@
+"""Seeded synthetic inputs for paged KV-cache attention.
+
+Shared by the CPU oracle's tests, the GPU parity tests and the benchmark. It
+draws values, assigns physical blocks to sequences and lays the drawn tokens
+into a block pool. It holds no attention arithmetic.
+"""
+
+from .synth import (  # noqa: F401
+    POISON_F16,
+    PagedInputs,
+    build,
+    config1,
+    config1_full_append,
+    config2,
+    config3,
+    config4,
+    config5,
+    decode_case,
+    mixed_case,
+    prefix_shared_case,
+    repermute,
+    unshare_prefix,
+    CONFIGS,
+)
