@@ -1,0 +1,203 @@
+/*
+ * pagedkv.h - C ABI of the paged KV-cache attention library (MI355X, gfx950).
+ *
+ * The KV cache of one attention layer is a pool of fixed-size blocks,
+ *
+ *     kv_pool[num_blocks][block_size][2][num_kv_heads][head_size]   (fp16)
+ *
+ * the per-layer pool tensor of the page "vLLM 部署深度指南" (section
+ * "PagedAttention 原理", code listing of the simplified KV-cache class).
+ * Index 0 of the axis of size 2 holds keys, index 1 values; under
+ * grouped-query attention the head axis counts KV heads. A block holds 16
+ * tokens (same page, "PagedAttention 方案" and the --block-size default in the
+ * launch-flag table). Sequence b reaches its tokens through row b of
+ * block_tables: logical block j of the sequence lives in physical block
+ * block_tables[b * max_blocks_per_seq + j], so logical position t is slot
+ * block_tables[b][t / 16] * 16 + t % 16 (page "vLLM GitHub 项目 …", section 二,
+ * items 1 and 4: blocks need not be contiguous and may be shared).
+ *
+ * Conventions for every entry point below:
+ *  - Pointers named as device pointers must point to device memory the caller
+ *    owns and keeps alive until the work on `stream` is done. The library
+ *    allocates no memory and keeps no state except a per-thread message of the
+ *    last HIP error (pa_last_error).
+ *  - `stream` is a hipStream_t passed as void*; NULL is the null stream. Every
+ *    device operation is asynchronous and ordered on `stream`; nothing waits
+ *    for the device.
+ *  - All tensors are dense, row-major, in the element types stated. fp16 is
+ *    IEEE binary16; fp32 is IEEE binary32.
+ *  - A status other than PA_OK means nothing was launched. Scalar arguments
+ *    are checked on the host before any launch. Device-resident contents
+ *    (lengths, table entries, slots) are checked by the kernels where a bad
+ *    value would address memory outside the pool or the tables: such a row's
+ *    output is set to NaN (decode, prefill) or the token is skipped (append).
+ *  - Sizes the device work depends on (max_context_len, max_q_len) are host
+ *    scalars, so no call ever reads device memory from the host.
+ */
+#ifndef PAGEDKV_H
+#define PAGEDKV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  PA_OK = 0,
+  PA_ERR_INVALID = 1,     /* null pointer, non-positive count, inconsistent sizes      */
+  PA_ERR_UNSUPPORTED = 2, /* valid request with no kernel here: block_size != 16,
+                             head_size not in {64, 128}, group size not in {1,2,4,8}  */
+  PA_ERR_WORKSPACE = 3,   /* workspace smaller than pa_decode_workspace_bytes         */
+  PA_ERR_HIP = 4          /* the HIP runtime refused a launch; see pa_last_error       */
+} pa_status;
+
+/* Static text for a status code. Never NULL. */
+const char* pa_status_string(int status);
+/* Text of the last HIP error seen on this thread ("" if none). Never NULL. */
+const char* pa_last_error(void);
+/* ABI version, currently 1. */
+int32_t pa_abi_version(void);
+
+/* ---------------------------------------------------------------------------
+ * Layout helpers: pure host arithmetic, no device access. A negative return
+ * value means an argument was out of range.
+ * ------------------------------------------------------------------------- */
+
+/* Blocks held by a sequence of `len` tokens: ceil(len / block_size)
+ * ("allocate" in the KV-cache listing on page "vLLM 部署深度指南"). */
+int64_t pa_blocks_for_len(int64_t len, int32_t block_size);
+
+/* Bytes of one block: block_size * 2 * num_kv_heads * head_size * elem_bytes. */
+int64_t pa_block_bytes(int32_t block_size, int32_t num_kv_heads, int32_t head_size,
+                       int32_t elem_bytes);
+
+/* Bytes of a pool of num_blocks blocks. */
+int64_t pa_pool_bytes(int64_t num_blocks, int32_t block_size, int32_t num_kv_heads,
+                      int32_t head_size, int32_t elem_bytes);
+
+/* Blocks that fit in floor(free_bytes * utilization) bytes; the sizing rule of
+ * the --gpu-memory-utilization flag (default 0.9) on page "vLLM 部署深度指南".
+ * utilization must lie in (0, 1]. */
+int64_t pa_num_blocks_fit(int64_t free_bytes, double utilization, int32_t block_size,
+                          int32_t num_kv_heads, int32_t head_size, int32_t elem_bytes);
+
+/* Slot of logical position `pos` of a sequence whose block-table row (host
+ * memory, at least pos / block_size + 1 entries) is `block_table_row`. */
+int64_t pa_slot(const int32_t* block_table_row, int64_t pos, int32_t block_size);
+
+/* Element offset in the pool of (slot, kv, head, dim); kv 0 = key, 1 = value. */
+int64_t pa_kv_elem_offset(int64_t slot, int32_t kv, int32_t head, int32_t dim,
+                          int32_t num_kv_heads, int32_t head_size);
+
+/* Partitions of a context of max_context_len tokens: ceil(len / partition_size),
+ * at least 1. */
+int32_t pa_num_partitions(int32_t max_context_len, int32_t partition_size);
+
+/* Workspace bytes pa_decode needs: 0 when one partition covers max_context_len,
+ * else num_seqs * num_q_heads * partitions * (head_size + 2) * 4, rounded up to 256. */
+int64_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads,
+                                  int32_t max_context_len, int32_t partition_size,
+                                  int32_t head_size);
+
+/* ---------------------------------------------------------------------------
+ * Device operations.
+ * ------------------------------------------------------------------------- */
+
+/* Write this step's new tokens into their slots (``append_kv`` of the listing on
+ * page "vLLM 部署深度指南": new K/V go into the sequence's physical block, which
+ * need not be contiguous with the others).
+ *
+ *   kv_pool      device fp16 [num_blocks][block_size][2][num_kv_heads][head_size], written
+ *   key, value   device fp16, token t's row at key + t * key_token_stride (elements),
+ *                num_kv_heads * head_size contiguous elements per row; a stride of 0
+ *                means num_kv_heads * head_size
+ *   slot_mapping device int64 [num_tokens]: token t goes to slot slot_mapping[t]
+ *                (block * block_size + offset). A negative slot skips the token, and so
+ *                does a slot >= num_blocks * block_size. Slots must be distinct; with
+ *                duplicates the surviving value is unspecified.
+ * Copies bits: the pool afterwards holds exactly the given fp16 values. */
+pa_status pa_kv_append(void* kv_pool, const void* key, const void* value,
+                       const int64_t* slot_mapping, int32_t num_tokens, int32_t num_kv_heads,
+                       int32_t head_size, int32_t block_size, int64_t num_blocks,
+                       int64_t key_token_stride, int64_t value_token_stride, void* stream);
+
+/* One decode step of paged attention: query row b (one token per sequence, at the
+ * sequence's last position) attends to the first context_lens[b] tokens of
+ * sequence b, the token appended this step included.
+ *
+ *   out           device fp16 [num_seqs][num_q_heads][head_size], written
+ *   q             device fp16 [num_seqs][num_q_heads][head_size]
+ *   kv_pool       device fp16 pool (layout above), read
+ *   block_tables  device int32 [num_seqs][max_blocks_per_seq], entries in [0, num_blocks)
+ *                 for the first ceil(context_lens[b] / block_size) of row b; the rest
+ *                 are never read
+ *   context_lens  device int32 [num_seqs], each in [0, max_context_len] and at most
+ *                 max_blocks_per_seq * block_size. A length of 0 gives a zero row; a
+ *                 length outside these bounds, or a table entry outside
+ *                 [0, num_blocks), gives a NaN row.
+ *   scale         softmax scale, normally 1 / sqrt(head_size)
+ *   partition_size  tokens per split-context partition, a positive multiple of
+ *                 block_size; a context longer than one partition is computed as
+ *                 partitions merged by a log-sum-exp reduction
+ *   workspace     device memory of at least pa_decode_workspace_bytes(...) bytes,
+ *                 256-byte aligned (may be NULL when that size is 0); scratch only
+ * Query head h reads KV head h / (num_q_heads / num_kv_heads). Arithmetic: fp16
+ * inputs, fp32 products, sums and softmax, fp16 output rounded to nearest even. */
+pa_status pa_decode(void* out, const void* q, const void* kv_pool, const int32_t* block_tables,
+                    const int32_t* context_lens, int32_t num_seqs, int32_t num_q_heads,
+                    int32_t num_kv_heads, int32_t head_size, int32_t block_size,
+                    int32_t max_blocks_per_seq, int64_t num_blocks, int32_t max_context_len,
+                    float scale, int32_t partition_size, void* workspace,
+                    int64_t workspace_bytes, void* stream);
+
+/* Causal attention of prefill chunks over their paged context (the scheduler on
+ * page "vLLM 部署深度指南" puts prefills and decodes into one step). Request r owns
+ * query rows [query_start_loc[r], query_start_loc[r+1]) and seq_lens[r] tokens in
+ * the pool, its own chunk already appended, so P = seq_lens[r] - chunk length
+ * tokens come before the chunk; chunk row i sits at position P + i and sees
+ * positions 0 .. P + i.
+ *
+ *   out              device fp16 [total_q][num_q_heads][head_size], written
+ *   q                device fp16 [total_q][num_q_heads][head_size]
+ *   block_tables     device int32 [num_reqs][max_blocks_per_seq]
+ *   query_start_loc  device int32 [num_reqs + 1], non-decreasing, starts at 0, ends at
+ *                    total_q; each chunk at most max_q_len rows
+ *   seq_lens         device int32 [num_reqs], chunk length <= seq_lens[r] <= max_seq_len
+ *                    and <= max_blocks_per_seq * block_size; rows of a request that breaks
+ *                    these bounds, or whose table holds an entry outside [0, num_blocks),
+ *                    are set to NaN
+ * Arithmetic: fp16 inputs on the matrix cores with fp32 accumulation, fp32 softmax,
+ * fp16 output rounded to nearest even. */
+pa_status pa_prefill_chunk(void* out, const void* q, const void* kv_pool,
+                           const int32_t* block_tables, const int32_t* query_start_loc,
+                           const int32_t* seq_lens, int32_t num_reqs, int32_t total_q,
+                           int32_t max_q_len, int32_t max_seq_len, int32_t num_q_heads,
+                           int32_t num_kv_heads, int32_t head_size, int32_t block_size,
+                           int32_t max_blocks_per_seq, int64_t num_blocks, float scale,
+                           void* stream);
+
+/* Copy one sequence's keys and values, in logical order, out of the pool: the
+ * block-table indexing of the attention kernels, made visible bit for bit.
+ *
+ *   k_out, v_out     device fp16 [len][num_kv_heads][head_size], written
+ *   block_table_row  device int32 [ceil(len / block_size)]; an entry outside
+ *                    [0, num_blocks) leaves its tokens' rows unwritten */
+pa_status pa_gather_kv(void* k_out, void* v_out, const void* kv_pool,
+                       const int32_t* block_table_row, int32_t len, int32_t num_kv_heads,
+                       int32_t head_size, int32_t block_size, int64_t num_blocks,
+                       void* stream);
+
+/* Read `bytes` bytes (a multiple of 16) of device memory once, as a plain HBM
+ * read stream, and write one fp32 per workgroup to `sink` (device,
+ * at least pa_stream_read_sink_len(bytes) floats) so the reads are not dropped.
+ * A measurement aid: its rate is the read bandwidth the box reaches. */
+pa_status pa_stream_read(const void* buf, int64_t bytes, float* sink, void* stream);
+int64_t pa_stream_read_sink_len(int64_t bytes);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PAGEDKV_H */

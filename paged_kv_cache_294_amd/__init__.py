@@ -1,0 +1,35 @@
+"""Paged KV-cache attention for MI355X (gfx950): a C-ABI HIP library and its Python binding.
+
+The library (``libpagedkv.so``, declared in ``include/pagedkv.h``) holds the kernels:
+``pa_kv_append`` (scatter of new tokens into pool slots), ``pa_decode`` (split-context
+paged decode with a log-sum-exp merge), ``pa_prefill_chunk`` (causal chunked prefill on
+the matrix cores), ``pa_gather_kv`` and the pool-layout helpers. The functions below
+only marshal torch tensors into the C calls.
+"""
+
+from ._lib import (  # noqa: F401
+    LIB_PATH,
+    SIGNATURES,
+    PagedKVError,
+    load,
+    pa_abi_version,
+    pa_block_bytes,
+    pa_blocks_for_len,
+    pa_decode,
+    pa_decode_workspace_bytes,
+    pa_gather_kv,
+    pa_kv_append,
+    pa_kv_elem_offset,
+    pa_num_blocks_fit,
+    pa_num_partitions,
+    pa_pool_bytes,
+    pa_prefill_chunk,
+    pa_slot,
+    pa_stream_read,
+    pa_stream_read_sink_len,
+    PA_OK,
+    PA_ERR_INVALID,
+    PA_ERR_UNSUPPORTED,
+    PA_ERR_WORKSPACE,
+    PA_ERR_HIP,
+)

@@ -1,0 +1,257 @@
+"""ctypes binding of ``libpagedkv.so``: argument marshalling only.
+
+Every function has the name of the C entry point it calls (``include/pagedkv.h``).
+Device tensors are torch tensors (device memory and streams come from PyTorch); their
+data pointers and shapes are passed through unchanged and all computation happens in
+the library's HIP kernels. A non-zero status raises :class:`PagedKVError`. The library
+must be built (``python -m paged_kv_cache_294_amd.build``); there is no fallback.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libpagedkv.so")
+
+PA_OK, PA_ERR_INVALID, PA_ERR_UNSUPPORTED, PA_ERR_WORKSPACE, PA_ERR_HIP = range(5)
+
+_i32, _i64, _f32, _f64, _vp = ctypes.c_int32, ctypes.c_int64, ctypes.c_float, ctypes.c_double, ctypes.c_void_p
+
+# name -> (restype, argtypes), mirroring include/pagedkv.h
+SIGNATURES = {
+    "pa_status_string": (ctypes.c_char_p, [ctypes.c_int]),
+    "pa_last_error": (ctypes.c_char_p, []),
+    "pa_abi_version": (_i32, []),
+    "pa_blocks_for_len": (_i64, [_i64, _i32]),
+    "pa_block_bytes": (_i64, [_i32, _i32, _i32, _i32]),
+    "pa_pool_bytes": (_i64, [_i64, _i32, _i32, _i32, _i32]),
+    "pa_num_blocks_fit": (_i64, [_i64, _f64, _i32, _i32, _i32, _i32]),
+    "pa_slot": (_i64, [ctypes.POINTER(_i32), _i64, _i32]),
+    "pa_kv_elem_offset": (_i64, [_i64, _i32, _i32, _i32, _i32, _i32]),
+    "pa_num_partitions": (_i32, [_i32, _i32]),
+    "pa_decode_workspace_bytes": (_i64, [_i32, _i32, _i32, _i32, _i32]),
+    "pa_kv_append": (ctypes.c_int, [_vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i64, _i64, _i64, _vp]),
+    "pa_decode": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _i64,
+                                 _i32, _f32, _i32, _vp, _i64, _vp]),
+    "pa_prefill_chunk": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32,
+                                        _i32, _i32, _i32, _i32, _i64, _f32, _vp]),
+    "pa_gather_kv": (ctypes.c_int, [_vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i64, _vp]),
+    "pa_stream_read": (ctypes.c_int, [_vp, _i64, _vp, _vp]),
+    "pa_stream_read_sink_len": (_i64, [_i64]),
+}
+
+
+class PagedKVError(RuntimeError):
+    def __init__(self, fn, status):
+        lib = load()
+        msg = lib.pa_status_string(status).decode()
+        detail = lib.pa_last_error().decode() if status == PA_ERR_HIP else ""
+        super().__init__(f"{fn}: {msg}" + (f" ({detail})" if detail else ""))
+        self.status = status
+
+
+_LIB = None
+
+
+def load() -> ctypes.CDLL:
+    """Load the library once; raise if it has not been built."""
+    global _LIB
+    if _LIB is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(
+                f"{LIB_PATH} is missing: build it with `python -m paged_kv_cache_294_amd.build`")
+        lib = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in SIGNATURES.items():
+            fn = getattr(lib, name)
+            fn.restype, fn.argtypes = res, args
+        _LIB = lib
+    return _LIB
+
+
+def _check(fn, status):
+    if status != PA_OK:
+        raise PagedKVError(fn, status)
+
+
+def _stream(stream):
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def _dev(t, name, dtype):
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise TypeError(f"{name} must be a device tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    return t.data_ptr()
+
+
+def _dense(t, name, dtype):
+    ptr = _dev(t, name, dtype)
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return ptr
+
+
+def _pool_geometry(kv_pool):
+    if kv_pool.dim() != 5 or kv_pool.shape[2] != 2:
+        raise ValueError("kv_pool must be [num_blocks, block_size, 2, num_kv_heads, head_size]")
+    nb, bs, _, hkv, d = kv_pool.shape
+    return int(nb), int(bs), int(hkv), int(d)
+
+
+# ---------------------------------------------------------------------------------------
+# layout helpers
+# ---------------------------------------------------------------------------------------
+
+def pa_abi_version() -> int:
+    return load().pa_abi_version()
+
+
+def pa_blocks_for_len(length: int, block_size: int = 16) -> int:
+    return load().pa_blocks_for_len(length, block_size)
+
+
+def pa_block_bytes(block_size: int, num_kv_heads: int, head_size: int, elem_bytes: int = 2) -> int:
+    return load().pa_block_bytes(block_size, num_kv_heads, head_size, elem_bytes)
+
+
+def pa_pool_bytes(num_blocks: int, block_size: int, num_kv_heads: int, head_size: int,
+                  elem_bytes: int = 2) -> int:
+    return load().pa_pool_bytes(num_blocks, block_size, num_kv_heads, head_size, elem_bytes)
+
+
+def pa_num_blocks_fit(free_bytes: int, utilization: float, block_size: int, num_kv_heads: int,
+                      head_size: int, elem_bytes: int = 2) -> int:
+    return load().pa_num_blocks_fit(free_bytes, utilization, block_size, num_kv_heads, head_size,
+                                    elem_bytes)
+
+
+def pa_slot(block_table_row, pos: int, block_size: int = 16) -> int:
+    arr = (_i32 * len(block_table_row))(*[int(x) for x in block_table_row])
+    return load().pa_slot(arr, pos, block_size)
+
+
+def pa_kv_elem_offset(slot: int, kv: int, head: int, dim: int, num_kv_heads: int,
+                      head_size: int) -> int:
+    return load().pa_kv_elem_offset(slot, kv, head, dim, num_kv_heads, head_size)
+
+
+def pa_num_partitions(max_context_len: int, partition_size: int) -> int:
+    return load().pa_num_partitions(max_context_len, partition_size)
+
+
+def pa_decode_workspace_bytes(num_seqs: int, num_q_heads: int, max_context_len: int,
+                              partition_size: int, head_size: int) -> int:
+    return load().pa_decode_workspace_bytes(num_seqs, num_q_heads, max_context_len, partition_size,
+                                            head_size)
+
+
+# ---------------------------------------------------------------------------------------
+# device operations
+# ---------------------------------------------------------------------------------------
+
+def pa_kv_append(kv_pool, key, value, slot_mapping, stream=None):
+    """Write key[t] / value[t] ([T, Hkv, D] fp16) into pool slot slot_mapping[t] (int64)."""
+    nb, bs, hkv, d = _pool_geometry(kv_pool)
+    pool_p = _dense(kv_pool, "kv_pool", torch.float16)
+    slots_p = _dense(slot_mapping, "slot_mapping", torch.int64)
+    T = int(slot_mapping.shape[0])
+    for t, name in ((key, "key"), (value, "value")):
+        _dev(t, name, torch.float16)
+        if tuple(t.shape) != (T, hkv, d) or t.stride(2) != 1 or t.stride(1) != d:
+            raise ValueError(f"{name} must be [T, num_kv_heads, head_size] with dense rows")
+    st = load().pa_kv_append(pool_p, key.data_ptr(), value.data_ptr(), slots_p, T, hkv, d, bs, nb,
+                             key.stride(0), value.stride(0), _stream(stream))
+    _check("pa_kv_append", st)
+
+
+def pa_decode(out, q, kv_pool, block_tables, context_lens, max_context_len, scale=None,
+              partition_size=512, workspace=None, stream=None):
+    """Paged decode: out[b] = attention of q[b] ([B, Hq, D]) over its first context_lens[b] tokens.
+
+    ``max_context_len`` is a host upper bound of context_lens. ``workspace`` is a device
+    uint8 tensor of at least :func:`pa_decode_workspace_bytes` bytes; one is allocated
+    here when it is None.
+    """
+    nb, bs, hkv, d = _pool_geometry(kv_pool)
+    B, hq, dq = q.shape
+    if dq != d or tuple(out.shape) != (B, hq, d):
+        raise ValueError("q and out must be [num_seqs, num_q_heads, head_size]")
+    if block_tables.dim() != 2 or block_tables.shape[0] != B or tuple(context_lens.shape) != (B,):
+        raise ValueError("block_tables must be [num_seqs, max_blocks], context_lens [num_seqs]")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    need = pa_decode_workspace_bytes(B, hq, max_context_len, partition_size, d)
+    if need < 0:
+        raise PagedKVError("pa_decode_workspace_bytes", PA_ERR_INVALID)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_p, ws_n = (0, 0) if workspace is None else (_dense(workspace, "workspace", torch.uint8),
+                                                    workspace.numel())
+    st = load().pa_decode(
+        _dense(out, "out", torch.float16), _dense(q, "q", torch.float16),
+        _dense(kv_pool, "kv_pool", torch.float16), _dense(block_tables, "block_tables", torch.int32),
+        _dense(context_lens, "context_lens", torch.int32), B, hq, hkv, d, bs,
+        int(block_tables.shape[1]), nb, int(max_context_len), float(scale), int(partition_size),
+        ws_p, ws_n, _stream(stream))
+    _check("pa_decode", st)
+
+
+def pa_prefill_chunk(out, q, kv_pool, block_tables, query_start_loc, seq_lens, max_q_len,
+                     max_seq_len, scale=None, stream=None):
+    """Causal attention of prefill chunks (rows of q [total_q, Hq, D]) over their paged context."""
+    nb, bs, hkv, d = _pool_geometry(kv_pool)
+    total_q, hq, dq = q.shape
+    R = int(seq_lens.shape[0])
+    if dq != d or tuple(out.shape) != (total_q, hq, d):
+        raise ValueError("q and out must be [total_q, num_q_heads, head_size]")
+    if tuple(query_start_loc.shape) != (R + 1,) or block_tables.dim() != 2 or block_tables.shape[0] != R:
+        raise ValueError("query_start_loc must be [num_reqs+1], block_tables [num_reqs, max_blocks]")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    st = load().pa_prefill_chunk(
+        _dense(out, "out", torch.float16), _dense(q, "q", torch.float16),
+        _dense(kv_pool, "kv_pool", torch.float16), _dense(block_tables, "block_tables", torch.int32),
+        _dense(query_start_loc, "query_start_loc", torch.int32),
+        _dense(seq_lens, "seq_lens", torch.int32), R, total_q, int(max_q_len), int(max_seq_len), hq,
+        hkv, d, bs, int(block_tables.shape[1]), nb, float(scale), _stream(stream))
+    _check("pa_prefill_chunk", st)
+
+
+def pa_gather_kv(k_out, v_out, kv_pool, block_table_row, length, stream=None):
+    """Copy a sequence's first ``length`` keys/values ([length, Hkv, D]) out of the pool."""
+    nb, bs, hkv, d = _pool_geometry(kv_pool)
+    for t, name in ((k_out, "k_out"), (v_out, "v_out")):
+        if tuple(t.shape) != (length, hkv, d):
+            raise ValueError(f"{name} must be [length, num_kv_heads, head_size]")
+    st = load().pa_gather_kv(
+        _dense(k_out, "k_out", torch.float16), _dense(v_out, "v_out", torch.float16),
+        _dense(kv_pool, "kv_pool", torch.float16),
+        _dense(block_table_row, "block_table_row", torch.int32), int(length), hkv, d, bs, nb,
+        _stream(stream))
+    _check("pa_gather_kv", st)
+
+
+def pa_stream_read_sink_len(nbytes: int) -> int:
+    return load().pa_stream_read_sink_len(nbytes)
+
+
+def pa_stream_read(buf, sink, stream=None):
+    """Read every byte of ``buf`` once (a measurement aid); ``sink`` is a float32 device tensor."""
+    if not buf.is_cuda or not buf.is_contiguous():
+        raise ValueError("buf must be a dense device tensor")
+    nbytes = buf.numel() * buf.element_size()
+    if sink.numel() < pa_stream_read_sink_len(nbytes):
+        raise ValueError("sink too small")
+    st = load().pa_stream_read(buf.data_ptr(), nbytes, _dense(sink, "sink", torch.float32),
+                               _stream(stream))
+    _check("pa_stream_read", st)

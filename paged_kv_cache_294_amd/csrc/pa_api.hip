@@ -1,0 +1,271 @@
+// C ABI of the paged KV-cache attention library: host-side argument checks, grid and
+// workspace sizing, launches. Every declaration is in include/pagedkv.h.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+#include <cstdio>
+#include <cstring>
+
+#include "../../include/pagedkv.h"
+#include "pa_launch.h"
+
+#define PA_EXPORT extern "C" __attribute__((visibility("default")))
+
+namespace {
+
+constexpr int kBlock = 16;
+constexpr double kLog2e = 1.4426950408889634;
+
+thread_local char g_last_error[256] = "";
+
+pa_status hip_status(hipError_t e) {
+  if (e == hipSuccess) return PA_OK;
+  std::snprintf(g_last_error, sizeof(g_last_error), "%s: %s", hipGetErrorName(e),
+                hipGetErrorString(e));
+  return PA_ERR_HIP;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// Checks shared by the device operations: the pool geometry this library has kernels for.
+pa_status check_geometry(int32_t block_size, int32_t num_kv_heads, int32_t head_size) {
+  if (block_size <= 0 || num_kv_heads <= 0 || head_size <= 0) return PA_ERR_INVALID;
+  if (block_size != kBlock) return PA_ERR_UNSUPPORTED;
+  if (head_size != 64 && head_size != 128) return PA_ERR_UNSUPPORTED;
+  return PA_OK;
+}
+
+pa_status check_heads(int32_t num_q_heads, int32_t num_kv_heads) {
+  if (num_q_heads <= 0 || num_kv_heads <= 0 || num_q_heads % num_kv_heads != 0)
+    return PA_ERR_INVALID;
+  const int g = num_q_heads / num_kv_heads;
+  if (g != 1 && g != 2 && g != 4 && g != 8) return PA_ERR_UNSUPPORTED;
+  return PA_OK;
+}
+
+}  // namespace
+
+PA_EXPORT const char* pa_status_string(int status) {
+  switch (status) {
+    case PA_OK: return "ok";
+    case PA_ERR_INVALID: return "invalid argument";
+    case PA_ERR_UNSUPPORTED: return "unsupported configuration";
+    case PA_ERR_WORKSPACE: return "workspace too small";
+    case PA_ERR_HIP: return "HIP runtime error";
+    default: return "unknown status";
+  }
+}
+
+PA_EXPORT const char* pa_last_error(void) { return g_last_error; }
+
+PA_EXPORT int32_t pa_abi_version(void) { return 1; }
+
+// ---------------------------------------------------------------------------------------
+// layout helpers
+// ---------------------------------------------------------------------------------------
+
+PA_EXPORT int64_t pa_blocks_for_len(int64_t len, int32_t block_size) {
+  if (len < 0 || block_size <= 0) return -1;
+  return (len + block_size - 1) / block_size;
+}
+
+PA_EXPORT int64_t pa_block_bytes(int32_t block_size, int32_t num_kv_heads, int32_t head_size,
+                                 int32_t elem_bytes) {
+  if (block_size <= 0 || num_kv_heads <= 0 || head_size <= 0 || elem_bytes <= 0) return -1;
+  return (int64_t)block_size * 2 * num_kv_heads * head_size * elem_bytes;
+}
+
+PA_EXPORT int64_t pa_pool_bytes(int64_t num_blocks, int32_t block_size, int32_t num_kv_heads,
+                                int32_t head_size, int32_t elem_bytes) {
+  const int64_t bb = pa_block_bytes(block_size, num_kv_heads, head_size, elem_bytes);
+  if (bb < 0 || num_blocks < 0) return -1;
+  if (num_blocks > INT64_MAX / bb) return -1;
+  return num_blocks * bb;
+}
+
+PA_EXPORT int64_t pa_num_blocks_fit(int64_t free_bytes, double utilization, int32_t block_size,
+                                    int32_t num_kv_heads, int32_t head_size, int32_t elem_bytes) {
+  const int64_t bb = pa_block_bytes(block_size, num_kv_heads, head_size, elem_bytes);
+  if (bb < 0 || free_bytes < 0 || !(utilization > 0.0 && utilization <= 1.0)) return -1;
+  const double usable = std::floor((double)free_bytes * utilization);
+  return (int64_t)(usable / (double)bb);
+}
+
+PA_EXPORT int64_t pa_slot(const int32_t* block_table_row, int64_t pos, int32_t block_size) {
+  if (!block_table_row || pos < 0 || block_size <= 0) return -1;
+  const int32_t phys = block_table_row[pos / block_size];
+  if (phys < 0) return -1;
+  return (int64_t)phys * block_size + pos % block_size;
+}
+
+PA_EXPORT int64_t pa_kv_elem_offset(int64_t slot, int32_t kv, int32_t head, int32_t dim,
+                                    int32_t num_kv_heads, int32_t head_size) {
+  if (slot < 0 || (kv != 0 && kv != 1) || head < 0 || head >= num_kv_heads || dim < 0 ||
+      dim >= head_size)
+    return -1;
+  return ((slot * 2 + kv) * num_kv_heads + head) * (int64_t)head_size + dim;
+}
+
+PA_EXPORT int32_t pa_num_partitions(int32_t max_context_len, int32_t partition_size) {
+  if (max_context_len < 0 || partition_size <= 0) return -1;
+  const int32_t p = (int32_t)(((int64_t)max_context_len + partition_size - 1) / partition_size);
+  return p < 1 ? 1 : p;
+}
+
+PA_EXPORT int64_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads,
+                                            int32_t max_context_len, int32_t partition_size,
+                                            int32_t head_size) {
+  if (num_seqs < 0 || num_q_heads <= 0 || head_size <= 0) return -1;
+  const int32_t p = pa_num_partitions(max_context_len, partition_size);
+  if (p < 0) return -1;
+  if (p == 1) return 0;
+  const int64_t rows = (int64_t)num_seqs * num_q_heads * p;
+  int64_t bytes = rows * head_size * 4;  // o
+  bytes = (bytes + 255) / 256 * 256;
+  bytes += rows * 2 * 4;                 // (m, l)
+  return (bytes + 255) / 256 * 256;
+}
+
+// ---------------------------------------------------------------------------------------
+// device operations
+// ---------------------------------------------------------------------------------------
+
+PA_EXPORT pa_status pa_kv_append(void* kv_pool, const void* key, const void* value,
+                                 const int64_t* slot_mapping, int32_t num_tokens,
+                                 int32_t num_kv_heads, int32_t head_size, int32_t block_size,
+                                 int64_t num_blocks, int64_t key_token_stride,
+                                 int64_t value_token_stride, void* stream) {
+  if (num_tokens < 0 || num_blocks <= 0) return PA_ERR_INVALID;
+  if (pa_status s = check_geometry(block_size, num_kv_heads, head_size)) return s;
+  if (num_tokens == 0) return PA_OK;
+  if (!kv_pool || !key || !value || !slot_mapping) return PA_ERR_INVALID;
+  const int64_t row = (int64_t)num_kv_heads * head_size;
+  if (key_token_stride == 0) key_token_stride = row;
+  if (value_token_stride == 0) value_token_stride = row;
+  if (key_token_stride < row || value_token_stride < row) return PA_ERR_INVALID;
+  if (key_token_stride % 8 || value_token_stride % 8) return PA_ERR_INVALID;  // 16-byte rows
+  if (!aligned16(kv_pool) || !aligned16(key) || !aligned16(value)) return PA_ERR_INVALID;
+  if (row > INT32_MAX / 2) return PA_ERR_INVALID;
+  return hip_status(pkv::launch_kv_append(kv_pool, key, value, slot_mapping, num_tokens, (int)row,
+                                          num_blocks * block_size, key_token_stride,
+                                          value_token_stride, (hipStream_t)stream));
+}
+
+PA_EXPORT pa_status pa_decode(void* out, const void* q, const void* kv_pool,
+                              const int32_t* block_tables, const int32_t* context_lens,
+                              int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                              int32_t head_size, int32_t block_size, int32_t max_blocks_per_seq,
+                              int64_t num_blocks, int32_t max_context_len, float scale,
+                              int32_t partition_size, void* workspace, int64_t workspace_bytes,
+                              void* stream) {
+  if (num_seqs < 0 || max_blocks_per_seq <= 0 || num_blocks <= 0 || max_context_len < 0)
+    return PA_ERR_INVALID;
+  if (pa_status s = check_geometry(block_size, num_kv_heads, head_size)) return s;
+  if (pa_status s = check_heads(num_q_heads, num_kv_heads)) return s;
+  if (partition_size <= 0 || partition_size % block_size) return PA_ERR_INVALID;
+  if (!std::isfinite(scale)) return PA_ERR_INVALID;
+  if (num_seqs > 65535) return PA_ERR_UNSUPPORTED;
+  if ((int64_t)max_blocks_per_seq * block_size > INT32_MAX) return PA_ERR_INVALID;
+  // the kernels address up to 16 tokens * 2 * Hkv * D elements inside a block as int32
+  if ((int64_t)block_size * 2 * num_kv_heads * head_size > INT32_MAX) return PA_ERR_UNSUPPORTED;
+  if (num_seqs == 0) return PA_OK;
+  if (!out || !q || !kv_pool || !block_tables || !context_lens) return PA_ERR_INVALID;
+  if (!aligned16(out) || !aligned16(q) || !aligned16(kv_pool)) return PA_ERR_INVALID;
+
+  pkv::DecodeArgs a{};
+  a.out = out;
+  a.q = q;
+  a.pool = kv_pool;
+  a.block_tables = block_tables;
+  a.context_lens = context_lens;
+  a.num_seqs = num_seqs;
+  a.num_q_heads = num_q_heads;
+  a.num_kv_heads = num_kv_heads;
+  a.head_size = head_size;
+  a.max_blocks_per_seq = max_blocks_per_seq;
+  a.num_blocks = num_blocks;
+  a.max_context_len = max_context_len;
+  a.partition_blocks = partition_size / block_size;
+  a.num_partitions = pa_num_partitions(max_context_len, partition_size);
+  if (a.num_partitions > 65535) return PA_ERR_UNSUPPORTED;
+  a.scale_log2 = (float)((double)scale * kLog2e);
+  if (a.num_partitions > 1) {
+    const int64_t need = pa_decode_workspace_bytes(num_seqs, num_q_heads, max_context_len,
+                                                   partition_size, head_size);
+    if (!workspace || workspace_bytes < need) return PA_ERR_WORKSPACE;
+    if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return PA_ERR_INVALID;
+    const int64_t rows = (int64_t)num_seqs * num_q_heads * a.num_partitions;
+    const int64_t o_bytes = (rows * head_size * 4 + 255) / 256 * 256;
+    a.ws_o = static_cast<float*>(workspace);
+    a.ws_ml = reinterpret_cast<float*>(static_cast<char*>(workspace) + o_bytes);
+  }
+  return hip_status(pkv::launch_decode(a, (hipStream_t)stream));
+}
+
+PA_EXPORT pa_status pa_prefill_chunk(void* out, const void* q, const void* kv_pool,
+                                     const int32_t* block_tables, const int32_t* query_start_loc,
+                                     const int32_t* seq_lens, int32_t num_reqs, int32_t total_q,
+                                     int32_t max_q_len, int32_t max_seq_len, int32_t num_q_heads,
+                                     int32_t num_kv_heads, int32_t head_size, int32_t block_size,
+                                     int32_t max_blocks_per_seq, int64_t num_blocks, float scale,
+                                     void* stream) {
+  if (num_reqs < 0 || total_q < 0 || max_q_len < 0 || max_seq_len < 0 ||
+      max_blocks_per_seq <= 0 || num_blocks <= 0)
+    return PA_ERR_INVALID;
+  if (pa_status s = check_geometry(block_size, num_kv_heads, head_size)) return s;
+  if (pa_status s = check_heads(num_q_heads, num_kv_heads)) return s;
+  if (!std::isfinite(scale)) return PA_ERR_INVALID;
+  if (max_q_len > max_seq_len) return PA_ERR_INVALID;
+  if ((int64_t)max_blocks_per_seq * block_size > INT32_MAX) return PA_ERR_INVALID;
+  if ((int64_t)block_size * 2 * num_kv_heads * head_size > INT32_MAX) return PA_ERR_UNSUPPORTED;
+  if (num_reqs == 0 || total_q == 0 || max_q_len == 0) return PA_OK;
+  if (!out || !q || !kv_pool || !block_tables || !query_start_loc || !seq_lens)
+    return PA_ERR_INVALID;
+  if (!aligned16(out) || !aligned16(q) || !aligned16(kv_pool)) return PA_ERR_INVALID;
+  pkv::PrefillArgs a{};
+  a.out = out;
+  a.q = q;
+  a.pool = kv_pool;
+  a.block_tables = block_tables;
+  a.query_start_loc = query_start_loc;
+  a.seq_lens = seq_lens;
+  a.num_reqs = num_reqs;
+  a.total_q = total_q;
+  a.max_q_len = max_q_len;
+  a.max_seq_len = max_seq_len;
+  a.num_q_heads = num_q_heads;
+  a.num_kv_heads = num_kv_heads;
+  a.head_size = head_size;
+  a.max_blocks_per_seq = max_blocks_per_seq;
+  a.num_blocks = num_blocks;
+  a.scale_log2 = (float)((double)scale * kLog2e);
+  hipError_t e = pkv::launch_prefill(a, (hipStream_t)stream);
+  if (e == hipErrorNotSupported) return PA_ERR_UNSUPPORTED;
+  return hip_status(e);
+}
+
+PA_EXPORT pa_status pa_gather_kv(void* k_out, void* v_out, const void* kv_pool,
+                                 const int32_t* block_table_row, int32_t len,
+                                 int32_t num_kv_heads, int32_t head_size, int32_t block_size,
+                                 int64_t num_blocks, void* stream) {
+  if (len < 0 || num_blocks <= 0) return PA_ERR_INVALID;
+  if (pa_status s = check_geometry(block_size, num_kv_heads, head_size)) return s;
+  if (len == 0) return PA_OK;
+  if (!k_out || !v_out || !kv_pool || !block_table_row) return PA_ERR_INVALID;
+  if (!aligned16(k_out) || !aligned16(v_out) || !aligned16(kv_pool)) return PA_ERR_INVALID;
+  const int64_t row = (int64_t)num_kv_heads * head_size;
+  if (row > INT32_MAX / 2) return PA_ERR_INVALID;
+  return hip_status(pkv::launch_gather_kv(k_out, v_out, kv_pool, block_table_row, len, (int)row,
+                                          num_blocks, (hipStream_t)stream));
+}
+
+PA_EXPORT int64_t pa_stream_read_sink_len(int64_t bytes) {
+  if (bytes <= 0 || bytes % 16) return -1;
+  return pkv::stream_read_groups(bytes);
+}
+
+PA_EXPORT pa_status pa_stream_read(const void* buf, int64_t bytes, float* sink, void* stream) {
+  if (!buf || !sink || bytes <= 0 || bytes % 16 || !aligned16(buf)) return PA_ERR_INVALID;
+  return hip_status(pkv::launch_stream_read(buf, bytes, sink, (hipStream_t)stream));
+}

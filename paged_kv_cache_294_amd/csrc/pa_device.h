@@ -1,0 +1,73 @@
+// Device helpers shared by the paged-attention kernels (gfx950, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace pkv {
+
+typedef _Float16 half_t;
+typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
+typedef _Float16 half4_t __attribute__((ext_vector_type(4)));
+typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
+typedef float float4_t __attribute__((ext_vector_type(4)));
+typedef float float16_t __attribute__((ext_vector_type(16)));
+
+constexpr int kWave = 64;
+constexpr int kBlockSize = 16;  // tokens per KV block
+
+// Pool element offset of (slot, kv) row start: pool is [NB][16][2][Hkv][D].
+__device__ __forceinline__ int64_t row_offset(int64_t slot, int kv, int kv_row_elems) {
+  return (slot * 2 + kv) * (int64_t)kv_row_elems;
+}
+
+// DPP lane moves (gfx9 encodings). Only row-local patterns are used.
+enum : int {
+  kDppXor1 = 0xB1,         // quad_perm [1,0,3,2]
+  kDppXor2 = 0x4E,         // quad_perm [2,3,0,1]
+  kDppHalfMirror = 0x141,  // lane i <-> 7-i inside each half row of 8
+  kDppMirror = 0x140,      // lane i <-> 15-i inside each row of 16
+};
+
+template <int Ctrl>
+__device__ __forceinline__ float dpp_mov(float x) {
+  return __builtin_bit_cast(
+      float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), Ctrl, 0xF, 0xF, false));
+}
+
+// Sum over groups of N consecutive lanes (N in {8, 16}) aligned to N; every lane of the
+// group gets the group's sum.
+template <int N>
+__device__ __forceinline__ float group_sum(float x) {
+  static_assert(N == 8 || N == 16, "row-local sums only");
+  x += dpp_mov<kDppXor1>(x);
+  x += dpp_mov<kDppXor2>(x);
+  x += dpp_mov<kDppHalfMirror>(x);
+  if constexpr (N == 16) x += dpp_mov<kDppMirror>(x);
+  return x;
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+__device__ __forceinline__ float dot8(half8_t a, half8_t b, float acc) {
+  acc = __builtin_amdgcn_fdot2(half2_t{a[0], a[1]}, half2_t{b[0], b[1]}, acc, false);
+  acc = __builtin_amdgcn_fdot2(half2_t{a[2], a[3]}, half2_t{b[2], b[3]}, acc, false);
+  acc = __builtin_amdgcn_fdot2(half2_t{a[4], a[5]}, half2_t{b[4], b[5]}, acc, false);
+  acc = __builtin_amdgcn_fdot2(half2_t{a[6], a[7]}, half2_t{b[6], b[7]}, acc, false);
+  return acc;
+}
+
+__device__ __forceinline__ float wave_max(float x) {
+  for (int o = 32; o >= 1; o >>= 1) x = fmaxf(x, __shfl_xor(x, o, kWave));
+  return x;
+}
+
+__device__ __forceinline__ float wave_sum(float x) {
+  for (int o = 32; o >= 1; o >>= 1) x += __shfl_xor(x, o, kWave);
+  return x;
+}
+
+__device__ __forceinline__ float neg_inf() { return -__builtin_inff(); }
+__device__ __forceinline__ float qnan() { return __builtin_nanf(""); }
+
+}  // namespace pkv

@@ -1,0 +1,53 @@
+// Launchers of the device kernels. Internal to the library: the C ABI in pagedkv.h checks
+// every argument before calling these, so they only size grids and launch.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace pkv {
+
+hipError_t launch_kv_append(void* pool, const void* key, const void* value, const int64_t* slots,
+                            int num_tokens, int kv_row_elems, int64_t num_slots,
+                            int64_t key_stride, int64_t value_stride, hipStream_t stream);
+
+struct DecodeArgs {
+  void* out;
+  const void* q;
+  const void* pool;
+  const int32_t* block_tables;
+  const int32_t* context_lens;
+  float* ws_o;   // [B][Hq][P][D] fp32, or null when P == 1
+  float* ws_ml;  // [B][Hq][P][2] fp32 (max in log2 units, sum), or null when P == 1
+  int num_seqs, num_q_heads, num_kv_heads, head_size;
+  int max_blocks_per_seq;
+  int64_t num_blocks;
+  int max_context_len;
+  int partition_blocks;  // partition size in blocks
+  int num_partitions;    // partitions the grid covers
+  float scale_log2;      // softmax scale * log2(e)
+};
+hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
+
+struct PrefillArgs {
+  void* out;
+  const void* q;
+  const void* pool;
+  const int32_t* block_tables;
+  const int32_t* query_start_loc;
+  const int32_t* seq_lens;
+  int num_reqs, total_q, max_q_len, max_seq_len;
+  int num_q_heads, num_kv_heads, head_size;
+  int max_blocks_per_seq;
+  int64_t num_blocks;
+  float scale_log2;
+};
+hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream);
+
+hipError_t launch_gather_kv(void* k_out, void* v_out, const void* pool, const int32_t* table_row,
+                            int len, int kv_row_elems, int64_t num_blocks, hipStream_t stream);
+
+int64_t stream_read_groups(int64_t bytes);
+hipError_t launch_stream_read(const void* buf, int64_t bytes, float* sink, hipStream_t stream);
+
+}  // namespace pkv

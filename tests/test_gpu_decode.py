@@ -1,0 +1,289 @@
+"""GPU parity of kv_append, gather and paged decode against the CPU oracle (MI355X)."""
+
+import dataclasses
+import functools
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import paged_kv_cache_294_amd as pkv
+import workloads
+from gpu_util import bits, check_attention, dev, host, note
+
+pytestmark = pytest.mark.gpu
+
+
+# ---------------------------------------------------------------------------------------
+# running the library on a generated batch
+# ---------------------------------------------------------------------------------------
+
+class Dev:
+    """Device copies of a batch, with the step's tokens appended on the GPU."""
+
+    def __init__(self, inp, append=True):
+        self.inp = inp
+        self.pool = dev(inp.pool)
+        self.q = dev(inp.q)
+        self.bt = dev(inp.block_tables)
+        self.lens = dev(inp.seq_lens)
+        self.qsl = dev(inp.query_start_loc)
+        if append and len(inp.slot_mapping):
+            pkv.pa_kv_append(self.pool, dev(inp.key_new), dev(inp.value_new), dev(inp.slot_mapping))
+
+    def decode(self, partition_size=512, max_context_len=None):
+        inp = self.inp
+        p = inp.num_prefill
+        q = self.q[inp.num_prefill_tokens:]
+        bt, lens = self.bt[p:], self.lens[p:]
+        out = torch.empty_like(q)
+        mcl = int(inp.seq_lens[p:].max()) if max_context_len is None else max_context_len
+        pkv.pa_decode(out, q, self.pool, bt, lens, mcl, inp.scale, partition_size)
+        return host(out)
+
+
+def oracle_pool(inp):
+    return oracle.kv_append(inp.pool, inp.key_new, inp.value_new, inp.slot_mapping)
+
+
+def oracle_decode(inp, pool=None):
+    pool = oracle_pool(inp) if pool is None else pool
+    q, bt, lens = inp.decode_part()
+    return oracle.decode(q, pool, bt, lens, inp.scale)
+
+
+@functools.lru_cache(maxsize=2)
+def cfg(i):
+    note(f"generating config {i}")
+    return workloads.CONFIGS[i]()
+
+
+def free():
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+
+
+# ---------------------------------------------------------------------------------------
+# kv_append: bit-exact, whole pool compared
+# ---------------------------------------------------------------------------------------
+
+def check_append(inp):
+    d = Dev(inp, append=True)
+    got = host(d.pool)
+    ref = oracle_pool(inp)
+    assert np.array_equal(bits(got), bits(ref)), "pool differs from the oracle's append"
+    del d
+    free()
+
+
+def test_append_tiny_full_into_nan_pool():
+    inp = workloads.config1_full_append()
+    check_append(inp)
+    # the appended pool is the tiny decode batch's pool
+    d = Dev(inp, append=True)
+    assert np.array_equal(bits(host(d.pool)), bits(workloads.config1().pool))
+
+
+def test_append_small_mixed_and_ragged():
+    check_append(workloads.mixed_case(31, [0, 5, 37, 100], [9, 16, 23, 64], [1, 3, 40, 17], 4, 2, 64))
+    check_append(workloads.decode_case(32, [1, 15, 16, 17, 31, 32, 33], 8, 8, 128))
+
+
+def test_append_skips_negative_and_out_of_pool_slots():
+    inp = workloads.decode_case(33, [5, 20, 40, 7], 4, 4, 64)
+    slots = inp.slot_mapping.copy()
+    slots[0] = -1
+    slots[2] = inp.num_blocks * 16 + 5  # beyond the pool: skipped
+    bad = dataclasses.replace(inp, slot_mapping=slots)
+    d = Dev(bad, append=True)
+    got = host(d.pool)
+    ref = oracle.kv_append(inp.pool, inp.key_new, inp.value_new,
+                           np.where(slots >= inp.num_blocks * 16, -1, slots))
+    assert np.array_equal(bits(got), bits(ref))
+
+
+def test_append_strided_rows():
+    inp = workloads.decode_case(34, [3, 9, 30], 4, 4, 128)
+    T, H, D = inp.key_new.shape
+    # key/value as views into a fused [T, 3, H, D] projection output
+    fused = np.zeros((T, 3, H, D), np.float16)
+    fused[:, 1] = inp.key_new
+    fused[:, 2] = inp.value_new
+    f = dev(fused)
+    pool = dev(inp.pool)
+    pkv.pa_kv_append(pool, f[:, 1], f[:, 2], dev(inp.slot_mapping))
+    assert np.array_equal(bits(host(pool)), bits(oracle_pool(inp)))
+
+
+def test_append_config2_full():
+    check_append(cfg(2))
+
+
+def test_append_config5_full():
+    check_append(cfg(5))
+
+
+# ---------------------------------------------------------------------------------------
+# gather: block-table indexing, bit-exact
+# ---------------------------------------------------------------------------------------
+
+def check_gather(inp, seqs=None):
+    d = Dev(inp, append=True)
+    pool = oracle_pool(inp)
+    for b in (range(inp.num_seqs) if seqs is None else seqs):
+        L = int(inp.seq_lens[b])
+        k = torch.empty((L, inp.num_kv_heads, inp.head_size), dtype=torch.float16, device="cuda")
+        v = torch.empty_like(k)
+        pkv.pa_gather_kv(k, v, d.pool, d.bt[b], L)
+        K, V = oracle.gather_kv(pool, inp.block_tables[b], L)
+        assert np.array_equal(bits(host(k)), bits(K)), b
+        assert np.array_equal(bits(host(v)), bits(V)), b
+
+
+def test_gather_tiny():
+    check_gather(workloads.config1())
+
+
+def test_gather_shared_and_mixed():
+    check_gather(workloads.prefix_shared_case(35, 3, 4, 2, list(range(1, 13)), 8, 2, 64))
+    check_gather(workloads.mixed_case(36, [0, 33], [17, 40], [2, 100], 4, 4, 128))
+
+
+def test_gather_config2_sampled():
+    check_gather(cfg(2), seqs=[0, 1, 77, 255])
+    free()
+
+
+# ---------------------------------------------------------------------------------------
+# decode parity
+# ---------------------------------------------------------------------------------------
+
+def test_decode_tiny():
+    inp = workloads.config1()
+    got = Dev(inp).decode()
+    ref = oracle_decode(inp)
+    check_attention(got, ref, "tiny")
+    # a context of one token returns that token's value row exactly
+    v0 = inp.pool[inp.block_tables[0, 0], 0, 1]
+    assert np.array_equal(bits(got[0]), bits(v0))
+
+
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("G", [1, 2, 4, 8])
+@pytest.mark.parametrize("ps", [16, 64, 512])
+def test_decode_small(D, G, ps):
+    lens = [1, 2, 15, 16, 17, 31, 33, 64, 100, 257, 511, 512, 513, 700]
+    hkv = 4 if G < 8 else 2
+    inp = workloads.decode_case(40 + D + G + ps, lens, hkv * G, hkv, D)
+    note(f"decode D={D} G={G} partition={ps}")
+    got = Dev(inp).decode(partition_size=ps)
+    check_attention(got, oracle_decode(inp), f"D{D} G{G} ps{ps}")
+
+
+def test_decode_length_one_rows_are_exact():
+    inp = workloads.decode_case(41, [1] * 8, 16, 4, 128)
+    got = Dev(inp).decode()
+    # the single (appended) token's value row, per query head's KV head
+    for b in range(8):
+        for h in range(16):
+            assert np.array_equal(bits(got[b, h]), bits(inp.value_new[b, h // 4]))
+
+
+def test_decode_config2_full():
+    inp = cfg(2)
+    d = Dev(inp)
+    got = d.decode()
+    del d
+    free()
+    check_attention(got, oracle_decode(inp), "config2")
+
+
+def test_decode_config3_sampled():
+    inp = cfg(3)
+    d = Dev(inp)
+    outs = {ps: d.decode(partition_size=ps) for ps in (512, 2048)}
+    del d
+    free()
+    rng = np.random.default_rng(0)
+    pairs = [(b, int(h)) for b in range(8) for h in rng.choice(32, 4, replace=False)]
+    ref = oracle.decode_rows(inp.q, inp.pool, inp.block_tables, inp.seq_lens, inp.scale, pairs)
+    for ps, got in outs.items():
+        rows = np.stack([got[b, h] for b, h in pairs])
+        check_attention(rows, ref, f"config3 ps{ps}")
+    assert np.abs(outs[512].astype(np.float64) - outs[2048].astype(np.float64)).max() <= 1e-4
+
+
+def test_decode_config4_full_and_shared_equals_private():
+    inp = cfg(4)
+    got = Dev(inp).decode()
+    free()
+    check_attention(got, oracle_decode(inp), "config4")
+    priv = workloads.unshare_prefix(inp)
+    got2 = Dev(priv).decode()
+    free()
+    assert np.array_equal(bits(got), bits(got2)), "shared prefix blocks change the output"
+
+
+def test_decode_config5_decode_part():
+    inp = cfg(5)
+    d = Dev(inp)
+    got = d.decode()
+    del d
+    free()
+    check_attention(got, oracle_decode(inp), "config5 decode")
+
+
+# ---------------------------------------------------------------------------------------
+# invariants on the GPU
+# ---------------------------------------------------------------------------------------
+
+def test_decode_block_permutation_is_bit_identical():
+    lens = np.random.default_rng(42).integers(100, 1500, 24)
+    inp = workloads.decode_case(42, lens, 32, 32, 128)
+    a = Dev(inp).decode()
+    b = Dev(workloads.repermute(inp, 7)).decode()
+    assert np.array_equal(bits(a), bits(b))
+
+
+def test_decode_partition_sweep():
+    lens = [1, 255, 256, 257, 511, 512, 513, 1023, 1024, 1025, 3000]
+    inp = workloads.decode_case(43, lens, 8, 8, 128)
+    ref = oracle_decode(inp)
+    d = Dev(inp)
+    outs = {ps: d.decode(partition_size=ps) for ps in (256, 512, 1024, 1 << 16)}
+    for ps, got in outs.items():
+        check_attention(got, ref, f"sweep ps{ps}")
+    base = outs[1 << 16].astype(np.float64)
+    for ps, got in outs.items():
+        assert np.abs(got.astype(np.float64) - base).max() <= 1e-4, ps
+
+
+def test_decode_max_context_bound_larger_than_lengths():
+    inp = workloads.decode_case(44, [5, 40, 300], 4, 4, 64)
+    got = Dev(inp).decode(max_context_len=4096)  # more partitions than any sequence has
+    check_attention(got, oracle_decode(inp), "loose max_context_len")
+
+
+def test_decode_zero_length_and_bad_rows():
+    inp = workloads.decode_case(45, [0, 30, 600, 600, 20], 8, 4, 128, append=False)
+    d = Dev(inp, append=False)
+    lens = inp.seq_lens.copy()
+    lens[4] = 10_000  # beyond max_context_len and the table: NaN row
+    d.lens = dev(lens)
+    bt = inp.block_tables.copy()
+    bt[2, 20] = inp.num_blocks + 3  # outside the pool, in partition 1 of 3: NaN row
+    bt[1, 0] = -1                    # outside the pool, single partition: NaN row
+    d.bt = dev(bt)
+    got = d.decode(partition_size=256, max_context_len=600).astype(np.float64)
+    assert np.all(got[0] == 0)
+    assert np.all(np.isnan(got[1])) and np.all(np.isnan(got[2])) and np.all(np.isnan(got[4]))
+    ref = oracle.decode(inp.q, inp.pool, inp.block_tables, inp.seq_lens, inp.scale)
+    check_attention(got[3:4], ref[3:4], "good row next to bad ones")
+
+
+def test_stream_read_runs():
+    buf = torch.ones(1 << 24, dtype=torch.uint8, device="cuda")
+    sink = torch.zeros(pkv.pa_stream_read_sink_len(buf.numel()), dtype=torch.float32, device="cuda")
+    pkv.pa_stream_read(buf, sink)
+    assert np.isfinite(host(sink)).all()
