@@ -141,6 +141,39 @@ def stream_read_gbps(torch, pkv, nbytes=4 << 30, reps=10):
     return nbytes / (ms * 1e-3) / 1e9
 
 
+def run_counter_sequence(inp, partition_size):
+    """Dispatches for counter passes, in a fixed order: a torch copy of 1 GiB (reads and
+    writes exactly 1 GiB: the calibration of FETCH_SIZE / WRITE_SIZE), pa_stream_read of
+    1 GiB (reads 1 GiB), then three decode steps (kv_append + pa_decode)."""
+    import torch
+    import paged_kv_cache_294_amd as pkv
+
+    nbytes = 1 << 30
+    src = torch.ones(nbytes, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    sink = torch.zeros(pkv.pa_stream_read_sink_len(nbytes), dtype=torch.float32, device="cuda")
+    pool = torch.from_numpy(inp.pool).cuda()
+    q = torch.from_numpy(inp.q).cuda()
+    bt = torch.from_numpy(inp.block_tables).cuda()
+    lens = torch.from_numpy(inp.seq_lens).cuda()
+    key = torch.from_numpy(inp.key_new).cuda()
+    value = torch.from_numpy(inp.value_new).cuda()
+    slots = torch.from_numpy(inp.slot_mapping).cuda()
+    out = torch.empty_like(q)
+    mcl = int(inp.seq_lens.max())
+    torch.cuda.synchronize()
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    pkv.pa_stream_read(src, sink)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        pkv.pa_kv_append(pool, key, value, slots)
+        pkv.pa_decode(out, q, pool, bt, lens, mcl, inp.scale, partition_size)
+        torch.cuda.synchronize()
+    log(f"counter sequence done: copy {nbytes} B, stream_read {nbytes} B, 3 decode steps; "
+        f"decode algorithmic KV bytes per launch {kv_read_bytes(inp)}")
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -150,6 +183,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-stream-read", action="store_true")
     ap.add_argument("--cpu-cores", type=int, default=16)
+    ap.add_argument("--mode", choices=("bench", "counters"), default="bench",
+                    help="counters: a short fixed dispatch sequence for rocprofv3 --pmc passes "
+                         "(1 GiB torch copy, 1 GiB pa_stream_read, then 3 decode steps)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported "
@@ -163,6 +199,10 @@ def main():
     log(f"generated in {time.perf_counter() - t0:.1f}s: {inp.num_blocks} blocks, "
         f"sum L = {int(inp.seq_lens.sum())}")
     kv_bytes = kv_read_bytes(inp)
+
+    if args.mode == "counters":
+        run_counter_sequence(inp, args.partition_size)
+        return
 
     cpu = None
     if not args.no_cpu_baseline:

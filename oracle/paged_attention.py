@@ -160,9 +160,11 @@ def softmax_attention(q_row: np.ndarray, keys: np.ndarray, values: np.ndarray, s
     """
     if keys.shape[0] == 0:
         return np.zeros(values.shape[1], dtype=np.float64)
-    s = scale * (keys.astype(np.float64) @ q_row.astype(np.float64))
+    keys = np.asarray(keys, dtype=np.float64)
+    values = np.asarray(values, dtype=np.float64)
+    s = scale * (keys @ np.asarray(q_row, dtype=np.float64))
     p = np.exp(s - s.max())
-    return (p @ values.astype(np.float64)) / p.sum()
+    return (p @ values) / p.sum()
 
 
 def decode(q, pool, block_tables, context_lens, scale):
@@ -178,6 +180,7 @@ def decode(q, pool, block_tables, context_lens, scale):
         if L == 0:
             continue
         K, V = gather_kv(pool, block_tables[b], L)
+        K, V = K.astype(np.float64), V.astype(np.float64)  # fp16 -> fp64 is exact
         for h in range(Hq):
             k = kv_head_of(h, Hq, Hkv)
             out[b, h] = softmax_attention(q[b, h], K[:, k], V[:, k], scale)
@@ -261,6 +264,7 @@ def prefill_chunk(q, pool, block_tables, query_start_loc, seq_lens, scale, rows=
         if not wanted:
             continue
         K, V = gather_kv(pool, block_tables[r], S)
+        K, V = K.astype(np.float64), V.astype(np.float64)  # fp16 -> fp64 is exact
         for i in wanted:
             visible = P + i + 1
             for h in range(Hq):

@@ -1,6 +1,294 @@
-// Chunked prefill: not built yet; the C ABI reports PA_ERR_UNSUPPORTED.
+// Chunked prefill on gfx950 matrix cores: causal attention of a chunk of C query rows
+// over the P tokens cached before it plus the chunk itself, all read from the paged pool
+// through the request's block-table row. The scheduler on page "vLLM 部署深度指南"
+// (continuous-batching listing) runs such prefills in the same step as decodes.
+//
+// Work split. One workgroup of four waves per (request, query head, 128-row tile of the
+// chunk); each wave owns 32 query rows. The KV context is streamed in tiles of 64
+// tokens (four 16-token blocks found through the table) and staged in LDS, double
+// buffered, shared by the four waves.
+//
+// Contractions, both on v_mfma_f32_32x32x16_f16 (fp16 in, fp32 accumulate):
+//   S^T[token][row] = K[token][:] . Q[row][:]   (A = K rows from LDS, B = Q rows in
+//                                                registers: both in natural row-major order)
+//   O^T[dim][row]  += V^T[dim][token] . P^T[token][row]
+// The S^T accumulator holds, in each lane, scores of one query row for 16 tokens of a
+// 32-token tile; converted to fp16 they are exactly the B operand of the second product,
+// so P never leaves registers. V is transposed once per tile while it is written to LDS;
+// its token order inside each 16-token group is permuted so that the 8 tokens a lane
+// feeds to one product sit next to each other (one 16-byte LDS read per operand).
+//
+// Softmax. Online, fp32, per query row, in log2 units (scale * log2(e) applied to the
+// scores). Causal mask: chunk row i (position P + i) sees tokens 0 .. P + i; only tiles
+// crossing that diagonal or the end of the context are masked, and tiles past every row
+// of a wave are skipped by that wave.
+#include "pa_device.h"
 #include "pa_launch.h"
 
 namespace pkv {
-hipError_t launch_prefill(const PrefillArgs&, hipStream_t) { return hipErrorNotSupported; }
+namespace {
+
+constexpr int kBM = 128;     // query rows per workgroup
+constexpr int kWRows = 32;   // query rows per wave
+constexpr int kBN = 64;      // tokens per KV tile
+constexpr int kThreads = 256;
+
+__device__ __forceinline__ int vt_pos(int t) {
+  // token order inside a 16-token group: 0-3, 8-11, 4-7, 12-15
+  const int u = t & 15;
+  return (t & ~15) | (u & 3) | ((u & 4) << 1) | ((u & 8) >> 1);
+}
+
+template <int D>
+struct PrefillSmem {
+  static constexpr int KP = D + 8;     // K row pitch (halves): rows 16 B apart in bank space
+  static constexpr int VP = kBN + 8;   // V^T row pitch (halves)
+  half_t k[2][kBN * KP];
+  half_t vt[2][D * VP];
+};
+
+template <int D>
+__device__ __forceinline__ void write_rows(const PrefillArgs& a, int q0, int row, int h,
+                                           float value) {
+  half_t* out = static_cast<half_t*>(a.out) + ((int64_t)(q0 + row) * a.num_q_heads + h) * D;
+  for (int d = 0; d < D; ++d) out[d] = (half_t)value;
+}
+
+template <int D>
+__global__ __launch_bounds__(kThreads, 2) void prefill_kernel(const PrefillArgs a) {
+  constexpr int KS = D / 16;          // k-steps of S^T (16 dims each)
+  constexpr int DT = D / 32;          // 32-dim tiles of O^T
+  constexpr int PIECES = D / 8;       // 16-byte pieces per K (or V) row of one head
+  constexpr int K_PER_THREAD = kBN * PIECES / kThreads;
+  constexpr int V_ROUNDS = PIECES / 8;  // each round: 32 token pairs x 8 pieces
+  using Smem = PrefillSmem<D>;
+  constexpr int KP = Smem::KP, VP = Smem::VP;
+  extern __shared__ __align__(16) unsigned char smem_raw[];
+  Smem& sm = *reinterpret_cast<Smem*>(smem_raw);
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int w = tid >> 6;
+  const int g = lane >> 5;
+  const int r = blockIdx.z;
+  const int h = blockIdx.y;
+  const int i0 = blockIdx.x * kBM;
+  const int kvh = h / (a.num_q_heads / a.num_kv_heads);
+
+  const int q0 = a.query_start_loc[r];
+  const int q1 = a.query_start_loc[r + 1];
+  const int C = q1 - q0;
+  const int S = a.seq_lens[r];
+  const int P = S - C;
+  const bool rows_ok = q0 >= 0 && q1 >= q0 && q1 <= a.total_q;
+  const bool bad = !rows_ok || C > a.max_q_len || S < C || S > a.max_seq_len ||
+                   S > a.max_blocks_per_seq * kBlockSize;
+  if (bad) {
+    if (rows_ok)
+      for (int i = i0 + tid; i < min(i0 + kBM, C); i += kThreads) write_rows<D>(a, q0, i, h, qnan());
+    return;
+  }
+  if (i0 >= C) return;
+
+  // ---- this wave's query rows: B operand of S^T, 8 dims of row (lane % 32) per k-step --
+  const int row_w = i0 + kWRows * w;
+  const int qrow = row_w + (lane & 31);
+  const half_t* qp = static_cast<const half_t*>(a.q);
+  half8_t qb[KS];
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) {
+    if (qrow < C)
+      qb[ks] = *reinterpret_cast<const half8_t*>(
+          qp + ((int64_t)(q0 + qrow) * a.num_q_heads + h) * D + 16 * ks + 8 * g);
+    else
+      qb[ks] = half8_t{};
+  }
+
+  const int kv_end = min(S, P + min(i0 + kBM, C));               // tokens the workgroup sees
+  const int wave_end = row_w < C ? P + min(row_w + kWRows, C) : 0;  // tokens this wave sees
+  const int ntiles = (kv_end + kBN - 1) / kBN;
+
+  const int kv_row = a.num_kv_heads * D;
+  const int tok_stride = 2 * kv_row;
+  const half_t* pool = static_cast<const half_t*>(a.pool);
+  const int32_t* bt = a.block_tables + (int64_t)r * a.max_blocks_per_seq;
+  const int nblk = (S + kBlockSize - 1) / kBlockSize;
+  bool bad_table = false;
+
+  // staging registers: K pieces (token tid/PIECES + j*256/PIECES, piece tid%PIECES) and V
+  // pieces (token pair tid%32, piece tid/32 + 8*round)
+  half8_t kreg[K_PER_THREAD], vreg[V_ROUNDS][2];
+
+  auto load_tile = [&](int t0) {
+    int phys[kBN / kBlockSize];
+#pragma unroll
+    for (int jb = 0; jb < kBN / kBlockSize; ++jb) {
+      const int blk = t0 / kBlockSize + jb;
+      phys[jb] = blk < nblk ? bt[blk] : -1;
+      if (blk < nblk && (phys[jb] < 0 || phys[jb] >= a.num_blocks)) {
+        bad_table = true;
+        phys[jb] = -1;
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < K_PER_THREAD; ++j) {
+      const int p = tid + j * kThreads;
+      const int t = p / PIECES, c = p % PIECES;
+      const int pb = phys[t / kBlockSize];
+      if (t0 + t < S && pb >= 0)
+        kreg[j] = *reinterpret_cast<const half8_t*>(
+            pool + ((int64_t)pb * kBlockSize + t % kBlockSize) * tok_stride + kvh * D + 8 * c);
+      else
+        kreg[j] = half8_t{};
+    }
+#pragma unroll
+    for (int rd = 0; rd < V_ROUNDS; ++rd) {
+      const int c = tid / 32 + 8 * rd;
+#pragma unroll
+      for (int e = 0; e < 2; ++e) {
+        const int t = 2 * (tid & 31) + e;
+        const int pb = phys[t / kBlockSize];
+        if (t0 + t < S && pb >= 0)
+          vreg[rd][e] = *reinterpret_cast<const half8_t*>(
+              pool + ((int64_t)pb * kBlockSize + t % kBlockSize) * tok_stride + kv_row + kvh * D +
+              8 * c);
+        else
+          vreg[rd][e] = half8_t{};
+      }
+    }
+  };
+
+  auto store_tile = [&](int buf) {
+#pragma unroll
+    for (int j = 0; j < K_PER_THREAD; ++j) {
+      const int p = tid + j * kThreads;
+      const int t = p / PIECES, c = p % PIECES;
+      *reinterpret_cast<half8_t*>(&sm.k[buf][t * KP + 8 * c]) = kreg[j];
+    }
+#pragma unroll
+    for (int rd = 0; rd < V_ROUNDS; ++rd) {
+      const int c = tid / 32 + 8 * rd;
+      const int pos = vt_pos(2 * (tid & 31));  // even; the pair's second token follows it
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        half2_t pr = {vreg[rd][0][i], vreg[rd][1][i]};
+        *reinterpret_cast<half2_t*>(&sm.vt[buf][(8 * c + i) * VP + pos]) = pr;
+      }
+    }
+  };
+
+  float m = neg_inf(), l = 0.0f;
+  float16_t o[DT];
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt) o[dt] = float16_t{};
+
+  load_tile(0);
+  store_tile(0);
+  __syncthreads();
+
+  for (int it = 0; it < ntiles; ++it) {
+    const int buf = it & 1;
+    const int t0 = it * kBN;
+    const bool has_next = it + 1 < ntiles;
+    if (has_next) load_tile(t0 + kBN);
+
+    if (t0 < wave_end) {
+      // S^T for the tile's two 32-token halves
+      float16_t sacc[2];
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt) {
+        sacc[tt] = float16_t{};
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+          const half8_t ka = *reinterpret_cast<const half8_t*>(
+              &sm.k[buf][(32 * tt + (lane & 31)) * KP + 16 * ks + 8 * g]);
+          sacc[tt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(ka, qb[ks], sacc[tt], 0, 0, 0);
+        }
+      }
+      // scale, mask, online softmax for query row qrow
+      const bool full = (t0 + kBN <= P + row_w + 1) && (t0 + kBN <= S);
+      float mloc = neg_inf();
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          float s = sacc[tt][v] * a.scale_log2;
+          if (!full) {
+            const int t = t0 + 32 * tt + 8 * (v >> 2) + 4 * g + (v & 3);
+            if (t >= S || t > P + qrow) s = neg_inf();
+          }
+          sacc[tt][v] = s;
+          mloc = fmaxf(mloc, s);
+        }
+      mloc = fmaxf(mloc, __shfl_xor(mloc, 32, kWave));
+      const float mnew = fmaxf(m, mloc);
+      const float base = (mnew == neg_inf()) ? 0.0f : mnew;
+      const float alpha = fast_exp2(m - base);
+      float lsum = 0.0f;
+      half8_t pb[4];
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk)
+#pragma unroll
+        for (int s = 0; s < 8; ++s) {
+          const float pv = fast_exp2(sacc[kk >> 1][8 * (kk & 1) + s] - base);
+          lsum += pv;
+          pb[kk][s] = (half_t)pv;
+        }
+      lsum += __shfl_xor(lsum, 32, kWave);
+      l = l * alpha + lsum;
+      m = mnew;
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) o[dt] *= alpha;
+      // O^T += V^T P^T
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk)
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) {
+          const half8_t va = *reinterpret_cast<const half8_t*>(
+              &sm.vt[buf][(32 * dt + (lane & 31)) * VP + 16 * kk + 8 * g]);
+          o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(va, pb[kk], o[dt], 0, 0, 0);
+        }
+    }
+
+    if (has_next) store_tile(buf ^ 1);
+    __syncthreads();
+  }
+
+  if (qrow >= C) return;
+  half_t* out = static_cast<half_t*>(a.out) + ((int64_t)(q0 + qrow) * a.num_q_heads + h) * D;
+  const float inv = bad_table ? qnan() : 1.0f / l;
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+    for (int v4 = 0; v4 < 4; ++v4) {
+      half4_t x;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) x[e] = (half_t)(o[dt][4 * v4 + e] * inv);
+      *reinterpret_cast<half4_t*>(out + 32 * dt + 8 * v4 + 4 * g) = x;
+    }
+}
+
+template <int D>
+hipError_t launch_prefill_d(const PrefillArgs& a, hipStream_t stream) {
+  const size_t smem = sizeof(PrefillSmem<D>);
+  static bool attr_set = false;  // the attribute is per function, set once per process
+  if (!attr_set) {
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&prefill_kernel<D>),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
+    if (e != hipSuccess) return e;
+    attr_set = true;
+  }
+  dim3 grid((a.max_q_len + kBM - 1) / kBM, a.num_q_heads, a.num_reqs);
+  hipLaunchKernelGGL((prefill_kernel<D>), grid, dim3(kThreads), smem, stream, a);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream) {
+  if (a.head_size == 128) return launch_prefill_d<128>(a, stream);
+  if (a.head_size == 64) return launch_prefill_d<64>(a, stream);
+  return hipErrorInvalidValue;
+}
+
 }  // namespace pkv

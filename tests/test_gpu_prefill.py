@@ -1,0 +1,127 @@
+"""GPU parity of the MFMA chunked-prefill kernel against the CPU oracle (MI355X)."""
+
+import functools
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import paged_kv_cache_294_amd as pkv
+import workloads
+from gpu_util import check_attention, dev, host, note
+
+pytestmark = pytest.mark.gpu
+
+
+def gpu_prefill(inp, pool=None, bt=None, lens=None, qsl=None, max_q_len=None):
+    """Append the batch's new tokens on the GPU, then run the prefill chunks."""
+    pool_d = dev(inp.pool) if pool is None else pool
+    if pool is None and len(inp.slot_mapping):
+        pkv.pa_kv_append(pool_d, dev(inp.key_new), dev(inp.value_new), dev(inp.slot_mapping))
+    q, bt_h, qsl_h, lens_h = inp.prefill_part()
+    bt = dev(bt_h) if bt is None else bt
+    lens = dev(lens_h) if lens is None else lens
+    qsl = dev(qsl_h) if qsl is None else qsl
+    qd = dev(q)
+    out = torch.empty_like(qd)
+    mq = int(np.diff(qsl_h).max()) if max_q_len is None else max_q_len
+    pkv.pa_prefill_chunk(out, qd, pool_d, bt, qsl, lens, mq, int(lens_h.max()), inp.scale)
+    return host(out), pool_d
+
+
+def oracle_prefill(inp, rows=None):
+    pool = oracle.kv_append(inp.pool, inp.key_new, inp.value_new, inp.slot_mapping)
+    q, bt, qsl, lens = inp.prefill_part()
+    return oracle.prefill_chunk(q, pool, bt, qsl, lens, inp.scale, rows=rows)
+
+
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("G", [1, 4])
+def test_prefill_small_ragged(D, G):
+    priors = [0, 5, 100, 700, 31]
+    chunks = [1, 17, 64, 130, 300]
+    inp = workloads.mixed_case(50 + D + G, priors, chunks, [9], 4 * G, 4, D)
+    note(f"prefill D={D} G={G}")
+    got, _ = gpu_prefill(inp)
+    check_attention(got, oracle_prefill(inp), f"prefill D{D} G{G}")
+
+
+def test_prefill_pure_causal_chunks():
+    inp = workloads.mixed_case(51, [0, 0, 0], [128, 129, 255], [], 8, 8, 128)
+    got, _ = gpu_prefill(inp)
+    check_attention(got, oracle_prefill(inp), "P=0 causal")
+
+
+def test_prefill_long_prior():
+    inp = workloads.mixed_case(52, [3584, 1000], [512, 77], [], 32, 8, 128)
+    got, _ = gpu_prefill(inp)
+    check_attention(got, oracle_prefill(inp), "long prior")
+
+
+@functools.lru_cache(maxsize=1)
+def config5():
+    note("generating config 5")
+    return workloads.config5()
+
+
+def test_prefill_config5_full():
+    inp = config5()
+    got, pool = gpu_prefill(inp)
+    del pool
+    torch.cuda.empty_cache()
+    note("oracle prefill of config 5 (4096 rows x 32 heads)")
+    check_attention(got, oracle_prefill(inp), "config5 prefill")
+
+
+def test_prefill_row_matches_decode_kernel():
+    """Chunk row i and a decode query at position P+i over P+i+1 tokens give the same row."""
+    inp = workloads.mixed_case(53, [40, 300], [64, 100], [], 8, 4, 128)
+    got, pool = gpu_prefill(inp)
+    q, bt, qsl, lens = inp.prefill_part()
+    rows, qs, bts, ctx = [], [], [], []
+    for r in range(2):
+        P = int(lens[r]) - int(qsl[r + 1] - qsl[r])
+        for i in (0, 1, 31, int(qsl[r + 1] - qsl[r]) - 1):
+            rows.append(int(qsl[r]) + i)
+            qs.append(q[int(qsl[r]) + i])
+            bts.append(bt[r])
+            ctx.append(P + i + 1)
+    qd = dev(np.stack(qs))
+    out = torch.empty_like(qd)
+    pkv.pa_decode(out, qd, pool, dev(np.stack(bts)), dev(np.array(ctx, np.int32)), max(ctx),
+                  inp.scale, 512)
+    dec = host(out).astype(np.float64)
+    assert np.abs(dec - got[rows].astype(np.float64)).max() <= 2e-3
+
+
+def test_prefill_chunk_split_equals_whole():
+    """A 512-row chunk equals the same rows run as two 256-row chunks over the same table."""
+    inp = workloads.mixed_case(54, [900], [512], [], 8, 8, 128)
+    whole, pool = gpu_prefill(inp)
+    q, bt, qsl, lens = inp.prefill_part()
+    S = int(lens[0])
+    qsl2 = dev(np.array([0, 256, 512], np.int32))
+    lens2 = dev(np.array([S - 256, S], np.int32))
+    bt2 = dev(np.stack([bt[0], bt[0]]))
+    out = torch.empty_like(dev(q))
+    pkv.pa_prefill_chunk(out, dev(q), pool, bt2, qsl2, lens2, 256, S, inp.scale)
+    split = host(out).astype(np.float64)
+    assert np.abs(split - whole.astype(np.float64)).max() <= 2e-3
+    check_attention(split, oracle_prefill(inp), "split chunk")
+
+
+def test_prefill_bad_rows_are_nan():
+    inp = workloads.mixed_case(55, [20, 50, 10], [30, 40, 20], [], 4, 4, 64)
+    pool = dev(oracle.kv_append(inp.pool, inp.key_new, inp.value_new, inp.slot_mapping))
+    q, bt, qsl, lens = inp.prefill_part()
+    bt = bt.copy()
+    bt[1, 2] = inp.num_blocks + 9   # request 1: a table entry outside the pool
+    lens = lens.copy()
+    lens[2] = 5                     # request 2: shorter than its chunk
+    got, _ = gpu_prefill(inp, pool=pool, bt=dev(bt), lens=dev(lens))
+    ref = oracle_prefill(inp)
+    r0, r1, r2 = int(qsl[1]), int(qsl[2]), int(qsl[3])
+    check_attention(got[:r0], ref[:r0], "good request")
+    assert np.all(np.isnan(got[r0:r1].astype(np.float64)))
+    assert np.all(np.isnan(got[r1:r2].astype(np.float64)))
