@@ -174,6 +174,52 @@ def run_counter_sequence(inp, partition_size):
         f"decode algorithmic KV bytes per launch {kv_read_bytes(inp)}")
 
 
+def summarize_trace(path, command):
+    import csv
+    rows = list(csv.DictReader(open(path)))
+    print(f"# rocprofv3 kernel statistics\n# command: {command}")
+    print(f"{'kernel':<72} {'calls':>6} {'avg_us':>10} {'min_us':>10} {'max_us':>10} {'pct':>6}")
+    for r in rows:
+        print(f"{r['Name'][:72]:<72} {int(r['Calls']):>6} {float(r['AverageNs']) / 1e3:>10.2f} "
+              f"{float(r['MinNs']) / 1e3:>10.2f} {float(r['MaxNs']) / 1e3:>10.2f} "
+              f"{float(r['Percentage']):>6.2f}")
+
+
+def summarize_counters(fetch_csv, write_csv, command):
+    """Per-dispatch FETCH_SIZE / WRITE_SIZE (KiB) of the --mode counters sequence, scaled by
+    the reading of the 1 GiB copy (the second 1 GiB dispatch reads and writes 1 GiB)."""
+    import csv
+    fetch = list(csv.DictReader(open(fetch_csv)))
+    write = list(csv.DictReader(open(write_csv)))
+    gib = float(1 << 30)
+    # the 1 GiB device-to-device copy is the first dispatch that writes >= 1 GiB after the fills
+    copy_i = next(i for i, r in enumerate(write)
+                  if "copy" in r["Kernel_Name"].lower() and float(r["Counter_Value"]) * 1024 >= gib * 0.99)
+    f_scale = gib / (float(fetch[copy_i]["Counter_Value"]) * 1024)
+    w_scale = gib / (float(write[copy_i]["Counter_Value"]) * 1024)
+    print(f"# rocprofv3 FETCH_SIZE / WRITE_SIZE passes of `bench.py --mode counters`")
+    print(f"# command: {command}")
+    print(f"# calibration: 1 GiB copy reads FETCH_SIZE={fetch[copy_i]['Counter_Value']} KiB, "
+          f"WRITE_SIZE={write[copy_i]['Counter_Value']} KiB")
+    print(f"fetch_scale: {f_scale:.5f}")
+    print(f"write_scale: {w_scale:.5f}")
+    per = {}
+    for f, w in zip(fetch, write):
+        name = f"{f['Kernel_Name'][:60]} [grid {f['Grid_Size']}]"
+        rb = float(f["Counter_Value"]) * 1024 * f_scale
+        wb = float(w["Counter_Value"]) * 1024 * w_scale
+        per.setdefault(name, []).append((rb, wb))
+    print(f"{'kernel':<72} {'n':>3} {'read_bytes':>14} {'write_bytes':>14}")
+    for name, v in per.items():
+        rb = sum(x[0] for x in v) / len(v)
+        wb = sum(x[1] for x in v) / len(v)
+        print(f"{name[:72]:<72} {len(v):>3} {rb:>14.0f} {wb:>14.0f}")
+    dec = [sum(x[0] + x[1] for x in v) / len(v) for n, v in per.items()
+           if "decode_partition_kernel" in n or "decode_reduce_kernel" in n]
+    print(f"hbm_bytes_per_launch: {sum(dec):.0f}")
+    print(f"kernel_source_sha256_16: {source_digest(DECODE_SRC)}")
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -186,7 +232,19 @@ def main():
     ap.add_argument("--mode", choices=("bench", "counters"), default="bench",
                     help="counters: a short fixed dispatch sequence for rocprofv3 --pmc passes "
                          "(1 GiB torch copy, 1 GiB pa_stream_read, then 3 decode steps)")
+    ap.add_argument("--summarize-trace", metavar="KERNEL_STATS_CSV",
+                    help="print a profile summary of a rocprofv3 --stats kernel_stats.csv and exit")
+    ap.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="print the HBM traffic summary of two rocprofv3 --pmc passes of "
+                         "--mode counters (FETCH_SIZE, then WRITE_SIZE) and exit")
+    ap.add_argument("--command", default="", help="command line recorded in a summary")
     args = ap.parse_args()
+    if args.summarize_trace:
+        summarize_trace(args.summarize_trace, args.command)
+        return
+    if args.summarize_counters:
+        summarize_counters(*args.summarize_counters, args.command)
+        return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported "
               "(the decode path would shard by sequence or KV head with no exchange).",
