@@ -8,9 +8,11 @@ import torch
 # Attention outputs: fp16 result of fp32 arithmetic against the fp64 oracle.
 MAX_ABS = 5e-3
 MEAN_ABS = 5e-4
-# Stricter bar of our own: at long contexts outputs are small (RMS ~ 1/sqrt(L)), so the
-# absolute bound alone would pass a kernel that drops whole partitions.
-MAX_OVER_RMS = 1e-2
+# Stricter bar of our own, per output row (one query row of one head): at long contexts
+# outputs are small (RMS ~ 1/sqrt(L)), so the absolute bound alone would pass a kernel
+# that drops whole partitions; rows of one batch differ in scale, so each row is held to
+# its own RMS.
+MAX_OVER_ROW_RMS = 1e-2
 
 
 def note(msg):
@@ -37,12 +39,17 @@ def check_attention(got_f16, ref_f64, label=""):
     assert got.shape == ref.shape, (got.shape, ref.shape)
     assert np.isfinite(got).all(), f"{label}: non-finite output"
     err = np.abs(got - ref)
-    rms = float(np.sqrt(np.mean(ref * ref)))
-    stats = dict(max_abs=float(err.max()), mean_abs=float(err.mean()), rms=rms,
-                 max_over_rms=float(err.max() / rms) if rms > 0 else 0.0)
+    D = ref.shape[-1]
+    row_rms = np.sqrt(np.mean(ref.reshape(-1, D) ** 2, axis=1))
+    row_err = err.reshape(-1, D).max(axis=1)
+    live = row_rms > 0
+    worst = float((row_err[live] / row_rms[live]).max()) if live.any() else 0.0
+    stats = dict(max_abs=float(err.max()), mean_abs=float(err.mean()),
+                 rms=float(np.sqrt(np.mean(ref * ref))), max_over_row_rms=worst)
     note(f"  {label}: {stats}")
     assert stats["max_abs"] <= MAX_ABS, (label, stats)
     assert stats["mean_abs"] <= MEAN_ABS, (label, stats)
-    if rms > 0:
-        assert stats["max_over_rms"] <= MAX_OVER_RMS, (label, stats)
+    assert worst <= MAX_OVER_ROW_RMS, (label, stats)
+    # rows whose reference is exactly zero (empty contexts) must come out zero
+    assert np.all(err.reshape(-1, D)[~live] == 0), label
     return stats
