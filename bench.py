@@ -1,16 +1,20 @@
 #!/usr/bin/env python3
-"""Benchmark of one paged-attention decode step on one MI355X.
+"""Benchmark of one paged-attention step on one MI355X.
 
-A step is the whole hot path over one batch: ``pa_kv_append`` of this step's new
-tokens into their pool slots, then ``pa_decode`` (split-context partitions and their
-log-sum-exp merge). The default workload is the Llama-7B-layer-shaped decode batch:
-256 sequences, context lengths U{128..2048}, 32 heads x 128, 16-token blocks, fp16,
-physical blocks shuffled, one new token per sequence.
+A step is the whole hot path over one batch: ``pa_kv_append`` of this step's new tokens
+into their pool slots, ``pa_prefill_chunk`` for prefill chunks (mixed workload only) and
+``pa_decode`` (split-context partitions and their log-sum-exp merge). Workloads:
 
-Printed: one JSON line with the KV-read rate (algorithmic bytes: every cached token's
-K and V row once per step) over the whole step, seq-steps/s, the decode kernel's
-roofline fraction against the 8 TB/s HBM peak, and the oracle's rate on the host
-cores (measured before the GPU is touched).
+  c2 (default)  256 decode sequences, context U{128..2048}, 32 heads x 128, + append
+  c3            8 sequences x 32768 tokens, 32 x 128 (64 partitions of 512)
+  c4            64 prompt groups x 4 samples sharing 64 blocks, 32q / 8kv heads x 128
+  c5            8 prefill chunks of 512 over priors U{0..3584} + 248 decodes U{256..4096},
+                append of all 4344 new tokens
+
+Printed: one JSON line. ``value`` is the KV-read rate of the step (algorithmic bytes:
+every decode context token's K and V row once) over the whole step time; ``roofline``
+is the decode kernel call against the 8 TB/s HBM peak; ``cpu_baseline`` is the oracle on
+the host cores, run before the GPU is touched.
 """
 
 from __future__ import annotations
@@ -30,19 +34,67 @@ sys.path.insert(0, ROOT)
 
 import workloads  # noqa: E402
 
-HBM_PEAK_GBPS = 8000.0  # MI355X HBM3E, vendor figure
+HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E, vendor figure
+MFMA_F16_PEAK_TFLOPS = 2500.0   # MI355X dense fp16 matrix peak, vendor figure
 PROFILES = os.path.join(ROOT, "profiles")
 DECODE_SRC = os.path.join(ROOT, "paged_kv_cache_294_amd", "csrc", "pa_decode.hip")
+
+WORKLOADS = {
+    "c2": (2, "decode step: kv_append of 256 tokens + paged decode of 256 sequences, "
+              "context U{128..2048}, 32 heads x 128, block 16, fp16, shuffled blocks"),
+    "c3": (3, "long-context decode: 8 sequences x 32768 tokens, 32 heads x 128, block 16, "
+              "fp16, split-context partitions"),
+    "c4": (4, "prefix-shared GQA decode: 64 groups x 4 samples, 1024-token shared prompt "
+              "(64 blocks) + 64..256 private tokens, 32 q / 8 kv heads x 128, fp16"),
+    "c5": (5, "mixed step: kv_append of 4344 tokens + 8 prefill chunks of 512 over priors "
+              "U{0..3584} + 248 decodes U{256..4096}, 32 heads x 128, fp16"),
+}
 
 
 def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
+# ---------------------------------------------------------------------------------------
+# algorithmic work
+# ---------------------------------------------------------------------------------------
+
 def kv_read_bytes(inp) -> int:
-    """Algorithmic KV bytes of a decode step: each context token's K and V rows once."""
+    """Decode KV bytes: each decode context token's K and V rows once (logical)."""
     lens = inp.seq_lens[inp.num_prefill:].astype(np.int64)
     return int(lens.sum()) * 2 * inp.num_kv_heads * inp.head_size * 2
+
+
+def kv_unique_bytes(inp) -> int:
+    """Decode KV bytes counting each physical block's filled slots once (shared prefixes)."""
+    row = 2 * inp.num_kv_heads * inp.head_size * 2
+    seen = {}
+    for b in range(inp.num_prefill, inp.num_seqs):
+        L = int(inp.seq_lens[b])
+        for j in range(-(-L // 16)):
+            blk = int(inp.block_tables[b, j])
+            seen[blk] = max(seen.get(blk, 0), min(16, L - 16 * j))
+    return sum(seen.values()) * row
+
+
+def prefill_flops(inp) -> int:
+    """Causal pairs only: 4 * D * Hq * sum_r (C * P_r + C (C + 1) / 2)."""
+    tot = 0
+    for r in range(inp.num_prefill):
+        C = int(inp.q_lens[r])
+        P = int(inp.seq_lens[r]) - C
+        tot += C * P + C * (C + 1) // 2
+    return 4 * inp.head_size * inp.num_q_heads * tot
+
+
+def append_bytes(inp) -> int:
+    return 2 * len(inp.slot_mapping) * 2 * inp.num_kv_heads * inp.head_size * 2
+
+
+def shares_blocks(inp) -> bool:
+    used = [inp.block_tables[b, : -(-int(inp.seq_lens[b]) // 16)] for b in range(inp.num_seqs)]
+    allb = np.concatenate(used) if used else np.zeros(0)
+    return len(np.unique(allb)) < len(allb)
 
 
 def source_digest(path) -> str:
@@ -75,7 +127,7 @@ def read_traffic(name, digest):
 _CPU = {}
 
 
-def _cpu_worker(chunk):
+def _cpu_decode(chunk):
     import oracle  # the oracle runs only in this leg of the benchmark
     inp, pool = _CPU["inp"], _CPU["pool"]
     q, bt, lens = inp.decode_part()
@@ -83,7 +135,15 @@ def _cpu_worker(chunk):
     return len(chunk)
 
 
-def cpu_baseline(inp, max_cores):
+def _cpu_prefill(rows):
+    import oracle
+    inp, pool = _CPU["inp"], _CPU["pool"]
+    q, bt, qsl, lens = inp.prefill_part()
+    oracle.prefill_chunk(q, pool, bt, qsl, lens, inp.scale, rows=set(rows))
+    return len(rows)
+
+
+def cpu_baseline(inp, max_cores, decode_seqs=None, prefill_every=8):
     import oracle
     try:
         from threadpoolctl import threadpool_limits
@@ -95,25 +155,38 @@ def cpu_baseline(inp, max_cores):
     pool = oracle.kv_append(inp.pool, inp.key_new, inp.value_new, inp.slot_mapping)
     t_append = time.perf_counter() - t0
     _CPU["inp"], _CPU["pool"] = inp, pool
-    seqs = np.arange(inp.num_decode)
-    chunks = [c for c in np.array_split(seqs, cores * 4) if len(c)]
+    nd = inp.num_decode if decode_seqs is None else min(decode_seqs, inp.num_decode)
+    chunks = [c for c in np.array_split(np.arange(nd), cores * 4) if len(c)]
+    ctx = mp.get_context("fork")
     t0 = time.perf_counter()
-    with mp.get_context("fork").Pool(cores) as workers:
-        done = sum(workers.map(_cpu_worker, chunks))
-    t_decode = time.perf_counter() - t0
+    with ctx.Pool(cores) as workers:
+        done = sum(workers.map(_cpu_decode, chunks))
+    t_decode = (time.perf_counter() - t0) * inp.num_decode / nd
+    sample = [f"oracle kv_append of {len(inp.slot_mapping)} tokens (copies the pool, 1 core, "
+              f"{t_append:.2f} s)",
+              f"oracle fp64 decode of {nd} of {inp.num_decode} sequences over {cores} worker "
+              f"processes, time scaled to all ({t_decode:.2f} s)"]
+    t_prefill = 0.0
+    if inp.num_prefill:
+        total_q = inp.num_prefill_tokens
+        rows = np.arange(0, total_q, prefill_every)
+        parts = [list(map(int, c)) for c in np.array_split(rows, cores * 4) if len(c)]
+        t0 = time.perf_counter()
+        with ctx.Pool(cores) as workers:
+            workers.map(_cpu_prefill, parts)
+        t_prefill = (time.perf_counter() - t0) * total_q / len(rows)
+        sample.append(f"oracle prefill of every {prefill_every}th of {total_q} chunk rows, "
+                      f"time scaled to all rows ({t_prefill:.2f} s)")
     _CPU.clear()
-    assert done == inp.num_decode
-    t = t_append + t_decode
+    assert done == nd
+    t = t_append + t_decode + t_prefill
     return {
         "value": kv_read_bytes(inp) / t / 1e9,
         "unit": "GB/s",
         "cores": cores,
         "kind": "oracle",
-        "sample": (f"whole step of the same batch: oracle kv_append of {len(inp.slot_mapping)} tokens "
-                   f"(copies the pool, 1 core, {t_append:.2f} s) + oracle decode of all "
-                   f"{inp.num_decode} sequences in fp64 over {cores} worker processes "
-                   f"({t_decode:.2f} s)"),
-        "seq_steps_per_s": inp.num_decode / t,
+        "sample": "; ".join(sample),
+        "seq_steps_per_s": inp.num_seqs / t,
         "seconds": t,
     }
 
@@ -141,10 +214,58 @@ def stream_read_gbps(torch, pkv, nbytes=4 << 30, reps=10):
     return nbytes / (ms * 1e-3) / 1e9
 
 
-def run_counter_sequence(inp, partition_size):
+class Step:
+    """Device copies of a batch and one step of the hot path over them."""
+
+    def __init__(self, torch, pkv, inp, partition_size, kv_stream):
+        self.torch, self.pkv, self.inp = torch, pkv, inp
+
+        def c(a):
+            return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+        self.pool = c(inp.pool)
+        self.key, self.value, self.slots = c(inp.key_new), c(inp.value_new), c(inp.slot_mapping)
+        qd, btd, lensd = inp.decode_part()
+        self.dq, self.dbt, self.dlens = c(qd), c(btd), c(lensd)
+        self.dout = torch.empty_like(self.dq)
+        self.mcl = int(lensd.max()) if len(lensd) else 0
+        self.ps = partition_size
+        self.flags = pkv.PA_DECODE_KV_STREAM if kv_stream else 0
+        ws = pkv.pa_decode_workspace_bytes(len(lensd), inp.num_q_heads, self.mcl, partition_size,
+                                           inp.head_size)
+        self.ws = torch.empty(max(ws, 256), dtype=torch.uint8, device="cuda")
+        self.has_prefill = inp.num_prefill > 0
+        if self.has_prefill:
+            qp, btp, qsl, lensp = inp.prefill_part()
+            self.pq, self.pbt, self.qsl, self.plens = c(qp), c(btp), c(qsl), c(lensp)
+            self.pout = torch.empty_like(self.pq)
+            self.max_q = int(np.diff(qsl).max())
+            self.max_s = int(lensp.max())
+
+    def run(self, ev=None):
+        pkv = self.pkv
+
+        def rec(i):
+            if ev is not None:
+                ev[i].record()
+
+        rec(0)
+        if len(self.inp.slot_mapping):
+            pkv.pa_kv_append(self.pool, self.key, self.value, self.slots)
+        rec(1)
+        if self.has_prefill:
+            pkv.pa_prefill_chunk(self.pout, self.pq, self.pool, self.pbt, self.qsl, self.plens,
+                                 self.max_q, self.max_s, self.inp.scale)
+        rec(2)
+        pkv.pa_decode(self.dout, self.dq, self.pool, self.dbt, self.dlens, self.mcl, self.inp.scale,
+                      self.ps, self.ws, self.flags)
+        rec(3)
+
+
+def run_counter_sequence(inp, partition_size, kv_stream):
     """Dispatches for counter passes, in a fixed order: a torch copy of 1 GiB (reads and
     writes exactly 1 GiB: the calibration of FETCH_SIZE / WRITE_SIZE), pa_stream_read of
-    1 GiB (reads 1 GiB), then three decode steps (kv_append + pa_decode)."""
+    1 GiB (reads 1 GiB), then three steps of the workload."""
     import torch
     import paged_kv_cache_294_amd as pkv
 
@@ -152,25 +273,16 @@ def run_counter_sequence(inp, partition_size):
     src = torch.ones(nbytes, dtype=torch.uint8, device="cuda")
     dst = torch.empty_like(src)
     sink = torch.zeros(pkv.pa_stream_read_sink_len(nbytes), dtype=torch.float32, device="cuda")
-    pool = torch.from_numpy(inp.pool).cuda()
-    q = torch.from_numpy(inp.q).cuda()
-    bt = torch.from_numpy(inp.block_tables).cuda()
-    lens = torch.from_numpy(inp.seq_lens).cuda()
-    key = torch.from_numpy(inp.key_new).cuda()
-    value = torch.from_numpy(inp.value_new).cuda()
-    slots = torch.from_numpy(inp.slot_mapping).cuda()
-    out = torch.empty_like(q)
-    mcl = int(inp.seq_lens.max())
+    step = Step(torch, pkv, inp, partition_size, kv_stream)
     torch.cuda.synchronize()
     dst.copy_(src)
     torch.cuda.synchronize()
     pkv.pa_stream_read(src, sink)
     torch.cuda.synchronize()
     for _ in range(3):
-        pkv.pa_kv_append(pool, key, value, slots)
-        pkv.pa_decode(out, q, pool, bt, lens, mcl, inp.scale, partition_size)
+        step.run()
         torch.cuda.synchronize()
-    log(f"counter sequence done: copy {nbytes} B, stream_read {nbytes} B, 3 decode steps; "
+    log(f"counter sequence done: copy {nbytes} B, stream_read {nbytes} B, 3 steps; "
         f"decode algorithmic KV bytes per launch {kv_read_bytes(inp)}")
 
 
@@ -187,17 +299,16 @@ def summarize_trace(path, command):
 
 def summarize_counters(fetch_csv, write_csv, command):
     """Per-dispatch FETCH_SIZE / WRITE_SIZE (KiB) of the --mode counters sequence, scaled by
-    the reading of the 1 GiB copy (the second 1 GiB dispatch reads and writes 1 GiB)."""
+    the reading of the 1 GiB copy."""
     import csv
     fetch = list(csv.DictReader(open(fetch_csv)))
     write = list(csv.DictReader(open(write_csv)))
     gib = float(1 << 30)
-    # the 1 GiB device-to-device copy is the first dispatch that writes >= 1 GiB after the fills
     copy_i = next(i for i, r in enumerate(write)
                   if "copy" in r["Kernel_Name"].lower() and float(r["Counter_Value"]) * 1024 >= gib * 0.99)
     f_scale = gib / (float(fetch[copy_i]["Counter_Value"]) * 1024)
     w_scale = gib / (float(write[copy_i]["Counter_Value"]) * 1024)
-    print(f"# rocprofv3 FETCH_SIZE / WRITE_SIZE passes of `bench.py --mode counters`")
+    print("# rocprofv3 FETCH_SIZE / WRITE_SIZE passes of `bench.py --mode counters`")
     print(f"# command: {command}")
     print(f"# calibration: 1 GiB copy reads FETCH_SIZE={fetch[copy_i]['Counter_Value']} KiB, "
           f"WRITE_SIZE={write[copy_i]['Counter_Value']} KiB")
@@ -221,17 +332,21 @@ def summarize_counters(fetch_csv, write_csv, command):
 
 
 def main():
-    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap = argparse.ArgumentParser(description=__doc__,
+                                 formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--partition-size", type=int, default=512)
+    ap.add_argument("--workload", choices=sorted(WORKLOADS), default="c2")
+    ap.add_argument("--partition-size", type=int, default=256)
+    ap.add_argument("--kv-stream", choices=("auto", "on", "off"), default="auto",
+                    help="non-temporal K/V loads in decode; auto: on unless blocks are shared")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-stream-read", action="store_true")
     ap.add_argument("--cpu-cores", type=int, default=16)
     ap.add_argument("--mode", choices=("bench", "counters"), default="bench",
                     help="counters: a short fixed dispatch sequence for rocprofv3 --pmc passes "
-                         "(1 GiB torch copy, 1 GiB pa_stream_read, then 3 decode steps)")
+                         "(1 GiB torch copy, 1 GiB pa_stream_read, then 3 steps)")
     ap.add_argument("--summarize-trace", metavar="KERNEL_STATS_CSV",
                     help="print a profile summary of a rocprofv3 --stats kernel_stats.csv and exit")
     ap.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
@@ -251,21 +366,24 @@ def main():
               file=sys.stderr)
         sys.exit(2)
 
-    log("generating the 256-sequence decode batch (seed 2)")
+    seed, desc = WORKLOADS[args.workload]
+    log(f"generating workload {args.workload} (seed {seed})")
     t0 = time.perf_counter()
-    inp = workloads.config2()
+    inp = workloads.CONFIGS[seed]()
     log(f"generated in {time.perf_counter() - t0:.1f}s: {inp.num_blocks} blocks, "
-        f"sum L = {int(inp.seq_lens.sum())}")
+        f"{inp.num_seqs} sequences, sum L = {int(inp.seq_lens.sum())}")
+    shared = shares_blocks(inp)
+    kv_stream = {"on": True, "off": False, "auto": not shared}[args.kv_stream]
     kv_bytes = kv_read_bytes(inp)
 
     if args.mode == "counters":
-        run_counter_sequence(inp, args.partition_size)
+        run_counter_sequence(inp, args.partition_size, kv_stream)
         return
 
     cpu = None
     if not args.no_cpu_baseline:
         log("CPU baseline: oracle on the host cores")
-        cpu = cpu_baseline(inp, args.cpu_cores)
+        cpu = cpu_baseline(inp, args.cpu_cores, decode_seqs=4 if args.workload == "c3" else None)
         log(f"CPU baseline done in {cpu['seconds']:.1f}s on {cpu['cores']} cores")
 
     import torch
@@ -282,56 +400,48 @@ def main():
         log(f"stream_read: {stream_gbps:.0f} GB/s")
 
     log("copying the batch to the GPU")
-    pool = torch.from_numpy(inp.pool).cuda()
-    q = torch.from_numpy(inp.q).cuda()
-    bt = torch.from_numpy(inp.block_tables).cuda()
-    lens = torch.from_numpy(inp.seq_lens).cuda()
-    key = torch.from_numpy(inp.key_new).cuda()
-    value = torch.from_numpy(inp.value_new).cuda()
-    slots = torch.from_numpy(inp.slot_mapping).cuda()
-    out = torch.empty_like(q)
-    mcl = int(inp.seq_lens.max())
-    ws_bytes = pkv.pa_decode_workspace_bytes(inp.num_seqs, inp.num_q_heads, mcl,
-                                             args.partition_size, inp.head_size)
-    ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device="cuda")
-
-    def step(ev=None):
-        if ev is not None:
-            ev[0].record()
-        pkv.pa_kv_append(pool, key, value, slots)
-        if ev is not None:
-            ev[1].record()
-        pkv.pa_decode(out, q, pool, bt, lens, mcl, inp.scale, args.partition_size, ws)
-        if ev is not None:
-            ev[2].record()
-
+    step = Step(torch, pkv, inp, args.partition_size, kv_stream)
     for _ in range(args.warmup):
-        step()
+        step.run()
     torch.cuda.synchronize()
     log(f"warmup done; timing {args.steps} steps")
 
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     w0 = time.perf_counter()
     start.record()
     for i in range(args.steps):
-        step(evs[i])
+        step.run(evs[i])
     end.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - w0
     ms_step = start.elapsed_time(end) / args.steps
-    append_ms = [e[0].elapsed_time(e[1]) for e in evs]
-    decode_ms = [e[1].elapsed_time(e[2]) for e in evs]
-    dec_avg = float(np.mean(decode_ms))
-    log(f"step {ms_step:.3f} ms (wall {wall / args.steps * 1e3:.3f} ms), decode {dec_avg:.3f} ms, "
-        f"append {np.mean(append_ms) * 1e3:.1f} us")
+    append_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
+    prefill_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in evs]))
+    decode_ms = float(np.mean([e[2].elapsed_time(e[3]) for e in evs]))
+    log(f"step {ms_step:.3f} ms (wall {wall / args.steps * 1e3:.3f} ms): append "
+        f"{append_ms * 1e3:.1f} us, prefill {prefill_ms * 1e3:.1f} us, decode {decode_ms * 1e3:.1f} us")
 
-    achieved = kv_bytes / (dec_avg * 1e-3) / 1e9
-    nparts = pkv.pa_num_partitions(mcl, args.partition_size)
-    digest = source_digest(DECODE_SRC)
-    traffic = read_traffic("pa_decode_c2_counters.txt", digest)
+    achieved = kv_bytes / (decode_ms * 1e-3) / 1e9
+    nparts = pkv.pa_num_partitions(step.mcl, args.partition_size)
+    traffic = read_traffic(f"pa_decode_{args.workload}_counters.txt", source_digest(DECODE_SRC))
     used_blocks = int(sum(-(-int(L) // 16) for L in inp.seq_lens))
+    kernels = {"decode": {"ms": decode_ms, "kv_read_GBps": achieved,
+                          "frac_hbm_peak": achieved / HBM_PEAK_GBPS, "partitions": nparts,
+                          "kv_stream": kv_stream}}
+    if len(inp.slot_mapping):
+        kernels["append"] = {"us": append_ms * 1e3, "tokens": len(inp.slot_mapping),
+                             "GBps": append_bytes(inp) / (append_ms * 1e-3) / 1e9}
+    if inp.num_prefill:
+        fl = prefill_flops(inp)
+        tf = fl / (prefill_ms * 1e-3) / 1e12
+        kernels["prefill"] = {"us": prefill_ms * 1e3, "gflop": fl / 1e9, "TFLOPs": tf,
+                              "frac_mfma_peak": tf / MFMA_F16_PEAK_TFLOPS}
+    if shared:
+        ub = kv_unique_bytes(inp)
+        kernels["decode"]["unique_kv_bytes"] = ub
+        kernels["decode"]["unique_kv_GBps"] = ub / (decode_ms * 1e-3) / 1e9
     result = {
         "metric": "paged-attn decode KV-read GB/s (% of HBM peak) + seq-steps/s, 1 GPU",
         "value": kv_bytes / (ms_step * 1e-3) / 1e9,
@@ -346,16 +456,14 @@ def main():
         "dtype": "f16",
         "data": "synthetic",
         "config": {
-            "workload": "decode step: kv_append of 256 tokens + paged decode of 256 sequences, "
-                        "context U{128..2048}, 32 heads x 128, block 16, fp16, shuffled blocks",
-            "num_seqs": inp.num_seqs, "num_heads": inp.num_q_heads, "head_size": inp.head_size,
+            "workload": desc,
+            "num_seqs": inp.num_seqs, "num_q_heads": inp.num_q_heads,
+            "num_kv_heads": inp.num_kv_heads, "head_size": inp.head_size,
             "block_size": inp.block_size, "partition_size": args.partition_size,
-            "partitions": nparts, "sum_context_tokens": int(inp.seq_lens.sum()), "seed": 2,
+            "sum_context_tokens": int(inp.seq_lens.sum()), "seed": seed,
         },
         "pct_of_hbm_peak": 100.0 * kv_bytes / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBPS,
         "seq_steps_per_s": inp.num_seqs / (ms_step * 1e-3),
-        "decode_ms": dec_avg,
-        "append_us": float(np.mean(append_ms)) * 1e3,
         "roofline": {
             "kernel": "pa_decode" + (" (partition + log-sum-exp reduce kernels)" if nparts > 1
                                      else " (partition kernel)"),
@@ -367,6 +475,7 @@ def main():
             "traffic": traffic,
             "algorithmic_bytes_per_launch": kv_bytes,
         },
+        "kernels": kernels,
         "cpu_baseline": None if cpu is None else {k: cpu[k] for k in
                                                   ("value", "unit", "cores", "kind", "sample")},
         "stream_read_gbps": stream_gbps,

@@ -143,14 +143,19 @@ pa_status pa_kv_append(void* kv_pool, const void* key, const void* value,
  *                 partitions merged by a log-sum-exp reduction
  *   workspace     device memory of at least pa_decode_workspace_bytes(...) bytes,
  *                 256-byte aligned (may be NULL when that size is 0); scratch only
+ *   flags         0 or PA_DECODE_KV_STREAM: every block is read by one sequence only in
+ *                 this call, so K/V loads carry the non-temporal cache hint (HBM
+ *                 streaming rate). Leave it off when sequences share prefix blocks, so
+ *                 shared blocks may be served from cache. Results are identical.
  * Query head h reads KV head h / (num_q_heads / num_kv_heads). Arithmetic: fp16
  * inputs, fp32 products, sums and softmax, fp16 output rounded to nearest even. */
+#define PA_DECODE_KV_STREAM 1u
 pa_status pa_decode(void* out, const void* q, const void* kv_pool, const int32_t* block_tables,
                     const int32_t* context_lens, int32_t num_seqs, int32_t num_q_heads,
                     int32_t num_kv_heads, int32_t head_size, int32_t block_size,
                     int32_t max_blocks_per_seq, int64_t num_blocks, int32_t max_context_len,
                     float scale, int32_t partition_size, void* workspace,
-                    int64_t workspace_bytes, void* stream);
+                    int64_t workspace_bytes, uint32_t flags, void* stream);
 
 /* Causal attention of prefill chunks over their paged context (the scheduler on
  * page "vLLM 部署深度指南" puts prefills and decodes into one step). Request r owns

@@ -27,6 +27,7 @@ from ._lib import (  # noqa: F401
     pa_slot,
     pa_stream_read,
     pa_stream_read_sink_len,
+    PA_DECODE_KV_STREAM,
     PA_OK,
     PA_ERR_INVALID,
     PA_ERR_UNSUPPORTED,

@@ -19,6 +19,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libpagedkv.so")
 
 PA_OK, PA_ERR_INVALID, PA_ERR_UNSUPPORTED, PA_ERR_WORKSPACE, PA_ERR_HIP = range(5)
+PA_DECODE_KV_STREAM = 1
 
 _i32, _i64, _f32, _f64, _vp = ctypes.c_int32, ctypes.c_int64, ctypes.c_float, ctypes.c_double, ctypes.c_void_p
 
@@ -37,7 +38,7 @@ SIGNATURES = {
     "pa_decode_workspace_bytes": (_i64, [_i32, _i32, _i32, _i32, _i32]),
     "pa_kv_append": (ctypes.c_int, [_vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i64, _i64, _i64, _vp]),
     "pa_decode": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _i64,
-                                 _i32, _f32, _i32, _vp, _i64, _vp]),
+                                 _i32, _f32, _i32, _vp, _i64, ctypes.c_uint32, _vp]),
     "pa_prefill_chunk": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32,
                                         _i32, _i32, _i32, _i32, _i64, _f32, _vp]),
     "pa_gather_kv": (ctypes.c_int, [_vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i64, _vp]),
@@ -175,12 +176,13 @@ def pa_kv_append(kv_pool, key, value, slot_mapping, stream=None):
 
 
 def pa_decode(out, q, kv_pool, block_tables, context_lens, max_context_len, scale=None,
-              partition_size=512, workspace=None, stream=None):
+              partition_size=512, workspace=None, flags=0, stream=None):
     """Paged decode: out[b] = attention of q[b] ([B, Hq, D]) over its first context_lens[b] tokens.
 
     ``max_context_len`` is a host upper bound of context_lens. ``workspace`` is a device
     uint8 tensor of at least :func:`pa_decode_workspace_bytes` bytes; one is allocated
-    here when it is None.
+    here when it is None. ``flags``: 0 or ``PA_DECODE_KV_STREAM`` (no block is shared
+    between the sequences of the call; K/V loads bypass cache retention).
     """
     nb, bs, hkv, d = _pool_geometry(kv_pool)
     B, hq, dq = q.shape
@@ -202,7 +204,7 @@ def pa_decode(out, q, kv_pool, block_tables, context_lens, max_context_len, scal
         _dense(kv_pool, "kv_pool", torch.float16), _dense(block_tables, "block_tables", torch.int32),
         _dense(context_lens, "context_lens", torch.int32), B, hq, hkv, d, bs,
         int(block_tables.shape[1]), nb, int(max_context_len), float(scale), int(partition_size),
-        ws_p, ws_n, _stream(stream))
+        ws_p, ws_n, int(flags), _stream(stream))
     _check("pa_decode", st)
 
 

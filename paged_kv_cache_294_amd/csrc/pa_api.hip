@@ -158,13 +158,14 @@ PA_EXPORT pa_status pa_decode(void* out, const void* q, const void* kv_pool,
                               int32_t head_size, int32_t block_size, int32_t max_blocks_per_seq,
                               int64_t num_blocks, int32_t max_context_len, float scale,
                               int32_t partition_size, void* workspace, int64_t workspace_bytes,
-                              void* stream) {
+                              uint32_t flags, void* stream) {
   if (num_seqs < 0 || max_blocks_per_seq <= 0 || num_blocks <= 0 || max_context_len < 0)
     return PA_ERR_INVALID;
   if (pa_status s = check_geometry(block_size, num_kv_heads, head_size)) return s;
   if (pa_status s = check_heads(num_q_heads, num_kv_heads)) return s;
   if (partition_size <= 0 || partition_size % block_size) return PA_ERR_INVALID;
   if (!std::isfinite(scale)) return PA_ERR_INVALID;
+  if (flags & ~PA_DECODE_KV_STREAM) return PA_ERR_INVALID;
   if (num_seqs > 65535) return PA_ERR_UNSUPPORTED;
   if ((int64_t)max_blocks_per_seq * block_size > INT32_MAX) return PA_ERR_INVALID;
   // the kernels address up to 16 tokens * 2 * Hkv * D elements inside a block as int32
@@ -190,6 +191,7 @@ PA_EXPORT pa_status pa_decode(void* out, const void* q, const void* kv_pool,
   a.num_partitions = pa_num_partitions(max_context_len, partition_size);
   if (a.num_partitions > 65535) return PA_ERR_UNSUPPORTED;
   a.scale_log2 = (float)((double)scale * kLog2e);
+  a.stream_kv = (flags & PA_DECODE_KV_STREAM) != 0;
   if (a.num_partitions > 1) {
     const int64_t need = pa_decode_workspace_bytes(num_seqs, num_q_heads, max_context_len,
                                                    partition_size, head_size);
@@ -267,5 +269,6 @@ PA_EXPORT int64_t pa_stream_read_sink_len(int64_t bytes) {
 
 PA_EXPORT pa_status pa_stream_read(const void* buf, int64_t bytes, float* sink, void* stream) {
   if (!buf || !sink || bytes <= 0 || bytes % 16 || !aligned16(buf)) return PA_ERR_INVALID;
+  if (pkv::stream_read_groups(bytes) > INT32_MAX) return PA_ERR_UNSUPPORTED;
   return hip_status(pkv::launch_stream_read(buf, bytes, sink, (hipStream_t)stream));
 }

@@ -53,7 +53,7 @@ __device__ __forceinline__ void write_const_rows(const DecodeArgs& a, int b, int
   }
 }
 
-template <int D, int G>
+template <int D, int G, bool Stream>
 __global__ __launch_bounds__(kThreads) void decode_partition_kernel(const DecodeArgs a) {
   using Gm = Geo<D>;
   constexpr int LPT = Gm::kLanesPerToken;
@@ -115,8 +115,8 @@ __global__ __launch_bounds__(kThreads) void decode_partition_kernel(const Decode
     const half_t* base = pool + (bad_table ? 0 : (int64_t)phys * block_elems) + lane_off;
 #pragma unroll
     for (int i = 0; i < LPB; ++i) {
-      kc[i] = *reinterpret_cast<const half8_t*>(base + i * TPL * tok_stride);
-      vc[i] = *reinterpret_cast<const half8_t*>(base + i * TPL * tok_stride + kv_row);
+      kc[i] = load16<Stream>(base + i * TPL * tok_stride);
+      vc[i] = load16<Stream>(base + i * TPL * tok_stride + kv_row);
     }
   }
 
@@ -132,8 +132,8 @@ __global__ __launch_bounds__(kThreads) void decode_partition_kernel(const Decode
       const half_t* base = pool + (bad_table ? 0 : (int64_t)phys * block_elems) + lane_off;
 #pragma unroll
       for (int i = 0; i < LPB; ++i) {
-        kn[i] = *reinterpret_cast<const half8_t*>(base + i * TPL * tok_stride);
-        vn[i] = *reinterpret_cast<const half8_t*>(base + i * TPL * tok_stride + kv_row);
+        kn[i] = load16<Stream>(base + i * TPL * tok_stride);
+        vn[i] = load16<Stream>(base + i * TPL * tok_stride + kv_row);
       }
     }
 
@@ -291,7 +291,10 @@ __global__ __launch_bounds__(kThreads) void decode_reduce_kernel(const DecodeArg
 template <int D, int G>
 hipError_t launch_decode_dg(const DecodeArgs& a, hipStream_t stream) {
   dim3 grid((a.num_kv_heads + kWavesPerGroup - 1) / kWavesPerGroup, a.num_partitions, a.num_seqs);
-  hipLaunchKernelGGL((decode_partition_kernel<D, G>), grid, dim3(kThreads), 0, stream, a);
+  if (a.stream_kv)
+    hipLaunchKernelGGL((decode_partition_kernel<D, G, true>), grid, dim3(kThreads), 0, stream, a);
+  else
+    hipLaunchKernelGGL((decode_partition_kernel<D, G, false>), grid, dim3(kThreads), 0, stream, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.num_partitions == 1) return e;
   dim3 rgrid((a.num_q_heads + kWavesPerGroup - 1) / kWavesPerGroup, a.num_seqs);

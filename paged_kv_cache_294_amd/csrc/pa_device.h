@@ -49,6 +49,15 @@ __device__ __forceinline__ float group_sum(float x) {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// 16-byte load; with Stream the load carries the non-temporal hint, for data read once.
+template <bool Stream>
+__device__ __forceinline__ half8_t load16(const half_t* p) {
+  if constexpr (Stream)
+    return __builtin_nontemporal_load(reinterpret_cast<const half8_t*>(p));
+  else
+    return *reinterpret_cast<const half8_t*>(p);
+}
+
 __device__ __forceinline__ float dot8(half8_t a, half8_t b, float acc) {
   acc = __builtin_amdgcn_fdot2(half2_t{a[0], a[1]}, half2_t{b[0], b[1]}, acc, false);
   acc = __builtin_amdgcn_fdot2(half2_t{a[2], a[3]}, half2_t{b[2], b[3]}, acc, false);

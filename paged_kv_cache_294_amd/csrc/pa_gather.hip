@@ -29,23 +29,29 @@ __global__ __launch_bounds__(kThreads) void gather_kv_kernel(
 }
 
 constexpr int kReadUnroll = 4;
-constexpr int64_t kMaxReadGroups = 256 * 16;
+constexpr int64_t kReadChunk = 16384;  // 16-byte pieces per workgroup (256 KiB)
 
-__global__ __launch_bounds__(kThreads) void stream_read_kernel(const uint4* __restrict__ buf,
+// Each workgroup streams one contiguous 256 KiB chunk with non-temporal 16-byte loads,
+// the fastest read shape measured on MI355X.
+__global__ __launch_bounds__(kThreads) void stream_read_kernel(const half8_t* __restrict__ buf,
                                                                int64_t n16, float* __restrict__ sink) {
-  const int64_t stride = (int64_t)gridDim.x * kThreads;
-  int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+  const int64_t base = (int64_t)blockIdx.x * kReadChunk;
+  const int64_t end = base + kReadChunk < n16 ? base + kReadChunk : n16;
   uint32_t acc = 0;
-  for (; i + (kReadUnroll - 1) * stride < n16; i += kReadUnroll * stride) {
-    uint4 v[kReadUnroll];
+  int64_t i = base + threadIdx.x;
+  for (; i + (kReadUnroll - 1) * kThreads < end; i += kReadUnroll * kThreads) {
+    half8_t v[kReadUnroll];
 #pragma unroll
-    for (int u = 0; u < kReadUnroll; ++u) v[u] = buf[i + u * stride];
+    for (int u = 0; u < kReadUnroll; ++u) v[u] = __builtin_nontemporal_load(buf + i + u * kThreads);
 #pragma unroll
-    for (int u = 0; u < kReadUnroll; ++u) acc ^= v[u].x ^ v[u].y ^ v[u].z ^ v[u].w;
+    for (int u = 0; u < kReadUnroll; ++u) {
+      const uint4 w = __builtin_bit_cast(uint4, v[u]);
+      acc ^= w.x ^ w.y ^ w.z ^ w.w;
+    }
   }
-  for (; i < n16; i += stride) {
-    const uint4 v = buf[i];
-    acc ^= v.x ^ v.y ^ v.z ^ v.w;
+  for (; i < end; i += kThreads) {
+    const uint4 w = __builtin_bit_cast(uint4, buf[i]);
+    acc ^= w.x ^ w.y ^ w.z ^ w.w;
   }
   // fold the wave, then one lane per wave writes; a non-zero xor is what the caller sees
   for (int o = 32; o >= 1; o >>= 1) acc ^= __shfl_xor(acc, o, kWave);
@@ -74,15 +80,14 @@ hipError_t launch_gather_kv(void* k_out, void* v_out, const void* pool, const in
 
 int64_t stream_read_groups(int64_t bytes) {
   const int64_t n16 = bytes / 16;
-  int64_t g = (n16 + kThreads * kReadUnroll - 1) / (kThreads * kReadUnroll);
-  if (g > kMaxReadGroups) g = kMaxReadGroups;
+  const int64_t g = (n16 + kReadChunk - 1) / kReadChunk;
   return g < 1 ? 1 : g;
 }
 
 hipError_t launch_stream_read(const void* buf, int64_t bytes, float* sink, hipStream_t stream) {
   const int64_t groups = stream_read_groups(bytes);
   hipLaunchKernelGGL(stream_read_kernel, dim3((unsigned)groups), dim3(kThreads), 0, stream,
-                     static_cast<const uint4*>(buf), bytes / 16, sink);
+                     static_cast<const half8_t*>(buf), bytes / 16, sink);
   return hipGetLastError();
 }
 

@@ -26,6 +26,7 @@ struct DecodeArgs {
   int partition_blocks;  // partition size in blocks
   int num_partitions;    // partitions the grid covers
   float scale_log2;      // softmax scale * log2(e)
+  bool stream_kv;        // K/V loads carry the non-temporal hint (blocks read once per step)
 };
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
 

@@ -116,7 +116,8 @@ def decode_call(lib, **kw):
     args.update(kw)
     return lib.pa_decode(args["out"], args["q"], args["pool"], args["bt"], args["lens"], args["B"],
                          args["hq"], args["hkv"], args["d"], args["bs"], args["mb"], args["nb"],
-                         args["maxlen"], args["scale"], args["ps"], args["ws"], args["wsn"], None)
+                         args["maxlen"], args["scale"], args["ps"], args["ws"], args["wsn"],
+                         args.get("flags", 0), None)
 
 
 @pytest.mark.parametrize("kw,status", [
@@ -132,6 +133,7 @@ def decode_call(lib, **kw):
     (dict(scale=float("nan")), pkv.PA_ERR_INVALID),
     (dict(B=-1), pkv.PA_ERR_INVALID),
     (dict(nb=0), pkv.PA_ERR_INVALID),
+    (dict(flags=2), pkv.PA_ERR_INVALID),
 ])
 def test_decode_rejects(lib, kw, status):
     assert decode_call(lib, **kw) == status

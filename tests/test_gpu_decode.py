@@ -32,14 +32,14 @@ class Dev:
         if append and len(inp.slot_mapping):
             pkv.pa_kv_append(self.pool, dev(inp.key_new), dev(inp.value_new), dev(inp.slot_mapping))
 
-    def decode(self, partition_size=512, max_context_len=None):
+    def decode(self, partition_size=512, max_context_len=None, flags=0):
         inp = self.inp
         p = inp.num_prefill
         q = self.q[inp.num_prefill_tokens:]
         bt, lens = self.bt[p:], self.lens[p:]
         out = torch.empty_like(q)
         mcl = int(inp.seq_lens[p:].max()) if max_context_len is None else max_context_len
-        pkv.pa_decode(out, q, self.pool, bt, lens, mcl, inp.scale, partition_size)
+        pkv.pa_decode(out, q, self.pool, bt, lens, mcl, inp.scale, partition_size, flags=flags)
         return host(out)
 
 
@@ -193,16 +193,19 @@ def test_decode_length_one_rows_are_exact():
 def test_decode_config2_full():
     inp = cfg(2)
     d = Dev(inp)
-    got = d.decode()
+    got = d.decode(partition_size=256)
+    streamed = d.decode(partition_size=256, flags=pkv.PA_DECODE_KV_STREAM)
     del d
     free()
     check_attention(got, oracle_decode(inp), "config2")
+    # the cache hint changes no result bit
+    assert np.array_equal(bits(got), bits(streamed))
 
 
 def test_decode_config3_sampled():
     inp = cfg(3)
     d = Dev(inp)
-    outs = {ps: d.decode(partition_size=ps) for ps in (512, 2048)}
+    outs = {ps: d.decode(partition_size=ps, flags=pkv.PA_DECODE_KV_STREAM) for ps in (512, 2048)}
     del d
     free()
     rng = np.random.default_rng(0)
