@@ -6,7 +6,9 @@
 // Work split. One workgroup of four waves per (request, query head, 128-row tile of the
 // chunk); each wave owns 32 query rows. The KV context is streamed in tiles of 64
 // tokens (four 16-token blocks found through the table) and staged in LDS, double
-// buffered, shared by the four waves.
+// buffered, shared by the four waves. Workgroups are issued heaviest first: requests
+// in decreasing order of context length (ranked inside the kernel), and within a
+// request the later row tiles (which see more tokens) first.
 //
 // Contractions, both on v_mfma_f32_32x32x16_f16 (fp16 in, fp32 accumulate):
 //   S^T[token][row] = K[token][:] . Q[row][:]   (A = K rows from LDS, B = Q rows in
@@ -18,10 +20,11 @@
 // its token order inside each 16-token group is permuted so that the 8 tokens a lane
 // feeds to one product sit next to each other (one 16-byte LDS read per operand).
 //
-// Softmax. Online, fp32, per query row, in log2 units (scale * log2(e) applied to the
-// scores). Causal mask: chunk row i (position P + i) sees tokens 0 .. P + i; only tiles
-// crossing that diagonal or the end of the context are masked, and tiles past every row
-// of a wave are skipped by that wave.
+// Softmax. Online, fp32, per query row, in log2 units: p = 2^(s * scale * log2(e) - m).
+// The reference max m of a row moves only when a score exceeds it by more than 2^8, so
+// the accumulator rescale is rare and fp16 P stays <= 256. Causal mask: chunk row i
+// (position P + i) sees tokens 0 .. P + i; only tiles crossing that diagonal or the end
+// of the context are masked, and tiles past every row of a wave are skipped by it.
 #include "pa_device.h"
 #include "pa_launch.h"
 
@@ -31,7 +34,10 @@ namespace {
 constexpr int kBM = 128;     // query rows per workgroup
 constexpr int kWRows = 32;   // query rows per wave
 constexpr int kBN = 64;      // tokens per KV tile
+constexpr int kTileBlocks = kBN / kBlockSize;
 constexpr int kThreads = 256;
+constexpr int kMaxRanked = 256;  // requests ranked by length; larger batches keep their order
+constexpr float kRescaleSlack = 8.0f;  // log2 units the reference max may lag the true max
 
 __device__ __forceinline__ int vt_pos(int t) {
   // token order inside a 16-token group: 0-3, 8-11, 4-7, 12-15
@@ -41,7 +47,7 @@ __device__ __forceinline__ int vt_pos(int t) {
 
 template <int D>
 struct PrefillSmem {
-  static constexpr int KP = D + 8;     // K row pitch (halves): rows 16 B apart in bank space
+  static constexpr int KP = D + 8;     // K row pitch (halves)
   static constexpr int VP = kBN + 8;   // V^T row pitch (halves)
   half_t k[2][kBN * KP];
   half_t vt[2][D * VP];
@@ -52,6 +58,25 @@ __device__ __forceinline__ void write_rows(const PrefillArgs& a, int q0, int row
                                            float value) {
   half_t* out = static_cast<half_t*>(a.out) + ((int64_t)(q0 + row) * a.num_q_heads + h) * D;
   for (int d = 0; d < D; ++d) out[d] = (half_t)value;
+}
+
+// The request this workgroup serves: rank blockIdx.z in decreasing seq_len order (ties by
+// index). Every thread returns the same value.
+__device__ int request_of_rank(const PrefillArgs& a, int rank, int* slot) {
+  if (a.num_reqs > kMaxRanked) return rank;
+  if (threadIdx.x == 0) *slot = rank;
+  __syncthreads();
+  for (int r = threadIdx.x; r < a.num_reqs; r += kThreads) {
+    const int sr = a.seq_lens[r];
+    int k = 0;
+    for (int u = 0; u < a.num_reqs; ++u) {
+      const int su = a.seq_lens[u];
+      k += (su > sr) || (su == sr && u < r);
+    }
+    if (k == rank) *slot = r;
+  }
+  __syncthreads();
+  return *slot;
 }
 
 template <int D>
@@ -65,14 +90,15 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(const PrefillArgs 
   constexpr int KP = Smem::KP, VP = Smem::VP;
   extern __shared__ __align__(16) unsigned char smem_raw[];
   Smem& sm = *reinterpret_cast<Smem*>(smem_raw);
+  __shared__ int s_req;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int w = tid >> 6;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, uniform per wave
   const int g = lane >> 5;
-  const int r = blockIdx.z;
   const int h = blockIdx.y;
-  const int i0 = blockIdx.x * kBM;
+  const int r = request_of_rank(a, blockIdx.z, &s_req);
+  const int i0 = (gridDim.x - 1 - blockIdx.x) * kBM;
   const int kvh = h / (a.num_q_heads / a.num_kv_heads);
 
   const int q0 = a.query_start_loc[r];
@@ -110,60 +136,82 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(const PrefillArgs 
 
   const int kv_row = a.num_kv_heads * D;
   const int tok_stride = 2 * kv_row;
+  const int64_t block_elems = (int64_t)kBlockSize * tok_stride;
   const half_t* pool = static_cast<const half_t*>(a.pool);
   const int32_t* bt = a.block_tables + (int64_t)r * a.max_blocks_per_seq;
   const int nblk = (S + kBlockSize - 1) / kBlockSize;
-  bool bad_table = false;
+  int bad_table = 0;  // uniform: set when a table entry of the context lies outside the pool
 
-  // staging registers: K pieces (token tid/PIECES + j*256/PIECES, piece tid%PIECES) and V
-  // pieces (token pair tid%32, piece tid/32 + 8*round)
-  half8_t kreg[K_PER_THREAD], vreg[V_ROUNDS][2];
-
-  auto load_tile = [&](int t0) {
-    int phys[kBN / kBlockSize];
+  // Staging assignment, fixed for every tile. K piece j of this thread: token
+  // kt[j] = tid / PIECES + j * (256 / PIECES) of the tile, 16-byte piece tid % PIECES.
+  // V: token pair (2 * (tid % 32), +1), piece tid / 32 + 8 * round.
+  int koff[K_PER_THREAD], voff[V_ROUNDS][2];
 #pragma unroll
-    for (int jb = 0; jb < kBN / kBlockSize; ++jb) {
+  for (int j = 0; j < K_PER_THREAD; ++j) {
+    const int t = tid / PIECES + j * (kThreads / PIECES);
+    koff[j] = (t % kBlockSize) * tok_stride + kvh * D + 8 * (tid % PIECES);
+  }
+#pragma unroll
+  for (int rd = 0; rd < V_ROUNDS; ++rd)
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+      const int t = 2 * (tid & 31) + e;
+      voff[rd][e] = (t % kBlockSize) * tok_stride + kv_row + kvh * D + 8 * (tid / 32 + 8 * rd);
+    }
+  const int vblk = (2 * (tid & 31)) / kBlockSize;  // block (in the tile) of this thread's V pair
+
+  struct Stage {
+    half8_t k[K_PER_THREAD];
+    half8_t v[V_ROUNDS][2];
+  };
+  Stage sa, sb;  // two tiles in flight: staging is issued two tiles ahead of the compute
+
+  auto load_tile = [&](int t0, Stage& st) {
+    const half_t* base[kTileBlocks];
+    int ok = t0 + kBN <= S;
+#pragma unroll
+    for (int jb = 0; jb < kTileBlocks; ++jb) {
       const int blk = t0 / kBlockSize + jb;
-      phys[jb] = blk < nblk ? bt[blk] : -1;
-      if (blk < nblk && (phys[jb] < 0 || phys[jb] >= a.num_blocks)) {
-        bad_table = true;
-        phys[jb] = -1;
-      }
+      int phys = __builtin_amdgcn_readfirstlane(blk < nblk ? bt[blk] : 0);
+      const int out_of_pool = phys < 0 || phys >= a.num_blocks;
+      bad_table |= out_of_pool & (blk < nblk);
+      phys = out_of_pool ? 0 : phys;
+      base[jb] = pool + (int64_t)phys * block_elems;
     }
+    bad_table = __builtin_amdgcn_readfirstlane(bad_table);
+    ok = __builtin_amdgcn_readfirstlane(ok & !bad_table);
+    if (ok) {  // a full tile: every token exists, no checks
 #pragma unroll
-    for (int j = 0; j < K_PER_THREAD; ++j) {
-      const int p = tid + j * kThreads;
-      const int t = p / PIECES, c = p % PIECES;
-      const int pb = phys[t / kBlockSize];
-      if (t0 + t < S && pb >= 0)
-        kreg[j] = *reinterpret_cast<const half8_t*>(
-            pool + ((int64_t)pb * kBlockSize + t % kBlockSize) * tok_stride + kvh * D + 8 * c);
-      else
-        kreg[j] = half8_t{};
-    }
+      for (int j = 0; j < K_PER_THREAD; ++j)
+        st.k[j] = *reinterpret_cast<const half8_t*>(
+            base[(tid / PIECES + j * (kThreads / PIECES)) / kBlockSize] + koff[j]);
 #pragma unroll
-    for (int rd = 0; rd < V_ROUNDS; ++rd) {
-      const int c = tid / 32 + 8 * rd;
+      for (int rd = 0; rd < V_ROUNDS; ++rd)
 #pragma unroll
-      for (int e = 0; e < 2; ++e) {
-        const int t = 2 * (tid & 31) + e;
-        const int pb = phys[t / kBlockSize];
-        if (t0 + t < S && pb >= 0)
-          vreg[rd][e] = *reinterpret_cast<const half8_t*>(
-              pool + ((int64_t)pb * kBlockSize + t % kBlockSize) * tok_stride + kv_row + kvh * D +
-              8 * c);
-        else
-          vreg[rd][e] = half8_t{};
+        for (int e = 0; e < 2; ++e)
+          st.v[rd][e] = *reinterpret_cast<const half8_t*>(base[vblk] + voff[rd][e]);
+    } else {  // the context's last tile: tokens past S read as zeros
+#pragma unroll
+      for (int j = 0; j < K_PER_THREAD; ++j) {
+        const int t = tid / PIECES + j * (kThreads / PIECES);
+        const half8_t v = *reinterpret_cast<const half8_t*>(base[t / kBlockSize] + koff[j]);
+        st.k[j] = (t0 + t < S && !bad_table) ? v : half8_t{};
       }
+#pragma unroll
+      for (int rd = 0; rd < V_ROUNDS; ++rd)
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+          const half8_t v = *reinterpret_cast<const half8_t*>(base[vblk] + voff[rd][e]);
+          st.v[rd][e] = (t0 + 2 * (tid & 31) + e < S && !bad_table) ? v : half8_t{};
+        }
     }
   };
 
-  auto store_tile = [&](int buf) {
+  auto store_tile = [&](const Stage& st, int buf) {
 #pragma unroll
     for (int j = 0; j < K_PER_THREAD; ++j) {
-      const int p = tid + j * kThreads;
-      const int t = p / PIECES, c = p % PIECES;
-      *reinterpret_cast<half8_t*>(&sm.k[buf][t * KP + 8 * c]) = kreg[j];
+      const int t = tid / PIECES + j * (kThreads / PIECES);
+      *reinterpret_cast<half8_t*>(&sm.k[buf][t * KP + 8 * (tid % PIECES)]) = st.k[j];
     }
 #pragma unroll
     for (int rd = 0; rd < V_ROUNDS; ++rd) {
@@ -171,26 +219,24 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(const PrefillArgs 
       const int pos = vt_pos(2 * (tid & 31));  // even; the pair's second token follows it
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
-        half2_t pr = {vreg[rd][0][i], vreg[rd][1][i]};
+        half2_t pr = {st.v[rd][0][i], st.v[rd][1][i]};
         *reinterpret_cast<half2_t*>(&sm.vt[buf][(8 * c + i) * VP + pos]) = pr;
       }
     }
   };
 
+  const float c2 = a.scale_log2;
   float m = neg_inf(), l = 0.0f;
   float16_t o[DT];
 #pragma unroll
   for (int dt = 0; dt < DT; ++dt) o[dt] = float16_t{};
 
-  load_tile(0);
-  store_tile(0);
-  __syncthreads();
-
-  for (int it = 0; it < ntiles; ++it) {
+  // tile `it` is computed from LDS buffer it & 1 while tile it + 1 waits in registers
+  // (loaded one iteration earlier) and tile it + 2 is being loaded into the other set
+  auto iteration = [&](int it, const Stage& next, Stage& spare) {
     const int buf = it & 1;
     const int t0 = it * kBN;
-    const bool has_next = it + 1 < ntiles;
-    if (has_next) load_tile(t0 + kBN);
+    if (it + 2 < ntiles) load_tile(t0 + 2 * kBN, spare);
 
     if (t0 < wave_end) {
       // S^T for the tile's two 32-token halves
@@ -205,40 +251,46 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(const PrefillArgs 
           sacc[tt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(ka, qb[ks], sacc[tt], 0, 0, 0);
         }
       }
-      // scale, mask, online softmax for query row qrow
-      const bool full = (t0 + kBN <= P + row_w + 1) && (t0 + kBN <= S);
-      float mloc = neg_inf();
+      // mask the diagonal / context-end tile, then the row max of the raw scores
+      if (!((t0 + kBN <= P + row_w + 1) && (t0 + kBN <= S))) {
+        // token t is visible to this row iff t <= min(S - 1, P + qrow)
+        const int lim = min(S - 1, P + qrow) - (t0 + 4 * g);
+#pragma unroll
+        for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+          for (int v = 0; v < 16; ++v)
+            if (32 * tt + 8 * (v >> 2) + (v & 3) > lim) sacc[tt][v] = neg_inf();
+      }
+      float mraw = neg_inf();
 #pragma unroll
       for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          float s = sacc[tt][v] * a.scale_log2;
-          if (!full) {
-            const int t = t0 + 32 * tt + 8 * (v >> 2) + 4 * g + (v & 3);
-            if (t >= S || t > P + qrow) s = neg_inf();
-          }
-          sacc[tt][v] = s;
-          mloc = fmaxf(mloc, s);
-        }
-      mloc = fmaxf(mloc, __shfl_xor(mloc, 32, kWave));
-      const float mnew = fmaxf(m, mloc);
-      const float base = (mnew == neg_inf()) ? 0.0f : mnew;
-      const float alpha = fast_exp2(m - base);
+        for (int v = 0; v < 16; ++v) mraw = fmaxf(mraw, sacc[tt][v]);
+      mraw = fmaxf(mraw, __shfl_xor(mraw, 32, kWave));
+      const float mtile = mraw * c2;  // c2 > 0; -inf stays -inf
+      // move the reference max only when the tile beats it by more than the slack
+      const bool move = mtile > m + kRescaleSlack;
+      if (__builtin_amdgcn_ballot_w64(move)) {
+        const float mnew = move ? mtile : m;
+        const float alpha = fast_exp2(m - mnew);  // 0 when m was -inf, 1 when not moved
+        l *= alpha;
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) o[dt] *= alpha;
+        m = mnew;
+      }
+      const float base = (m == neg_inf()) ? 0.0f : m;
       float lsum = 0.0f;
       half8_t pb[4];
 #pragma unroll
       for (int kk = 0; kk < 4; ++kk)
 #pragma unroll
         for (int s = 0; s < 8; ++s) {
-          const float pv = fast_exp2(sacc[kk >> 1][8 * (kk & 1) + s] - base);
+          const float pv = fast_exp2(fmaf(sacc[kk >> 1][8 * (kk & 1) + s], c2, -base));
           lsum += pv;
           pb[kk][s] = (half_t)pv;
         }
       lsum += __shfl_xor(lsum, 32, kWave);
-      l = l * alpha + lsum;
-      m = mnew;
-#pragma unroll
-      for (int dt = 0; dt < DT; ++dt) o[dt] *= alpha;
+      l += lsum;
       // O^T += V^T P^T
 #pragma unroll
       for (int kk = 0; kk < 4; ++kk)
@@ -250,8 +302,17 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(const PrefillArgs 
         }
     }
 
-    if (has_next) store_tile(buf ^ 1);
+    if (it + 1 < ntiles) store_tile(next, buf ^ 1);
     __syncthreads();
+  };
+
+  load_tile(0, sa);
+  if (ntiles > 1) load_tile(kBN, sb);
+  store_tile(sa, 0);
+  __syncthreads();
+  for (int it = 0; it < ntiles; it += 2) {
+    iteration(it, sb, sa);
+    if (it + 1 < ntiles) iteration(it + 1, sa, sb);
   }
 
   if (qrow >= C) return;
