@@ -252,6 +252,223 @@ __global__ __launch_bounds__(kThreads) void decode_partition_kernel(const Decode
   }
 }
 
+// Grouped-query decode on the matrix cores: the G query heads that read one KV head are
+// the N side of 16x16 MFMA tiles (G <= 16 columns used). Per 16-token block:
+//   S^T[token][head] = K[token][:] . Q[head][:]     v_mfma_f32_16x16x32_f16, A = K rows
+//                                                    loaded from HBM straight into operand
+//                                                    layout, B = Q rows (zero past G)
+//   O^T[dim][head]  += V^T[dim][token] . P^T[token][head]   v_mfma_f32_16x16x16f16
+// Lane (n, q) = (lane % 16, lane / 16) holds S^T rows 4q..4q+3 of column n, which as fp16
+// is exactly its B operand of the second product. V^T comes from the block staged in LDS
+// in natural row-major order through the transposing LDS read (ds_read_b64_tr_b16): source
+// lane i of a 16-lane group points at V[4q + i/4][16dt + 4(i%4)] and lane n receives
+// V[4q + k][16dt + n], k = 0..3. Softmax per head (column) in fp32, base 2, with the
+// reference max moved only when it is beaten by more than 2^8.
+template <int D>
+struct GqaGeo {
+  static constexpr int KS = D / 32;          // k-steps of S^T
+  static constexpr int DT = D / 16;          // 16-dim tiles of O^T
+  static constexpr int PIECES = D / 8;       // 16-byte pieces per token row of one head
+  static constexpr int VLOADS = PIECES / 4;  // V pieces per lane per block
+  static constexpr int VPITCH = D + 16;      // LDS row pitch (halves): 8 rows fill 64 banks
+};
+
+template <int D, int G, bool Stream>
+__global__ __launch_bounds__(kThreads) void decode_gqa_kernel(const DecodeArgs a) {
+  static_assert(G >= 1 && G <= 16, "query heads per KV head must fit 16 columns");
+  using Gm = GqaGeo<D>;
+  constexpr int KS = Gm::KS, DT = Gm::DT, PIECES = Gm::PIECES, VLOADS = Gm::VLOADS;
+  constexpr int VPITCH = Gm::VPITCH;
+  constexpr float kSlack = 8.0f;
+  __shared__ __align__(16) half_t vstage[kWavesPerGroup][kBlockSize * VPITCH];
+
+  const int lane = threadIdx.x & (kWave - 1);
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int kvh = blockIdx.x * kWavesPerGroup + w;
+  const int p = blockIdx.y;
+  const int b = blockIdx.z;
+  if (kvh >= a.num_kv_heads) return;
+  const int n = lane & 15;   // token row of K / query-head column
+  const int q4 = lane >> 4;  // 16-lane group
+  half_t* vs = vstage[w];
+
+  const int L = a.context_lens[b];
+  const bool bad_len = L < 0 || L > a.max_context_len || L > a.max_blocks_per_seq * kBlockSize;
+  half_t* out = static_cast<half_t*>(a.out);
+  if (bad_len || L == 0) {
+    if (p == 0 && lane < G * PIECES) {
+      const int h = kvh * G + lane / PIECES;
+      half8_t v;
+#pragma unroll
+      for (int d = 0; d < 8; ++d) v[d] = (half_t)(bad_len ? qnan() : 0.0f);
+      *reinterpret_cast<half8_t*>(out + ((int64_t)b * a.num_q_heads + h) * D + 8 * (lane % PIECES)) = v;
+    }
+    return;
+  }
+  const int part_tokens = a.partition_blocks * kBlockSize;
+  const int nparts = (L + part_tokens - 1) / part_tokens;
+  if (p >= nparts) return;
+  const int blk_begin = p * a.partition_blocks;
+  const int blk_end = min(blk_begin + a.partition_blocks, (L + kBlockSize - 1) / kBlockSize);
+
+  // B operand of S^T: query head n's dims 32ks + 8q4 .. +8, zero past the group
+  const half_t* qp = static_cast<const half_t*>(a.q);
+  half8_t qb[KS];
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks)
+    qb[ks] = n < G ? load16(qp + ((int64_t)b * a.num_q_heads + (int64_t)kvh * G + n) * D + 32 * ks + 8 * q4)
+                   : half8_t{};
+
+  const int kv_row = a.num_kv_heads * D;
+  const int tok_stride = 2 * kv_row;
+  const int64_t block_elems = (int64_t)kBlockSize * tok_stride;
+  const half_t* pool = static_cast<const half_t*>(a.pool);
+  const int32_t* bt = a.block_tables + (int64_t)b * a.max_blocks_per_seq;
+  // per-lane element offsets inside a block
+  const int koff = n * tok_stride + kvh * D + 8 * q4;  // + 32 ks
+  int voff[VLOADS], vlds[VLOADS];
+#pragma unroll
+  for (int j = 0; j < VLOADS; ++j) {
+    const int idx = lane + kWave * j;
+    const int t = idx / PIECES, c = idx % PIECES;
+    voff[j] = t * tok_stride + kv_row + kvh * D + 8 * c;
+    vlds[j] = t * VPITCH + 8 * c;
+  }
+  // transposing read of V tile dt: token 4q4 + n/4, dims 16dt + 4(n%4)
+  const int vtr = (4 * q4 + n / 4) * VPITCH + 4 * (n % 4);
+
+  float m = neg_inf(), l = 0.0f;  // per column (head n); l is this lane's partial sum
+  float4_t o[DT];
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt) o[dt] = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
+
+  int bt_vec = (lane < blk_end - blk_begin) ? bt[blk_begin + lane] : 0;
+  bool bad_table = false;
+  half8_t kc[KS], vc[VLOADS];
+  {
+    const int phys = __builtin_amdgcn_readfirstlane(bt_vec);
+    bad_table = phys < 0 || phys >= a.num_blocks;
+    const half_t* base = pool + (bad_table ? 0 : (int64_t)phys * block_elems);
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) kc[ks] = load16<Stream>(base + koff + 32 * ks);
+#pragma unroll
+    for (int j = 0; j < VLOADS; ++j) vc[j] = load16<Stream>(base + voff[j]);
+  }
+
+  for (int jb = blk_begin; jb < blk_end && !bad_table; ++jb) {
+    half8_t kn[KS], vn[VLOADS];
+    const int jn = jb + 1;
+    if (jn < blk_end) {
+      const int k64 = (jn - blk_begin) & 63;
+      if (k64 == 0) bt_vec = (lane < blk_end - jn) ? bt[jn + lane] : 0;
+      const int phys = __builtin_amdgcn_readlane(bt_vec, k64);
+      bad_table = phys < 0 || phys >= a.num_blocks;
+      const half_t* base = pool + (bad_table ? 0 : (int64_t)phys * block_elems);
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) kn[ks] = load16<Stream>(base + koff + 32 * ks);
+#pragma unroll
+      for (int j = 0; j < VLOADS; ++j) vn[j] = load16<Stream>(base + voff[j]);
+    }
+    const int tok0 = jb * kBlockSize;
+    const bool tail = tok0 + kBlockSize > L;
+    // stage V (tokens past the context end as zeros: their slots may hold anything)
+#pragma unroll
+    for (int j = 0; j < VLOADS; ++j) {
+      const int t = (lane + kWave * j) / PIECES;
+      *reinterpret_cast<half8_t*>(vs + vlds[j]) = (tail && tok0 + t >= L) ? half8_t{} : vc[j];
+    }
+    // S^T of the block
+    float4_t sacc = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+      sacc = __builtin_amdgcn_mfma_f32_16x16x32_f16(kc[ks], qb[ks], sacc, 0, 0, 0);
+    // mask, column max over the block's 16 tokens, lazy rescale
+    float mloc = neg_inf();
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      if (tail && tok0 + 4 * q4 + i >= L) sacc[i] = neg_inf();
+      mloc = fmaxf(mloc, sacc[i]);
+    }
+    mloc = fmaxf(mloc, __shfl_xor(mloc, 16, kWave));
+    mloc = fmaxf(mloc, __shfl_xor(mloc, 32, kWave));
+    const float mb = mloc * a.scale_log2;
+    const bool move = mb > m + kSlack;
+    if (__builtin_amdgcn_ballot_w64(move)) {
+      asm volatile("");
+      const float mnew = move ? mb : m;
+      const float alpha = fast_exp2(m - mnew);
+      l *= alpha;
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) o[dt] *= alpha;
+      m = mnew;
+    }
+    const float base = (m == neg_inf()) ? 0.0f : m;
+    half4_t pb;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float pv = fast_exp2(fmaf(sacc[i], a.scale_log2, -base));
+      pb[i] = (half_t)pv;
+      l += (float)pb[i];
+    }
+    // the staged V must be visible to this wave's transposing reads
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) {
+      const half4_t va = __builtin_bit_cast(
+          half4_t, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                       (__attribute__((address_space(3))) short4_t*)(vs + vtr + 16 * dt)));
+      o[dt] = __builtin_amdgcn_mfma_f32_16x16x16f16(va, pb, o[dt], 0, 0, 0);
+    }
+    // the next block's V overwrites the stage only after these reads have returned
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) kc[ks] = kn[ks];
+#pragma unroll
+    for (int j = 0; j < VLOADS; ++j) vc[j] = vn[j];
+  }
+
+  // column sums over the four 16-lane groups
+  l += __shfl_xor(l, 16, kWave);
+  l += __shfl_xor(l, 32, kWave);
+  if (n >= G) return;
+  const int64_t bh = (int64_t)b * a.num_q_heads + (int64_t)kvh * G + n;
+  if (bad_table) {
+    if (nparts == 1) {
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) {
+        half4_t x;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) x[i] = (half_t)qnan();
+        *reinterpret_cast<half4_t*>(out + bh * D + 16 * dt + 4 * q4) = x;
+      }
+    } else if (q4 == 0) {
+      float* wml = a.ws_ml + (bh * a.num_partitions + p) * 2;
+      wml[0] = qnan();
+      wml[1] = qnan();
+    }
+    return;
+  }
+  const float inv = 1.0f / l;
+  if (nparts == 1) {
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) {
+      half4_t x;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) x[i] = (half_t)(o[dt][i] * inv);
+      *reinterpret_cast<half4_t*>(out + bh * D + 16 * dt + 4 * q4) = x;
+    }
+  } else {
+    float* wo = a.ws_o + (bh * a.num_partitions + p) * D;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) *reinterpret_cast<float4_t*>(wo + 16 * dt + 4 * q4) = o[dt] * inv;
+    if (q4 == 0) {
+      float* wml = a.ws_ml + (bh * a.num_partitions + p) * 2;
+      wml[0] = m;
+      wml[1] = l;
+    }
+  }
+}
+
 // Merge the partitions of every (sequence, query head) that has more than one.
 template <int D>
 __global__ __launch_bounds__(kThreads) void decode_reduce_kernel(const DecodeArgs a) {
@@ -291,10 +508,17 @@ __global__ __launch_bounds__(kThreads) void decode_reduce_kernel(const DecodeArg
 template <int D, int G>
 hipError_t launch_decode_dg(const DecodeArgs& a, hipStream_t stream) {
   dim3 grid((a.num_kv_heads + kWavesPerGroup - 1) / kWavesPerGroup, a.num_partitions, a.num_seqs);
-  if (a.stream_kv)
-    hipLaunchKernelGGL((decode_partition_kernel<D, G, true>), grid, dim3(kThreads), 0, stream, a);
-  else
-    hipLaunchKernelGGL((decode_partition_kernel<D, G, false>), grid, dim3(kThreads), 0, stream, a);
+  if constexpr (G == 1) {  // one query head per KV head: vector ALUs
+    if (a.stream_kv)
+      hipLaunchKernelGGL((decode_partition_kernel<D, 1, true>), grid, dim3(kThreads), 0, stream, a);
+    else
+      hipLaunchKernelGGL((decode_partition_kernel<D, 1, false>), grid, dim3(kThreads), 0, stream, a);
+  } else {  // a query-head group per KV head: matrix cores
+    if (a.stream_kv)
+      hipLaunchKernelGGL((decode_gqa_kernel<D, G, true>), grid, dim3(kThreads), 0, stream, a);
+    else
+      hipLaunchKernelGGL((decode_gqa_kernel<D, G, false>), grid, dim3(kThreads), 0, stream, a);
+  }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.num_partitions == 1) return e;
   dim3 rgrid((a.num_q_heads + kWavesPerGroup - 1) / kWavesPerGroup, a.num_seqs);

@@ -9,6 +9,7 @@ namespace pkv {
 typedef _Float16 half_t;
 typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
 typedef _Float16 half4_t __attribute__((ext_vector_type(4)));
+typedef short short4_t __attribute__((ext_vector_type(4)));
 typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
 typedef float float4_t __attribute__((ext_vector_type(4)));
 typedef float float16_t __attribute__((ext_vector_type(16)));
@@ -49,13 +50,19 @@ __device__ __forceinline__ float group_sum(float x) {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
-// 16-byte load; with Stream the load carries the non-temporal hint, for data read once.
-template <bool Stream>
+// 16-byte load from global memory. The explicit global address space keeps the compiler
+// from falling back to flat loads (which also count against the LDS wait counter) when
+// it cannot trace a pointer back to a kernel argument. With Stream the load carries the
+// non-temporal hint, for data read once.
+typedef __attribute__((address_space(1))) const half8_t gconst_half8_t;
+
+template <bool Stream = false>
 __device__ __forceinline__ half8_t load16(const half_t* p) {
+  gconst_half8_t* gp = (gconst_half8_t*)(p);
   if constexpr (Stream)
-    return __builtin_nontemporal_load(reinterpret_cast<const half8_t*>(p));
+    return __builtin_nontemporal_load(gp);
   else
-    return *reinterpret_cast<const half8_t*>(p);
+    return *gp;
 }
 
 __device__ __forceinline__ float dot8(half8_t a, half8_t b, float acc) {

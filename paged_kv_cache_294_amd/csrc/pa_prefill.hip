@@ -36,8 +36,17 @@ constexpr int kWRows = 32;   // query rows per wave
 constexpr int kBN = 64;      // tokens per KV tile
 constexpr int kTileBlocks = kBN / kBlockSize;
 constexpr int kThreads = 256;
+constexpr int kXcds = 8;     // accelerator dies of an MI355X, each with its own L2
 constexpr int kMaxRanked = 256;  // requests ranked by length; larger batches keep their order
 constexpr float kRescaleSlack = 8.0f;  // log2 units the reference max may lag the true max
+// instruction classes of __builtin_amdgcn_sched_group_barrier
+constexpr int kSchedValu = 0x002;
+constexpr int kSchedMfma = 0x008;
+constexpr int kSchedDsRead = 0x100;
+
+// An empty volatile asm statement: keeps a rarely taken branch a branch instead of letting
+// the compiler run its body unconditionally behind selects.
+__device__ __forceinline__ void keep_branch() { asm volatile(""); }
 
 __device__ __forceinline__ int vt_pos(int t) {
   // token order inside a 16-token group: 0-3, 8-11, 4-7, 12-15
@@ -96,9 +105,17 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(const PrefillArgs 
   const int lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, uniform per wave
   const int g = lane >> 5;
-  const int h = blockIdx.y;
-  const int r = request_of_rank(a, blockIdx.z, &s_req);
-  const int i0 = (gridDim.x - 1 - blockIdx.x) * kBM;
+  // Work item of this workgroup. Workgroups go to the 8 XCDs round-robin in launch order
+  // (workgroup i to XCD i % 8), each XCD with its own L2. All row tiles of one (request,
+  // head) share its K/V, so they are given to the same XCD; (request, head) groups are
+  // dealt to the XCDs in heaviest-first order and each group's later row tiles go first.
+  const int tiles = (a.max_q_len + kBM - 1) / kBM;
+  const int xcd = blockIdx.x % kXcds, slot = blockIdx.x / kXcds;
+  const int group = (slot / tiles) * kXcds + xcd;
+  if (group >= a.num_reqs * a.num_q_heads) return;  // padding of the grid (uniform per WG)
+  const int h = group % a.num_q_heads;
+  const int r = request_of_rank(a, group / a.num_q_heads, &s_req);
+  const int i0 = (tiles - 1 - slot % tiles) * kBM;
   const int kvh = h / (a.num_q_heads / a.num_kv_heads);
 
   const int q0 = a.query_start_loc[r];
@@ -124,8 +141,7 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(const PrefillArgs 
 #pragma unroll
   for (int ks = 0; ks < KS; ++ks) {
     if (qrow < C)
-      qb[ks] = *reinterpret_cast<const half8_t*>(
-          qp + ((int64_t)(q0 + qrow) * a.num_q_heads + h) * D + 16 * ks + 8 * g);
+      qb[ks] = load16(qp + ((int64_t)(q0 + qrow) * a.num_q_heads + h) * D + 16 * ks + 8 * g);
     else
       qb[ks] = half8_t{};
   }
@@ -164,11 +180,14 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(const PrefillArgs 
     half8_t k[K_PER_THREAD];
     half8_t v[V_ROUNDS][2];
   };
-  Stage sa, sb;  // two tiles in flight: staging is issued two tiles ahead of the compute
+  Stage st;  // the next tile, loaded while the current one is computed
 
+  // Loads are unconditional (a block outside the table or the pool reads block 0, which
+  // exists), so the loaded registers flow straight into the LDS store after the compute;
+  // tokens past the context end are zeroed at store time.
+  int st_t0 = 0;  // first token of the staged tile
   auto load_tile = [&](int t0, Stage& st) {
     const half_t* base[kTileBlocks];
-    int ok = t0 + kBN <= S;
 #pragma unroll
     for (int jb = 0; jb < kTileBlocks; ++jb) {
       const int blk = t0 / kBlockSize + jb;
@@ -179,35 +198,31 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(const PrefillArgs 
       base[jb] = pool + (int64_t)phys * block_elems;
     }
     bad_table = __builtin_amdgcn_readfirstlane(bad_table);
-    ok = __builtin_amdgcn_readfirstlane(ok & !bad_table);
-    if (ok) {  // a full tile: every token exists, no checks
+    st_t0 = t0;
 #pragma unroll
-      for (int j = 0; j < K_PER_THREAD; ++j)
-        st.k[j] = *reinterpret_cast<const half8_t*>(
-            base[(tid / PIECES + j * (kThreads / PIECES)) / kBlockSize] + koff[j]);
+    for (int j = 0; j < K_PER_THREAD; ++j)
+      st.k[j] = load16(base[(tid / PIECES + j * (kThreads / PIECES)) / kBlockSize] + koff[j]);
 #pragma unroll
-      for (int rd = 0; rd < V_ROUNDS; ++rd)
+    for (int rd = 0; rd < V_ROUNDS; ++rd)
 #pragma unroll
-        for (int e = 0; e < 2; ++e)
-          st.v[rd][e] = *reinterpret_cast<const half8_t*>(base[vblk] + voff[rd][e]);
-    } else {  // the context's last tile: tokens past S read as zeros
+      for (int e = 0; e < 2; ++e) st.v[rd][e] = load16(base[vblk] + voff[rd][e]);
+  };
+
+  auto store_tile = [&](Stage& st, int buf) {
+    if (__builtin_amdgcn_readfirstlane(st_t0 + kBN > S || bad_table)) {
+      // the context's last tile (or a bad table): tokens past the end become zeros
+      keep_branch();
 #pragma unroll
       for (int j = 0; j < K_PER_THREAD; ++j) {
         const int t = tid / PIECES + j * (kThreads / PIECES);
-        const half8_t v = *reinterpret_cast<const half8_t*>(base[t / kBlockSize] + koff[j]);
-        st.k[j] = (t0 + t < S && !bad_table) ? v : half8_t{};
+        if (st_t0 + t >= S || bad_table) st.k[j] = half8_t{};
       }
 #pragma unroll
       for (int rd = 0; rd < V_ROUNDS; ++rd)
 #pragma unroll
-        for (int e = 0; e < 2; ++e) {
-          const half8_t v = *reinterpret_cast<const half8_t*>(base[vblk] + voff[rd][e]);
-          st.v[rd][e] = (t0 + 2 * (tid & 31) + e < S && !bad_table) ? v : half8_t{};
-        }
+        for (int e = 0; e < 2; ++e)
+          if (st_t0 + 2 * (tid & 31) + e >= S || bad_table) st.v[rd][e] = half8_t{};
     }
-  };
-
-  auto store_tile = [&](const Stage& st, int buf) {
 #pragma unroll
     for (int j = 0; j < K_PER_THREAD; ++j) {
       const int t = tid / PIECES + j * (kThreads / PIECES);
@@ -231,88 +246,124 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(const PrefillArgs 
 #pragma unroll
   for (int dt = 0; dt < DT; ++dt) o[dt] = float16_t{};
 
-  // tile `it` is computed from LDS buffer it & 1 while tile it + 1 waits in registers
-  // (loaded one iteration earlier) and tile it + 2 is being loaded into the other set
-  auto iteration = [&](int it, const Stage& next, Stage& spare) {
+  // tile `it` is computed from LDS buffer it & 1 while tile it + 1 is loaded into
+  // registers; it is written to the other buffer after the compute
+  load_tile(0, st);
+  store_tile(st, 0);
+  __syncthreads();
+  for (int it = 0; it < ntiles; ++it) {
     const int buf = it & 1;
     const int t0 = it * kBN;
-    if (it + 2 < ntiles) load_tile(t0 + 2 * kBN, spare);
+    const bool has_next = it + 1 < ntiles;
+    if (has_next) load_tile(t0 + kBN, st);
 
     if (t0 < wave_end) {
-      // S^T for the tile's two 32-token halves
-      float16_t sacc[2];
-#pragma unroll
-      for (int tt = 0; tt < 2; ++tt) {
-        sacc[tt] = float16_t{};
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-          const half8_t ka = *reinterpret_cast<const half8_t*>(
-              &sm.k[buf][(32 * tt + (lane & 31)) * KP + 16 * ks + 8 * g]);
-          sacc[tt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(ka, qb[ks], sacc[tt], 0, 0, 0);
-        }
-      }
-      // mask the diagonal / context-end tile, then the row max of the raw scores
-      if (!((t0 + kBN <= P + row_w + 1) && (t0 + kBN <= S))) {
-        // token t is visible to this row iff t <= min(S - 1, P + qrow)
-        const int lim = min(S - 1, P + qrow) - (t0 + 4 * g);
-#pragma unroll
-        for (int tt = 0; tt < 2; ++tt)
-#pragma unroll
-          for (int v = 0; v < 16; ++v)
-            if (32 * tt + 8 * (v >> 2) + (v & 3) > lim) sacc[tt][v] = neg_inf();
-      }
-      float mraw = neg_inf();
+      // Per 32-token half h of the tile: S_h = S^T chain, then the softmax state update
+      // and P_h = exp2(...) in fp16, then O^T += V^T_h P_h. The exps of one half are
+      // interleaved with the MFMA chain of the next (S_1 or PV_0) so the matrix cores
+      // keep working while the vector ALUs do the softmax.
+      const int diag = __builtin_amdgcn_readfirstlane(!((t0 + kBN <= P + row_w + 1) && (t0 + kBN <= S)));
+      const int lim = min(S - 1, P + qrow) - (t0 + 4 * g);  // last visible token, tile-relative
+      half8_t ka[2][KS];
 #pragma unroll
       for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
+        for (int ks = 0; ks < KS; ++ks)
+          ka[tt][ks] = *reinterpret_cast<const half8_t*>(
+              &sm.k[buf][(32 * tt + (lane & 31)) * KP + 16 * ks + 8 * g]);
+      __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2 * KS, 0);
+      float16_t sacc[2];
+      sacc[0] = float16_t{};
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks)
+        sacc[0] = __builtin_amdgcn_mfma_f32_32x32x16_f16(ka[0][ks], qb[ks], sacc[0], 0, 0, 0);
+
+      // softmax state update of half tt: mask, row max, lazy rescale; returns the exp base
+      auto update = [&](int tt) -> float {
+        if (diag) {
+          keep_branch();
+#pragma unroll
+          for (int v = 0; v < 16; ++v)
+            if (32 * tt + 8 * (v >> 2) + (v & 3) > lim) sacc[tt][v] = neg_inf();
+        }
+        float mraw = neg_inf();
+#pragma unroll
         for (int v = 0; v < 16; ++v) mraw = fmaxf(mraw, sacc[tt][v]);
-      mraw = fmaxf(mraw, __shfl_xor(mraw, 32, kWave));
-      const float mtile = mraw * c2;  // c2 > 0; -inf stays -inf
-      // move the reference max only when the tile beats it by more than the slack
-      const bool move = mtile > m + kRescaleSlack;
-      if (__builtin_amdgcn_ballot_w64(move)) {
-        const float mnew = move ? mtile : m;
-        const float alpha = fast_exp2(m - mnew);  // 0 when m was -inf, 1 when not moved
-        l *= alpha;
+        mraw = fmaxf(mraw, __shfl_xor(mraw, 32, kWave));
+        const float mh = mraw * c2;  // c2 > 0; -inf stays -inf
+        // move the reference max only when this half beats it by more than the slack
+        const bool move = mh > m + kRescaleSlack;
+        if (__builtin_amdgcn_ballot_w64(move)) {
+          keep_branch();
+          const float mnew = move ? mh : m;
+          const float alpha = fast_exp2(m - mnew);  // 0 when m was -inf, 1 when not moved
+          l *= alpha;
 #pragma unroll
-        for (int dt = 0; dt < DT; ++dt) o[dt] *= alpha;
-        m = mnew;
+          for (int dt = 0; dt < DT; ++dt) o[dt] *= alpha;
+          m = mnew;
+        }
+        return (m == neg_inf()) ? 0.0f : m;
+      };
+      // P of half tt as the fp16 B operands of two PV k-steps; adds its row sum to l
+      auto probs = [&](int tt, float base, half8_t* pb) {
+#pragma unroll
+        for (int k = 0; k < 2; ++k)
+#pragma unroll
+          for (int e = 0; e < 8; ++e)
+            pb[k][e] = (half_t)fast_exp2(fmaf(sacc[tt][8 * k + e], c2, -base));
+        float lsum = 0.0f;
+        const half2_t ones = {(half_t)1.0f, (half_t)1.0f};
+#pragma unroll
+        for (int k = 0; k < 2; ++k)
+#pragma unroll
+          for (int e = 0; e < 8; e += 2)
+            lsum = __builtin_amdgcn_fdot2(half2_t{pb[k][e], pb[k][e + 1]}, ones, lsum, false);
+        lsum += __shfl_xor(lsum, 32, kWave);
+        l += lsum;
+      };
+      auto pv = [&](int tt, const half8_t* pb) {
+        half8_t va[2][DT];
+#pragma unroll
+        for (int k = 0; k < 2; ++k)
+#pragma unroll
+          for (int dt = 0; dt < DT; ++dt)
+            va[k][dt] = *reinterpret_cast<const half8_t*>(
+                &sm.vt[buf][(32 * dt + (lane & 31)) * VP + 16 * (2 * tt + k) + 8 * g]);
+#pragma unroll
+        for (int k = 0; k < 2; ++k)
+#pragma unroll
+          for (int dt = 0; dt < DT; ++dt)
+            o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(va[k][dt], pb[k], o[dt], 0, 0, 0);
+      };
+
+      half8_t pb0[2], pb1[2];
+      const float base0 = update(0);
+      // S_1 chain, interleaved with the exps of half 0
+      sacc[1] = float16_t{};
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks)
+        sacc[1] = __builtin_amdgcn_mfma_f32_32x32x16_f16(ka[1][ks], qb[ks], sacc[1], 0, 0, 0);
+      probs(0, base0, pb0);
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 1);
+        __builtin_amdgcn_sched_group_barrier(kSchedValu, 4, 1);
       }
-      const float base = (m == neg_inf()) ? 0.0f : m;
-      float lsum = 0.0f;
-      half8_t pb[4];
+      const float base1 = update(1);
+      // PV of half 0, interleaved with the exps of half 1
+      pv(0, pb0);
+      probs(1, base1, pb1);
+      __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2 * DT, 2);
 #pragma unroll
-      for (int kk = 0; kk < 4; ++kk)
-#pragma unroll
-        for (int s = 0; s < 8; ++s) {
-          const float pv = fast_exp2(fmaf(sacc[kk >> 1][8 * (kk & 1) + s], c2, -base));
-          lsum += pv;
-          pb[kk][s] = (half_t)pv;
-        }
-      lsum += __shfl_xor(lsum, 32, kWave);
-      l += lsum;
-      // O^T += V^T P^T
-#pragma unroll
-      for (int kk = 0; kk < 4; ++kk)
-#pragma unroll
-        for (int dt = 0; dt < DT; ++dt) {
-          const half8_t va = *reinterpret_cast<const half8_t*>(
-              &sm.vt[buf][(32 * dt + (lane & 31)) * VP + 16 * kk + 8 * g]);
-          o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(va, pb[kk], o[dt], 0, 0, 0);
-        }
+      for (int k = 0; k < 2 * DT; ++k) {
+        __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 2);
+        __builtin_amdgcn_sched_group_barrier(kSchedValu, 4, 2);
+      }
+      pv(1, pb1);
     }
 
-    if (it + 1 < ntiles) store_tile(next, buf ^ 1);
+    if (has_next) store_tile(st, buf ^ 1);
     __syncthreads();
-  };
-
-  load_tile(0, sa);
-  if (ntiles > 1) load_tile(kBN, sb);
-  store_tile(sa, 0);
-  __syncthreads();
-  for (int it = 0; it < ntiles; it += 2) {
-    iteration(it, sb, sa);
-    if (it + 1 < ntiles) iteration(it + 1, sa, sb);
   }
 
   if (qrow >= C) return;
@@ -339,8 +390,11 @@ hipError_t launch_prefill_d(const PrefillArgs& a, hipStream_t stream) {
     if (e != hipSuccess) return e;
     attr_set = true;
   }
-  dim3 grid((a.max_q_len + kBM - 1) / kBM, a.num_q_heads, a.num_reqs);
-  hipLaunchKernelGGL((prefill_kernel<D>), grid, dim3(kThreads), smem, stream, a);
+  const int64_t groups = (int64_t)a.num_reqs * a.num_q_heads;
+  const int64_t tiles = (a.max_q_len + kBM - 1) / kBM;
+  const int64_t wgs = (groups + kXcds - 1) / kXcds * kXcds * tiles;
+  if (wgs > INT32_MAX) return hipErrorInvalidValue;
+  hipLaunchKernelGGL((prefill_kernel<D>), dim3((unsigned)wgs), dim3(kThreads), smem, stream, a);
   return hipGetLastError();
 }
 
