@@ -31,6 +31,7 @@ namespace {
 
 constexpr int kWavesPerGroup = 4;
 constexpr int kThreads = kWavesPerGroup * kWave;
+constexpr int kXcds = 8;  // accelerator dies of an MI355X
 
 template <int D>
 struct Geo {
@@ -38,6 +39,34 @@ struct Geo {
   static constexpr int kTokensPerLoad = kWave / kLanesPerToken;         // 4 or 8
   static constexpr int kLoadsPerBlock = kBlockSize / kTokensPerLoad;    // 4 or 2
 };
+
+// Work item (KV-head group, partition, sequence) of a workgroup. Workgroups reach the 8
+// XCDs round-robin in launch order (workgroup i to XCD i % 8), each XCD with its own L2.
+// The items of kSeqQuad consecutive sequences for one (partition, KV-head group) read the
+// same blocks when those sequences share prompt blocks, so they form a quad that runs on
+// one XCD in consecutive slots; quads are dealt to the XCDs round-robin, which keeps every
+// sequence's work spread over all XCDs.
+constexpr int kSeqQuad = 4;
+
+struct DecodeItem {
+  int hg, p, b;
+  bool valid;
+};
+
+__device__ __forceinline__ DecodeItem decode_item(const DecodeArgs& a) {
+  const int groups = (a.num_kv_heads + kWavesPerGroup - 1) / kWavesPerGroup;
+  const int64_t quads = (int64_t)((a.num_seqs + kSeqQuad - 1) / kSeqQuad) * a.num_partitions * groups;
+  const int xcd = blockIdx.x % kXcds;
+  const int slot = blockIdx.x / kXcds;
+  const int64_t quad = (int64_t)(slot / kSeqQuad) * kXcds + xcd;
+  DecodeItem it;
+  it.hg = (int)(quad % groups);
+  const int64_t rest = quad / groups;
+  it.p = (int)(rest % a.num_partitions);
+  it.b = (int)(rest / a.num_partitions) * kSeqQuad + slot % kSeqQuad;
+  it.valid = quad < quads && it.b < a.num_seqs;
+  return it;
+}
 
 template <int D, int G>
 __device__ __forceinline__ void write_const_rows(const DecodeArgs& a, int b, int kvh, int col,
@@ -61,9 +90,11 @@ __global__ __launch_bounds__(kThreads) void decode_partition_kernel(const Decode
   constexpr int LPB = Gm::kLoadsPerBlock;
 
   const int lane = threadIdx.x & (kWave - 1);
-  const int kvh = blockIdx.x * kWavesPerGroup + (threadIdx.x >> 6);
-  const int p = blockIdx.y;
-  const int b = blockIdx.z;
+  const DecodeItem item = decode_item(a);
+  if (!item.valid) return;
+  const int kvh = item.hg * kWavesPerGroup + (threadIdx.x >> 6);
+  const int p = item.p;
+  const int b = item.b;
   if (kvh >= a.num_kv_heads) return;
   const int row = lane / LPT;
   const int col = lane % LPT;
@@ -284,9 +315,11 @@ __global__ __launch_bounds__(kThreads) void decode_gqa_kernel(const DecodeArgs a
 
   const int lane = threadIdx.x & (kWave - 1);
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int kvh = blockIdx.x * kWavesPerGroup + w;
-  const int p = blockIdx.y;
-  const int b = blockIdx.z;
+  const DecodeItem item = decode_item(a);
+  if (!item.valid) return;
+  const int kvh = item.hg * kWavesPerGroup + w;
+  const int p = item.p;
+  const int b = item.b;
   if (kvh >= a.num_kv_heads) return;
   const int n = lane & 15;   // token row of K / query-head column
   const int q4 = lane >> 4;  // 16-lane group
@@ -507,7 +540,11 @@ __global__ __launch_bounds__(kThreads) void decode_reduce_kernel(const DecodeArg
 
 template <int D, int G>
 hipError_t launch_decode_dg(const DecodeArgs& a, hipStream_t stream) {
-  dim3 grid((a.num_kv_heads + kWavesPerGroup - 1) / kWavesPerGroup, a.num_partitions, a.num_seqs);
+  const int64_t groups = (a.num_kv_heads + kWavesPerGroup - 1) / kWavesPerGroup;
+  const int64_t quads = (int64_t)((a.num_seqs + kSeqQuad - 1) / kSeqQuad) * a.num_partitions * groups;
+  const int64_t wgs = (quads + kXcds - 1) / kXcds * kXcds * kSeqQuad;
+  if (wgs > INT32_MAX) return hipErrorInvalidValue;
+  const dim3 grid((unsigned)wgs);
   if constexpr (G == 1) {  // one query head per KV head: vector ALUs
     if (a.stream_kv)
       hipLaunchKernelGGL((decode_partition_kernel<D, 1, true>), grid, dim3(kThreads), 0, stream, a);
