@@ -4,27 +4,33 @@
 // (continuous-batching listing) runs such prefills in the same step as decodes.
 //
 // Work split. One workgroup of four waves per (request, query head, 128-row tile of the
-// chunk); each wave owns 32 query rows. The KV context is streamed in tiles of 64
-// tokens (four 16-token blocks found through the table) and staged in LDS, double
-// buffered, shared by the four waves. Workgroups are issued heaviest first: requests
-// in decreasing order of context length (ranked inside the kernel), and within a
-// request the later row tiles (which see more tokens) first.
+// chunk); each wave owns 32 query rows. Workgroups are issued heaviest first (requests in
+// decreasing order of context length, ranked inside the kernel; later row tiles first),
+// and all row tiles of one (request, head) go to the same XCD so they share its L2.
+//
+// Staging. The KV context is streamed in stages of 32 tokens (two 16-token blocks found
+// through the table). Each stage's K and V rows go from HBM straight into LDS with
+// global_load_lds_dwordx4 (a wave instruction fills 1 KB of LDS, 16 bytes per lane),
+// through a ring of four stages, so loads run three stages ahead of the matrix cores
+// without holding registers. Within each token row the 16-byte pieces are XOR-swizzled
+// by the token index (K by t & 7, V by 4 (t & 3), or 4 (t & 1) for 64-dim heads) to
+// spread LDS banks.
 //
 // Contractions, both on v_mfma_f32_32x32x16_f16 (fp16 in, fp32 accumulate):
 //   S^T[token][row] = K[token][:] . Q[row][:]   (A = K rows from LDS, B = Q rows in
 //                                                registers: both in natural row-major order)
 //   O^T[dim][row]  += V^T[dim][token] . P^T[token][row]
-// The S^T accumulator holds, in each lane, scores of one query row for 16 tokens of a
-// 32-token tile; converted to fp16 they are exactly the B operand of the second product,
-// so P never leaves registers. V is transposed once per tile while it is written to LDS;
-// its token order inside each 16-token group is permuted so that the 8 tokens a lane
-// feeds to one product sit next to each other (one 16-byte LDS read per operand).
+// A lane's S^T accumulator holds scores of one query row for 16 tokens of the stage; as
+// fp16 they are exactly its B operand of the second product, so P never leaves registers.
+// V^T comes from V kept in natural row-major order through the transposing LDS read
+// (ds_read_b64_tr_b16): in each 16-lane group, source lane i addresses V[t0 + i/4][d0 +
+// 4 (i%4)] and lane j receives V[t0 + k][d0 + j], k = 0..3.
 //
 // Softmax. Online, fp32, per query row, in log2 units: p = 2^(s * scale * log2(e) - m).
 // The reference max m of a row moves only when a score exceeds it by more than 2^8, so
 // the accumulator rescale is rare and fp16 P stays <= 256. Causal mask: chunk row i
-// (position P + i) sees tokens 0 .. P + i; only tiles crossing that diagonal or the end
-// of the context are masked, and tiles past every row of a wave are skipped by it.
+// (position P + i) sees tokens 0 .. P + i; only stages crossing that diagonal or the end
+// of the context are masked, and stages past every row of a wave are skipped by it.
 #include "pa_device.h"
 #include "pa_launch.h"
 
@@ -33,33 +39,65 @@ namespace {
 
 constexpr int kBM = 128;     // query rows per workgroup
 constexpr int kWRows = 32;   // query rows per wave
-constexpr int kBN = 64;      // tokens per KV tile
-constexpr int kTileBlocks = kBN / kBlockSize;
+constexpr int kBN = 32;      // tokens per stage
+constexpr int kStages = 4;   // ring depth
 constexpr int kThreads = 256;
 constexpr int kXcds = 8;     // accelerator dies of an MI355X, each with its own L2
 constexpr int kMaxRanked = 256;  // requests ranked by length; larger batches keep their order
 constexpr float kRescaleSlack = 8.0f;  // log2 units the reference max may lag the true max
-// instruction classes of __builtin_amdgcn_sched_group_barrier
-constexpr int kSchedValu = 0x002;
-constexpr int kSchedMfma = 0x008;
-constexpr int kSchedDsRead = 0x100;
+
+// 16 bytes per lane from global memory straight into LDS: lane i's bytes land at LDS byte
+// address lds_base + 16 i (global_load_lds_dwordx4; the LDS base goes through M0, which
+// the statement saves and restores). Written as inline assembly so the compiler does not
+// add its own conservative waits for these loads before every LDS read; the kernel waits
+// for them explicitly with wait_vm.
+__device__ __forceinline__ void load_lds16(const half_t* gsrc, uint32_t lds_base) {
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %2\n\t"
+      "global_load_lds_dwordx4 %1, off\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "v"(gsrc), "s"(lds_base)
+      : "memory");
+}
+
+template <typename T>
+__device__ __forceinline__ uint32_t lds_addr(T* p) {
+  return (uint32_t)(size_t)((__attribute__((address_space(3))) T*)p);
+}
 
 // An empty volatile asm statement: keeps a rarely taken branch a branch instead of letting
 // the compiler run its body unconditionally behind selects.
 __device__ __forceinline__ void keep_branch() { asm volatile(""); }
 
-__device__ __forceinline__ int vt_pos(int t) {
-  // token order inside a 16-token group: 0-3, 8-11, 4-7, 12-15
-  const int u = t & 15;
-  return (t & ~15) | (u & 3) | ((u & 4) << 1) | ((u & 8) >> 1);
+// Wait until at most N of this wave's vector-memory loads are outstanding.
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  // vmcnt low bits [3:0], high bits [15:14]; expcnt and lgkmcnt left at their maxima
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
+
+// Workgroup barrier after this wave's LDS operations have completed. Unlike
+// __syncthreads() it carries no memory fence, so staging loads still in flight (tracked by
+// the explicit vmcnt waits) are not drained; the "memory" clobber keeps the compiler from
+// moving LDS accesses across it.
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
+// XOR swizzles of the 16-byte pieces of a token row in LDS (results stay below D / 8)
+template <int D>
+__device__ __forceinline__ int kswz(int t) { return t & 7; }
+template <int D>
+__device__ __forceinline__ int vswz(int t) { return D >= 128 ? 4 * (t & 3) : 4 * (t & 1); }
 
 template <int D>
 struct PrefillSmem {
-  static constexpr int KP = D + 8;     // K row pitch (halves)
-  static constexpr int VP = kBN + 8;   // V^T row pitch (halves)
-  half_t k[2][kBN * KP];
-  half_t vt[2][D * VP];
+  static constexpr int ROW = D;                 // halves per token row (no padding)
+  static constexpr int TILE = kBN * ROW;        // halves per K (or V) stage
+  half_t k[kStages][TILE];
+  half_t v[kStages][TILE];
 };
 
 template <int D>
@@ -69,8 +107,8 @@ __device__ __forceinline__ void write_rows(const PrefillArgs& a, int q0, int row
   for (int d = 0; d < D; ++d) out[d] = (half_t)value;
 }
 
-// The request this workgroup serves: rank blockIdx.z in decreasing seq_len order (ties by
-// index). Every thread returns the same value.
+// The request with rank `rank` in decreasing seq_len order (ties by index). Every thread
+// returns the same value.
 __device__ int request_of_rank(const PrefillArgs& a, int rank, int* slot) {
   if (a.num_reqs > kMaxRanked) return rank;
   if (threadIdx.x == 0) *slot = rank;
@@ -92,11 +130,12 @@ template <int D>
 __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(const PrefillArgs a) {
   constexpr int KS = D / 16;          // k-steps of S^T (16 dims each)
   constexpr int DT = D / 32;          // 32-dim tiles of O^T
-  constexpr int PIECES = D / 8;       // 16-byte pieces per K (or V) row of one head
-  constexpr int K_PER_THREAD = kBN * PIECES / kThreads;
-  constexpr int V_ROUNDS = PIECES / 8;  // each round: 32 token pairs x 8 pieces
+  constexpr int PIECES = D / 8;       // 16-byte pieces per token row of one head
+  constexpr int TOK_PER_INST = kWave / PIECES;                   // token rows per wave load
+  constexpr int INST = kBN / TOK_PER_INST / (kThreads / kWave);  // K (or V) loads per wave/stage
+  static_assert(INST >= 1 && INST * TOK_PER_INST * (kThreads / kWave) == kBN, "stage split");
   using Smem = PrefillSmem<D>;
-  constexpr int KP = Smem::KP, VP = Smem::VP;
+  constexpr int ROW = Smem::ROW;
   extern __shared__ __align__(16) unsigned char smem_raw[];
   Smem& sm = *reinterpret_cast<Smem*>(smem_raw);
   __shared__ int s_req;
@@ -105,16 +144,16 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(const PrefillArgs 
   const int lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, uniform per wave
   const int g = lane >> 5;
-  // Work item of this workgroup. Workgroups go to the 8 XCDs round-robin in launch order
-  // (workgroup i to XCD i % 8), each XCD with its own L2. All row tiles of one (request,
-  // head) share its K/V, so they are given to the same XCD; (request, head) groups are
-  // dealt to the XCDs in heaviest-first order and each group's later row tiles go first.
+
+  // Work item of this workgroup (see the header comment on XCDs and order)
   const int tiles = (a.max_q_len + kBM - 1) / kBM;
   const int xcd = blockIdx.x % kXcds, slot = blockIdx.x / kXcds;
   const int group = (slot / tiles) * kXcds + xcd;
   if (group >= a.num_reqs * a.num_q_heads) return;  // padding of the grid (uniform per WG)
   const int h = group % a.num_q_heads;
-  const int r = request_of_rank(a, group / a.num_q_heads, &s_req);
+  // uniform, so the request's lengths and table entries are read with scalar loads (a vector
+  // load there would have to wait for every staging load in flight)
+  const int r = __builtin_amdgcn_readfirstlane(request_of_rank(a, group / a.num_q_heads, &s_req));
   const int i0 = (tiles - 1 - slot % tiles) * kBM;
   const int kvh = h / (a.num_q_heads / a.num_kv_heads);
 
@@ -138,105 +177,53 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(const PrefillArgs 
   const int qrow = row_w + (lane & 31);
   const half_t* qp = static_cast<const half_t*>(a.q);
   half8_t qb[KS];
-#pragma unroll
-  for (int ks = 0; ks < KS; ++ks) {
-    if (qrow < C)
-      qb[ks] = load16(qp + ((int64_t)(q0 + qrow) * a.num_q_heads + h) * D + 16 * ks + 8 * g);
-    else
-      qb[ks] = half8_t{};
-  }
 
   const int kv_end = min(S, P + min(i0 + kBM, C));               // tokens the workgroup sees
   const int wave_end = row_w < C ? P + min(row_w + kWRows, C) : 0;  // tokens this wave sees
-  const int ntiles = (kv_end + kBN - 1) / kBN;
+  const int nst = (kv_end + kBN - 1) / kBN;                       // stages
 
   const int kv_row = a.num_kv_heads * D;
   const int tok_stride = 2 * kv_row;
   const int64_t block_elems = (int64_t)kBlockSize * tok_stride;
   const half_t* pool = static_cast<const half_t*>(a.pool);
-  const int32_t* bt = a.block_tables + (int64_t)r * a.max_blocks_per_seq;
+  // the table is read-only here: through the constant address space the (uniform) entries
+  // come in with scalar loads, which do not wait behind the staging loads
+  const __attribute__((address_space(4))) int32_t* bt =
+      (const __attribute__((address_space(4))) int32_t*)(a.block_tables + (int64_t)r * a.max_blocks_per_seq);
   const int nblk = (S + kBlockSize - 1) / kBlockSize;
-  int bad_table = 0;  // uniform: set when a table entry of the context lies outside the pool
+  int bad_table = 0;  // uniform: a table entry of the context lies outside the pool
 
-  // Staging assignment, fixed for every tile. K piece j of this thread: token
-  // kt[j] = tid / PIECES + j * (256 / PIECES) of the tile, 16-byte piece tid % PIECES.
-  // V: token pair (2 * (tid % 32), +1), piece tid / 32 + 8 * round.
-  int koff[K_PER_THREAD], voff[V_ROUNDS][2];
+  // Loads of a stage. Wave w, load j fills token rows tj .. tj + TOK_PER_INST - 1 of the
+  // stage (tj = (w * INST + j) * TOK_PER_INST); lane l writes LDS slot l % PIECES of row
+  // tj + l / PIECES and reads global piece slot ^ swizzle(row).
+  int koff[INST], voff[INST];
 #pragma unroll
-  for (int j = 0; j < K_PER_THREAD; ++j) {
-    const int t = tid / PIECES + j * (kThreads / PIECES);
-    koff[j] = (t % kBlockSize) * tok_stride + kvh * D + 8 * (tid % PIECES);
+  for (int j = 0; j < INST; ++j) {
+    const int t = (w * INST + j) * TOK_PER_INST + lane / PIECES;
+    const int s = lane % PIECES;
+    koff[j] = (t % kBlockSize) * tok_stride + kvh * D + 8 * (s ^ kswz<D>(t));
+    voff[j] = (t % kBlockSize) * tok_stride + kv_row + kvh * D + 8 * (s ^ vswz<D>(t));
   }
+  auto issue_stage = [&](int st) {
+    const int t0 = st * kBN;
+    const half_t* base[kBN / kBlockSize];
 #pragma unroll
-  for (int rd = 0; rd < V_ROUNDS; ++rd)
-#pragma unroll
-    for (int e = 0; e < 2; ++e) {
-      const int t = 2 * (tid & 31) + e;
-      voff[rd][e] = (t % kBlockSize) * tok_stride + kv_row + kvh * D + 8 * (tid / 32 + 8 * rd);
-    }
-  const int vblk = (2 * (tid & 31)) / kBlockSize;  // block (in the tile) of this thread's V pair
-
-  struct Stage {
-    half8_t k[K_PER_THREAD];
-    half8_t v[V_ROUNDS][2];
-  };
-  Stage st;  // the next tile, loaded while the current one is computed
-
-  // Loads are unconditional (a block outside the table or the pool reads block 0, which
-  // exists), so the loaded registers flow straight into the LDS store after the compute;
-  // tokens past the context end are zeroed at store time.
-  int st_t0 = 0;  // first token of the staged tile
-  auto load_tile = [&](int t0, Stage& st) {
-    const half_t* base[kTileBlocks];
-#pragma unroll
-    for (int jb = 0; jb < kTileBlocks; ++jb) {
+    for (int jb = 0; jb < kBN / kBlockSize; ++jb) {
       const int blk = t0 / kBlockSize + jb;
-      int phys = __builtin_amdgcn_readfirstlane(blk < nblk ? bt[blk] : 0);
+      int phys = bt[min(blk, nblk - 1)];
       const int out_of_pool = phys < 0 || phys >= a.num_blocks;
       bad_table |= out_of_pool & (blk < nblk);
       phys = out_of_pool ? 0 : phys;
       base[jb] = pool + (int64_t)phys * block_elems;
     }
     bad_table = __builtin_amdgcn_readfirstlane(bad_table);
-    st_t0 = t0;
+    const int ring = st % kStages;
 #pragma unroll
-    for (int j = 0; j < K_PER_THREAD; ++j)
-      st.k[j] = load16(base[(tid / PIECES + j * (kThreads / PIECES)) / kBlockSize] + koff[j]);
-#pragma unroll
-    for (int rd = 0; rd < V_ROUNDS; ++rd)
-#pragma unroll
-      for (int e = 0; e < 2; ++e) st.v[rd][e] = load16(base[vblk] + voff[rd][e]);
-  };
-
-  auto store_tile = [&](Stage& st, int buf) {
-    if (__builtin_amdgcn_readfirstlane(st_t0 + kBN > S || bad_table)) {
-      // the context's last tile (or a bad table): tokens past the end become zeros
-      keep_branch();
-#pragma unroll
-      for (int j = 0; j < K_PER_THREAD; ++j) {
-        const int t = tid / PIECES + j * (kThreads / PIECES);
-        if (st_t0 + t >= S || bad_table) st.k[j] = half8_t{};
-      }
-#pragma unroll
-      for (int rd = 0; rd < V_ROUNDS; ++rd)
-#pragma unroll
-        for (int e = 0; e < 2; ++e)
-          if (st_t0 + 2 * (tid & 31) + e >= S || bad_table) st.v[rd][e] = half8_t{};
-    }
-#pragma unroll
-    for (int j = 0; j < K_PER_THREAD; ++j) {
-      const int t = tid / PIECES + j * (kThreads / PIECES);
-      *reinterpret_cast<half8_t*>(&sm.k[buf][t * KP + 8 * (tid % PIECES)]) = st.k[j];
-    }
-#pragma unroll
-    for (int rd = 0; rd < V_ROUNDS; ++rd) {
-      const int c = tid / 32 + 8 * rd;
-      const int pos = vt_pos(2 * (tid & 31));  // even; the pair's second token follows it
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        half2_t pr = {st.v[rd][0][i], st.v[rd][1][i]};
-        *reinterpret_cast<half2_t*>(&sm.vt[buf][(8 * c + i) * VP + pos]) = pr;
-      }
+    for (int j = 0; j < INST; ++j) {
+      const int tj = (w * INST + j) * TOK_PER_INST;  // first row of this load, uniform
+      const half_t* b = base[tj / kBlockSize];
+      load_lds16(b + koff[j], lds_addr(&sm.k[ring][tj * ROW]));
+      load_lds16(b + voff[j], lds_addr(&sm.v[ring][tj * ROW]));
     }
   };
 
@@ -246,124 +233,125 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(const PrefillArgs 
 #pragma unroll
   for (int dt = 0; dt < DT; ++dt) o[dt] = float16_t{};
 
-  // tile `it` is computed from LDS buffer it & 1 while tile it + 1 is loaded into
-  // registers; it is written to the other buffer after the compute
-  load_tile(0, st);
-  store_tile(st, 0);
-  __syncthreads();
-  for (int it = 0; it < ntiles; ++it) {
-    const int buf = it & 1;
+  // K operand row of this lane: token lane % 32 of the stage
+  const int krow = lane & 31;
+  // V^T operand: transposing reads of 4 tokens x 16 dims per 16-lane group
+  const int li = lane & 15;         // source lane inside the 16-lane group
+  const int dh = (lane >> 4) & 1;   // which 16 dims of the 32-dim tile
+  const int vtok = 4 * g + li / 4;  // token (within a 16-token k-step half) of this source lane
+
+  for (int st = 0; st < kStages - 1 && st < nst; ++st) issue_stage(st);
+  // the query rows come in behind the first stages, and one wait covers both: the compiler
+  // then knows of no load in flight inside the loop and leaves the waiting to the loop's
+  // own counted waits
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) {
+    if (qrow < C)
+      qb[ks] = load16(qp + ((int64_t)(q0 + qrow) * a.num_q_heads + h) * D + 16 * ks + 8 * g);
+    else
+      qb[ks] = half8_t{};
+  }
+  wait_vm<0>();
+
+  for (int it = 0; it < nst; ++it) {
+    // this wave's loads of stage `it` have landed once at most the loads of the stages
+    // issued after it are outstanding; the barrier makes every wave's loads visible and
+    // frees ring slot (it - 1) % kStages for stage it + kStages - 1
+    if (it + 2 < nst) wait_vm<4 * INST>();
+    else if (it + 1 < nst) wait_vm<2 * INST>();
+    else wait_vm<0>();
+    lds_barrier();
+    const int ring = it % kStages;
     const int t0 = it * kBN;
-    const bool has_next = it + 1 < ntiles;
-    if (has_next) load_tile(t0 + kBN, st);
+    if (__builtin_amdgcn_readfirstlane(t0 + kBN > S)) {
+      // the context's last stage: V rows past the end become zeros (their slots may hold
+      // anything, and 0 * NaN would reach the output)
+      keep_branch();
+      for (int e = tid; e < kBN * PIECES; e += kThreads) {
+        const int t = e / PIECES;
+        if (t0 + t >= S) *reinterpret_cast<half8_t*>(&sm.v[ring][t * ROW + 8 * (e % PIECES)]) = half8_t{};
+      }
+      lds_barrier();
+    }
+    if (it + kStages - 1 < nst) issue_stage(it + kStages - 1);
 
     if (t0 < wave_end) {
-      // Per 32-token half h of the tile: S_h = S^T chain, then the softmax state update
-      // and P_h = exp2(...) in fp16, then O^T += V^T_h P_h. The exps of one half are
-      // interleaved with the MFMA chain of the next (S_1 or PV_0) so the matrix cores
-      // keep working while the vector ALUs do the softmax.
+      // S^T for the stage's 32 tokens
+      half8_t ka[KS];
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks)
+        ka[ks] = *reinterpret_cast<const half8_t*>(
+            &sm.k[ring][krow * ROW + 8 * ((2 * ks + g) ^ kswz<D>(krow))]);
+      float16_t sacc = float16_t{};
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks)
+        sacc = __builtin_amdgcn_mfma_f32_32x32x16_f16(ka[ks], qb[ks], sacc, 0, 0, 0);
+
+      // mask the diagonal / context-end stage: token t visible iff t <= min(S-1, P+qrow)
       const int diag = __builtin_amdgcn_readfirstlane(!((t0 + kBN <= P + row_w + 1) && (t0 + kBN <= S)));
-      const int lim = min(S - 1, P + qrow) - (t0 + 4 * g);  // last visible token, tile-relative
-      half8_t ka[2][KS];
+      if (diag) {
+        keep_branch();
+        const int lim = min(S - 1, P + qrow) - (t0 + 4 * g);
 #pragma unroll
-      for (int tt = 0; tt < 2; ++tt)
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks)
-          ka[tt][ks] = *reinterpret_cast<const half8_t*>(
-              &sm.k[buf][(32 * tt + (lane & 31)) * KP + 16 * ks + 8 * g]);
-      __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2 * KS, 0);
-      float16_t sacc[2];
-      sacc[0] = float16_t{};
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks)
-        sacc[0] = __builtin_amdgcn_mfma_f32_32x32x16_f16(ka[0][ks], qb[ks], sacc[0], 0, 0, 0);
-
-      // softmax state update of half tt: mask, row max, lazy rescale; returns the exp base
-      auto update = [&](int tt) -> float {
-        if (diag) {
-          keep_branch();
-#pragma unroll
-          for (int v = 0; v < 16; ++v)
-            if (32 * tt + 8 * (v >> 2) + (v & 3) > lim) sacc[tt][v] = neg_inf();
-        }
-        float mraw = neg_inf();
-#pragma unroll
-        for (int v = 0; v < 16; ++v) mraw = fmaxf(mraw, sacc[tt][v]);
-        mraw = fmaxf(mraw, __shfl_xor(mraw, 32, kWave));
-        const float mh = mraw * c2;  // c2 > 0; -inf stays -inf
-        // move the reference max only when this half beats it by more than the slack
-        const bool move = mh > m + kRescaleSlack;
-        if (__builtin_amdgcn_ballot_w64(move)) {
-          keep_branch();
-          const float mnew = move ? mh : m;
-          const float alpha = fast_exp2(m - mnew);  // 0 when m was -inf, 1 when not moved
-          l *= alpha;
-#pragma unroll
-          for (int dt = 0; dt < DT; ++dt) o[dt] *= alpha;
-          m = mnew;
-        }
-        return (m == neg_inf()) ? 0.0f : m;
-      };
-      // P of half tt as the fp16 B operands of two PV k-steps; adds its row sum to l
-      auto probs = [&](int tt, float base, half8_t* pb) {
-#pragma unroll
-        for (int k = 0; k < 2; ++k)
-#pragma unroll
-          for (int e = 0; e < 8; ++e)
-            pb[k][e] = (half_t)fast_exp2(fmaf(sacc[tt][8 * k + e], c2, -base));
-        float lsum = 0.0f;
-        const half2_t ones = {(half_t)1.0f, (half_t)1.0f};
-#pragma unroll
-        for (int k = 0; k < 2; ++k)
-#pragma unroll
-          for (int e = 0; e < 8; e += 2)
-            lsum = __builtin_amdgcn_fdot2(half2_t{pb[k][e], pb[k][e + 1]}, ones, lsum, false);
-        lsum += __shfl_xor(lsum, 32, kWave);
-        l += lsum;
-      };
-      auto pv = [&](int tt, const half8_t* pb) {
-        half8_t va[2][DT];
-#pragma unroll
-        for (int k = 0; k < 2; ++k)
-#pragma unroll
-          for (int dt = 0; dt < DT; ++dt)
-            va[k][dt] = *reinterpret_cast<const half8_t*>(
-                &sm.vt[buf][(32 * dt + (lane & 31)) * VP + 16 * (2 * tt + k) + 8 * g]);
-#pragma unroll
-        for (int k = 0; k < 2; ++k)
-#pragma unroll
-          for (int dt = 0; dt < DT; ++dt)
-            o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(va[k][dt], pb[k], o[dt], 0, 0, 0);
-      };
-
-      half8_t pb0[2], pb1[2];
-      const float base0 = update(0);
-      // S_1 chain, interleaved with the exps of half 0
-      sacc[1] = float16_t{};
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks)
-        sacc[1] = __builtin_amdgcn_mfma_f32_32x32x16_f16(ka[1][ks], qb[ks], sacc[1], 0, 0, 0);
-      probs(0, base0, pb0);
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 1);
-        __builtin_amdgcn_sched_group_barrier(kSchedValu, 4, 1);
+        for (int v = 0; v < 16; ++v)
+          if (8 * (v >> 2) + (v & 3) > lim) sacc[v] = neg_inf();
       }
-      const float base1 = update(1);
-      // PV of half 0, interleaved with the exps of half 1
-      pv(0, pb0);
-      probs(1, base1, pb1);
-      __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2 * DT, 2);
+      float mraw = neg_inf();
 #pragma unroll
-      for (int k = 0; k < 2 * DT; ++k) {
-        __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 2);
-        __builtin_amdgcn_sched_group_barrier(kSchedValu, 4, 2);
+      for (int v = 0; v < 16; ++v) mraw = fmaxf(mraw, sacc[v]);
+      mraw = fmaxf(mraw, __shfl_xor(mraw, 32, kWave));
+      const float ms = mraw * c2;  // c2 > 0; -inf stays -inf
+      const bool move = ms > m + kRescaleSlack;
+      if (__builtin_amdgcn_ballot_w64(move)) {
+        keep_branch();
+        const float mnew = move ? ms : m;
+        const float alpha = fast_exp2(m - mnew);  // 0 when m was -inf, 1 when not moved
+        l *= alpha;
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) o[dt] *= alpha;
+        m = mnew;
       }
-      pv(1, pb1);
+      const float base = (m == neg_inf()) ? 0.0f : m;
+      half8_t pb[2];
+#pragma unroll
+      for (int k = 0; k < 2; ++k)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) pb[k][e] = (half_t)fast_exp2(fmaf(sacc[8 * k + e], c2, -base));
+      // the row sum of exactly the fp16 values the PV product uses (products exact, fp32 sum)
+      float lsum = 0.0f;
+      const half2_t ones = {(half_t)1.0f, (half_t)1.0f};
+#pragma unroll
+      for (int k = 0; k < 2; ++k)
+#pragma unroll
+        for (int e = 0; e < 8; e += 2)
+          lsum = __builtin_amdgcn_fdot2(half2_t{pb[k][e], pb[k][e + 1]}, ones, lsum, false);
+      lsum += __shfl_xor(lsum, 32, kWave);
+      l += lsum;
+
+      // O^T += V^T P^T: k-step k covers stage tokens 16k .. 16k+15; the lane's 8 k-slots
+      // are tokens 16k + 4g + {0..3} (first read) and 16k + 8 + 4g + {0..3} (second)
+      half8_t va[2][DT];
+#pragma unroll
+      for (int k = 0; k < 2; ++k)
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+          for (int hh = 0; hh < 2; ++hh) {
+            const int t = 16 * k + 8 * hh + vtok;
+            const int dim = 32 * dt + 16 * dh + 4 * (li % 4);
+            const int piece = (dim / 8) ^ vswz<D>(t);
+            const short4_t x = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (__attribute__((address_space(3))) short4_t*)&sm.v[ring][t * ROW + 8 * piece + (dim & 4)]);
+            const half4_t y = __builtin_bit_cast(half4_t, x);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) va[k][dt][4 * hh + e] = y[e];
+          }
+#pragma unroll
+      for (int k = 0; k < 2; ++k)
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt)
+          o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(va[k][dt], pb[k], o[dt], 0, 0, 0);
     }
-
-    if (has_next) store_tile(st, buf ^ 1);
-    __syncthreads();
   }
 
   if (qrow >= C) return;
