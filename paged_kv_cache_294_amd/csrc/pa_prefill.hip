@@ -46,20 +46,24 @@ constexpr int kXcds = 8;     // accelerator dies of an MI355X, each with its own
 constexpr int kMaxRanked = 256;  // requests ranked by length; larger batches keep their order
 constexpr float kRescaleSlack = 8.0f;  // log2 units the reference max may lag the true max
 
-// 16 bytes per lane from global memory straight into LDS: lane i's bytes land at LDS byte
-// address lds_base + 16 i (global_load_lds_dwordx4; the LDS base goes through M0, which
-// the statement saves and restores). Written as inline assembly so the compiler does not
-// add its own conservative waits for these loads before every LDS read; the kernel waits
-// for them explicitly with wait_vm.
-__device__ __forceinline__ void load_lds16(const half_t* gsrc, uint32_t lds_base) {
+// One K and one V load of a stage, 16 bytes per lane from global memory straight into LDS
+// (global_load_lds_dwordx4): lane i reads block + koff (resp. voff) and its bytes land at
+// LDS byte address kdst + 16 i (resp. vdst + 16 i). The LDS destination goes through M0,
+// which the statement saves and restores. Written as inline assembly so the compiler adds
+// none of its conservative waits for these loads before LDS reads; the kernel waits for
+// them itself with wait_vm.
+__device__ __forceinline__ void load_kv_lds16(const void* block, uint32_t koff, uint32_t voff,
+                                              uint32_t kdst, uint32_t vdst) {
   uint32_t saved;
   asm volatile(
       "s_mov_b32 %0, m0\n\t"
-      "s_mov_b32 m0, %2\n\t"
-      "global_load_lds_dwordx4 %1, off\n\t"
+      "s_mov_b32 m0, %3\n\t"
+      "global_load_lds_dwordx4 %1, %5\n\t"
+      "s_mov_b32 m0, %4\n\t"
+      "global_load_lds_dwordx4 %2, %5\n\t"
       "s_mov_b32 m0, %0"
       : "=&s"(saved)
-      : "v"(gsrc), "s"(lds_base)
+      : "v"(koff), "v"(voff), "s"(kdst), "s"(vdst), "s"(block)
       : "memory");
 }
 
@@ -184,47 +188,63 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(const PrefillArgs 
 
   const int kv_row = a.num_kv_heads * D;
   const int tok_stride = 2 * kv_row;
-  const int64_t block_elems = (int64_t)kBlockSize * tok_stride;
-  const half_t* pool = static_cast<const half_t*>(a.pool);
-  // the table is read-only here: through the constant address space the (uniform) entries
-  // come in with scalar loads, which do not wait behind the staging loads
-  const __attribute__((address_space(4))) int32_t* bt =
-      (const __attribute__((address_space(4))) int32_t*)(a.block_tables + (int64_t)r * a.max_blocks_per_seq);
+  const uint64_t block_bytes = (uint64_t)kBlockSize * tok_stride * sizeof(half_t);
+  const char* pool = static_cast<const char*>(a.pool);
+  const int32_t* bt = a.block_tables + (int64_t)r * a.max_blocks_per_seq;
   const int nblk = (S + kBlockSize - 1) / kBlockSize;
-  int bad_table = 0;  // uniform: a table entry of the context lies outside the pool
 
-  // Loads of a stage. Wave w, load j fills token rows tj .. tj + TOK_PER_INST - 1 of the
-  // stage (tj = (w * INST + j) * TOK_PER_INST); lane l writes LDS slot l % PIECES of row
-  // tj + l / PIECES and reads global piece slot ^ swizzle(row).
-  int koff[INST], voff[INST];
+  // Loads of a stage. Wave w fills token rows 8 w .. 8 w + 7 of each stage, all in block
+  // 2 st + w / 2 of the context; its load j covers rows tj .. tj + TOK_PER_INST - 1 (tj =
+  // (w INST + j) TOK_PER_INST), lane l writing LDS slot l % PIECES of row tj + l / PIECES
+  // and reading global piece slot ^ swizzle(row). Byte offsets inside the block:
+  uint32_t koff[INST], voff[INST];
 #pragma unroll
   for (int j = 0; j < INST; ++j) {
     const int t = (w * INST + j) * TOK_PER_INST + lane / PIECES;
-    const int s = lane % PIECES;
-    koff[j] = (t % kBlockSize) * tok_stride + kvh * D + 8 * (s ^ kswz<D>(t));
-    voff[j] = (t % kBlockSize) * tok_stride + kv_row + kvh * D + 8 * (s ^ vswz<D>(t));
+    const int sl = lane % PIECES;
+    koff[j] = 2u * ((t % kBlockSize) * tok_stride + kvh * D + 8 * (sl ^ kswz<D>(t)));
+    voff[j] = 2u * ((t % kBlockSize) * tok_stride + kv_row + kvh * D + 8 * (sl ^ vswz<D>(t)));
   }
+  const uint32_t lds_k0 = lds_addr(&sm.k[0][0]) + 2u * (w * INST * TOK_PER_INST * ROW);
+  constexpr uint32_t kStageBytes = 2u * Smem::TILE;
+  constexpr uint32_t kVBytes = kStages * kStageBytes;  // from sm.k to sm.v
+  constexpr uint32_t kInstBytes = 2u * TOK_PER_INST * ROW;
+
+  // Table entries of this wave's block in each stage, one stage per lane: register v of
+  // chunk c holds, in lane L, the entry for stage 64 (kTabRegs c + v) + L. Each lane also
+  // checks the entries of both blocks of its stage (uniform outcome across the waves): an
+  // entry of the context outside the pool makes the tile's rows NaN.
+  constexpr int kTabRegs = 2;
+  int tab[kTabRegs];
+  int bad_lanes = 0;
+  auto load_table = [&](int chunk) {
+#pragma unroll
+    for (int v = 0; v < kTabRegs; ++v) {
+      const int sidx = 64 * (kTabRegs * chunk + v) + lane;
+      int own = 0;
+#pragma unroll
+      for (int par = 0; par < 2; ++par) {
+        const int e = 2 * sidx + par;
+        const int x = bt[min(e, nblk - 1)];
+        const bool out_of_pool = x < 0 || x >= a.num_blocks;
+        bad_lanes |= (sidx < nst && e < nblk && out_of_pool);
+        if (par == (w >> 1)) own = out_of_pool ? 0 : x;
+      }
+      tab[v] = own;
+    }
+  };
   auto issue_stage = [&](int st) {
-    const int t0 = st * kBN;
-    const half_t* base[kBN / kBlockSize];
+    if (st > 0 && st % (64 * kTabRegs) == 0) load_table(st / (64 * kTabRegs));  // uniform
+    const int v = (st >> 6) % kTabRegs;
+    int cand = tab[0];
 #pragma unroll
-    for (int jb = 0; jb < kBN / kBlockSize; ++jb) {
-      const int blk = t0 / kBlockSize + jb;
-      int phys = bt[min(blk, nblk - 1)];
-      const int out_of_pool = phys < 0 || phys >= a.num_blocks;
-      bad_table |= out_of_pool & (blk < nblk);
-      phys = out_of_pool ? 0 : phys;
-      base[jb] = pool + (int64_t)phys * block_elems;
-    }
-    bad_table = __builtin_amdgcn_readfirstlane(bad_table);
-    const int ring = st % kStages;
+    for (int u = 1; u < kTabRegs; ++u) cand = (v == u) ? tab[u] : cand;
+    const int phys = __builtin_amdgcn_readlane(cand, st & 63);
+    const char* block = pool + (uint64_t)phys * block_bytes;
+    const uint32_t kdst = lds_k0 + (uint32_t)(st % kStages) * kStageBytes;
 #pragma unroll
-    for (int j = 0; j < INST; ++j) {
-      const int tj = (w * INST + j) * TOK_PER_INST;  // first row of this load, uniform
-      const half_t* b = base[tj / kBlockSize];
-      load_lds16(b + koff[j], lds_addr(&sm.k[ring][tj * ROW]));
-      load_lds16(b + voff[j], lds_addr(&sm.v[ring][tj * ROW]));
-    }
+    for (int j = 0; j < INST; ++j)
+      load_kv_lds16(block, koff[j], voff[j], kdst + j * kInstBytes, kdst + kVBytes + j * kInstBytes);
   };
 
   const float c2 = a.scale_log2;
@@ -240,6 +260,7 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(const PrefillArgs 
   const int dh = (lane >> 4) & 1;   // which 16 dims of the 32-dim tile
   const int vtok = 4 * g + li / 4;  // token (within a 16-token k-step half) of this source lane
 
+  load_table(0);
   for (int st = 0; st < kStages - 1 && st < nst; ++st) issue_stage(st);
   // the query rows come in behind the first stages, and one wait covers both: the compiler
   // then knows of no load in flight inside the loop and leaves the waiting to the loop's
@@ -299,12 +320,14 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(const PrefillArgs 
       float mraw = neg_inf();
 #pragma unroll
       for (int v = 0; v < 16; ++v) mraw = fmaxf(mraw, sacc[v]);
-      mraw = fmaxf(mraw, __shfl_xor(mraw, 32, kWave));
       const float ms = mraw * c2;  // c2 > 0; -inf stays -inf
-      const bool move = ms > m + kRescaleSlack;
-      if (__builtin_amdgcn_ballot_w64(move)) {
+      // lanes l and l ^ 32 hold the same row's scores for different tokens: a row's max
+      // moves iff one of its halves' maxima does, and only then do the halves exchange
+      // them (so both keep the same reference max)
+      if (__builtin_amdgcn_ballot_w64(ms > m + kRescaleSlack)) {
         keep_branch();
-        const float mnew = move ? ms : m;
+        const float mrow = fmaxf(ms, __shfl_xor(ms, 32, kWave));
+        const float mnew = mrow > m + kRescaleSlack ? mrow : m;
         const float alpha = fast_exp2(m - mnew);  // 0 when m was -inf, 1 when not moved
         l *= alpha;
 #pragma unroll
@@ -325,8 +348,7 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(const PrefillArgs 
 #pragma unroll
         for (int e = 0; e < 8; e += 2)
           lsum = __builtin_amdgcn_fdot2(half2_t{pb[k][e], pb[k][e + 1]}, ones, lsum, false);
-      lsum += __shfl_xor(lsum, 32, kWave);
-      l += lsum;
+      l += lsum;  // this half's tokens; the halves are added at the end
 
       // O^T += V^T P^T: k-step k covers stage tokens 16k .. 16k+15; the lane's 8 k-slots
       // are tokens 16k + 4g + {0..3} (first read) and 16k + 8 + 4g + {0..3} (second)
@@ -354,6 +376,8 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(const PrefillArgs 
     }
   }
 
+  l += __shfl_xor(l, 32, kWave);
+  const bool bad_table = __builtin_amdgcn_ballot_w64(bad_lanes) != 0;
   if (qrow >= C) return;
   half_t* out = static_cast<half_t*>(a.out) + ((int64_t)(q0 + qrow) * a.num_q_heads + h) * D;
   const float inv = bad_table ? qnan() : 1.0f / l;
