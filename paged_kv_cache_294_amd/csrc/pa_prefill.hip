@@ -11,10 +11,11 @@
 // Staging. The KV context is streamed in stages of 32 tokens (two 16-token blocks found
 // through the table). Each stage's K and V rows go from HBM straight into LDS with
 // global_load_lds_dwordx4 (a wave instruction fills 1 KB of LDS, 16 bytes per lane),
-// through a ring of four stages, so loads run three stages ahead of the matrix cores
-// without holding registers. Within each token row the 16-byte pieces are XOR-swizzled
-// by the token index (K by t & 7, V by 4 (t & 3), or 4 (t & 1) for 64-dim heads) to
-// spread LDS banks.
+// through a ring of three stages, so loads run two stages ahead of the matrix cores
+// without holding registers. Ring and registers (at most 168 VGPRs) are sized for three
+// workgroups per CU at 128-dim heads, whose interleaving hides the softmax behind the
+// other waves' products. Within each token row the 16-byte pieces are XOR-swizzled by
+// the token index so that the operand reads hit distinct LDS banks.
 //
 // Contractions, both on v_mfma_f32_32x32x16_f16 (fp16 in, fp32 accumulate):
 //   S^T[token][row] = K[token][:] . Q[row][:]   (A = K rows from LDS, B = Q rows in
@@ -40,7 +41,7 @@ namespace {
 constexpr int kBM = 128;     // query rows per workgroup
 constexpr int kWRows = 32;   // query rows per wave
 constexpr int kBN = 32;      // tokens per stage
-constexpr int kStages = 4;   // ring depth
+constexpr int kStages = 3;   // ring depth (48 KB of LDS at D = 128: three workgroups per CU)
 constexpr int kThreads = 256;
 constexpr int kXcds = 8;     // accelerator dies of an MI355X, each with its own L2
 constexpr int kMaxRanked = 256;  // requests ranked by length; larger batches keep their order
@@ -131,7 +132,7 @@ __device__ int request_of_rank(const PrefillArgs& a, int rank, int* slot) {
 }
 
 template <int D>
-__global__ __launch_bounds__(kThreads, 2) void prefill_kernel(const PrefillArgs a) {
+__global__ __launch_bounds__(kThreads, 3) void prefill_kernel(const PrefillArgs a) {
   constexpr int KS = D / 16;          // k-steps of S^T (16 dims each)
   constexpr int DT = D / 32;          // 32-dim tiles of O^T
   constexpr int PIECES = D / 8;       // 16-byte pieces per token row of one head
@@ -278,7 +279,8 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(const PrefillArgs 
     // this wave's loads of stage `it` have landed once at most the loads of the stages
     // issued after it are outstanding; the barrier makes every wave's loads visible and
     // frees ring slot (it - 1) % kStages for stage it + kStages - 1
-    if (it + 2 < nst) wait_vm<4 * INST>();
+    static_assert(kStages == 3 || kStages == 4, "waits below cover up to two stages ahead");
+    if (kStages == 4 && it + 2 < nst) wait_vm<4 * INST>();
     else if (it + 1 < nst) wait_vm<2 * INST>();
     else wait_vm<0>();
     lds_barrier();
