@@ -5,11 +5,15 @@ A step is the whole hot path over one batch: ``pa_kv_append`` of this step's new
 into their pool slots, ``pa_prefill_chunk`` for prefill chunks (mixed workload only) and
 ``pa_decode`` (split-context partitions and their log-sum-exp merge). Workloads:
 
+  c1            4 tiny decode sequences (1, 15, 16, 33 tokens), 4 heads x 64: launch-bound
   c2 (default)  256 decode sequences, context U{128..2048}, 32 heads x 128, + append
   c3            8 sequences x 32768 tokens, 32 x 128 (64 partitions of 512)
   c4            64 prompt groups x 4 samples sharing 64 blocks, 32q / 8kv heads x 128
   c5            8 prefill chunks of 512 over priors U{0..3584} + 248 decodes U{256..4096},
                 append of all 4344 new tokens
+
+The timed steps replay the step captured once into a HIP graph (``--launch graph``, the
+default, as a serving engine runs it) or launch it call by call (``--launch eager``).
 
 Printed: one JSON line. ``value`` is the KV-read rate of the step (algorithmic bytes:
 every decode context token's K and V row once) over the whole step time; ``roofline``
@@ -40,6 +44,8 @@ PROFILES = os.path.join(ROOT, "profiles")
 DECODE_SRC = os.path.join(ROOT, "paged_kv_cache_294_amd", "csrc", "pa_decode.hip")
 
 WORKLOADS = {
+    "c1": (1, "tiny decode: 4 sequences of 1, 15, 16, 33 tokens over a 16-block pool, "
+              "4 heads x 64, block 16, fp16 (launch-bound)"),
     "c2": (2, "decode step: kv_append of 256 tokens + paged decode of 256 sequences, "
               "context U{128..2048}, 32 heads x 128, block 16, fp16, shuffled blocks"),
     "c3": (3, "long-context decode: 8 sequences x 32768 tokens, 32 heads x 128, block 16, "
@@ -242,7 +248,7 @@ class Step:
             self.max_q = int(np.diff(qsl).max())
             self.max_s = int(lensp.max())
 
-    def run(self, ev=None):
+    def run(self, ev=None, stream=None):
         pkv = self.pkv
 
         def rec(i):
@@ -251,14 +257,14 @@ class Step:
 
         rec(0)
         if len(self.inp.slot_mapping):
-            pkv.pa_kv_append(self.pool, self.key, self.value, self.slots)
+            pkv.pa_kv_append(self.pool, self.key, self.value, self.slots, stream=stream)
         rec(1)
         if self.has_prefill:
             pkv.pa_prefill_chunk(self.pout, self.pq, self.pool, self.pbt, self.qsl, self.plens,
-                                 self.max_q, self.max_s, self.inp.scale)
+                                 self.max_q, self.max_s, self.inp.scale, stream=stream)
         rec(2)
         pkv.pa_decode(self.dout, self.dq, self.pool, self.dbt, self.dlens, self.mcl, self.inp.scale,
-                      self.ps, self.ws, self.flags)
+                      self.ps, self.ws, self.flags, stream=stream)
         rec(3)
 
 
@@ -341,6 +347,10 @@ def main():
     ap.add_argument("--partition-size", type=int, default=256)
     ap.add_argument("--kv-stream", choices=("auto", "on", "off"), default="auto",
                     help="non-temporal K/V loads in decode; auto: on unless blocks are shared")
+    ap.add_argument("--launch", choices=("graph", "eager"), default="graph",
+                    help="graph: time replays of the step captured once into a HIP graph "
+                         "(StepGraph), the serving path; eager: time the launches themselves. "
+                         "Per-kernel times always come from eager steps")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-stream-read", action="store_true")
     ap.add_argument("--cpu-cores", type=int, default=16)
@@ -423,6 +433,27 @@ def main():
     log(f"step {ms_step:.3f} ms (wall {wall / args.steps * 1e3:.3f} ms): append "
         f"{append_ms * 1e3:.1f} us, prefill {prefill_ms * 1e3:.1f} us, decode {decode_ms * 1e3:.1f} us")
 
+    eager_ms_step = ms_step
+    if args.launch == "graph":
+        side = torch.cuda.Stream()
+        graph = pkv.StepGraph(side)
+        torch.cuda.synchronize()
+        with torch.cuda.stream(side):
+            with graph:
+                step.run(stream=side)
+        for _ in range(args.warmup):
+            graph.launch()
+        torch.cuda.synchronize()
+        gs, ge = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        gs.record(side)
+        for _ in range(args.steps):
+            graph.launch()
+        ge.record(side)
+        torch.cuda.synchronize()
+        ms_step = gs.elapsed_time(ge) / args.steps
+        graph.close()
+        log(f"graph replay: step {ms_step:.3f} ms (eager {eager_ms_step:.3f} ms)")
+
     achieved = kv_bytes / (decode_ms * 1e-3) / 1e9
     nparts = pkv.pa_num_partitions(step.mcl, args.partition_size)
     traffic = read_traffic(f"pa_decode_{args.workload}_counters.txt", source_digest(DECODE_SRC))
@@ -461,7 +492,9 @@ def main():
             "num_kv_heads": inp.num_kv_heads, "head_size": inp.head_size,
             "block_size": inp.block_size, "partition_size": args.partition_size,
             "sum_context_tokens": int(inp.seq_lens.sum()), "seed": seed,
+            "launch": "hip graph replay" if args.launch == "graph" else "eager",
         },
+        "eager_ms_per_step": eager_ms_step,
         "pct_of_hbm_peak": 100.0 * kv_bytes / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBPS,
         "seq_steps_per_s": inp.num_seqs / (ms_step * 1e-3),
         "roofline": {

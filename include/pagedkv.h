@@ -201,6 +201,32 @@ pa_status pa_gather_kv(void* k_out, void* v_out, const void* kv_pool,
 pa_status pa_stream_read(const void* buf, int64_t bytes, float* sink, void* stream);
 int64_t pa_stream_read_sink_len(int64_t bytes);
 
+/* ---- captured steps (HIP graphs) ----------------------------------------------------
+ * A step (append, prefill, decode, reduce) is a few launches whose host-side cost rules
+ * small batches; serving engines replay such a step from a captured graph (page "vLLM
+ * 部署深度指南", GPTQ deployment listing and flag table: enforce_eager / --enforce-eager
+ * switch the CUDA-graph path off). These calls capture whatever this library (or
+ * anything else) enqueues on a stream between pa_graph_begin and pa_graph_end and
+ * replay it with one launch.
+ *
+ *   pa_graph_begin  starts capturing `stream` (must not be the null stream; relaxed
+ *                   mode). Every call enqueued on it until pa_graph_end is recorded, not
+ *                   run. The device buffers and host scalars of those calls are fixed in
+ *                   the graph: a replay reads the same buffers, so the caller updates
+ *                   inputs in place and keeps every buffer (workspaces included) alive
+ *                   until pa_graph_destroy.
+ *   pa_graph_end    ends the capture and instantiates it; *graph receives a host handle
+ *                   owned by the caller (NULL on error; the capture is ended either way).
+ *   pa_graph_launch replays the whole capture on `stream` (stream-ordered, asynchronous).
+ *   pa_graph_destroy releases the handle (NULL is ignored).
+ * Capturing records no memset nodes: the library's kernels clear nothing through
+ * hipMemset. */
+typedef struct pa_graph pa_graph;
+pa_status pa_graph_begin(void* stream);
+pa_status pa_graph_end(void* stream, pa_graph** graph);
+pa_status pa_graph_launch(const pa_graph* graph, void* stream);
+void pa_graph_destroy(pa_graph* graph);
+
 #ifdef __cplusplus
 }
 #endif

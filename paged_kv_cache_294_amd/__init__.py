@@ -3,7 +3,8 @@
 The library (``libpagedkv.so``, declared in ``include/pagedkv.h``) holds the kernels:
 ``pa_kv_append`` (scatter of new tokens into pool slots), ``pa_decode`` (split-context
 paged decode with a log-sum-exp merge), ``pa_prefill_chunk`` (causal chunked prefill on
-the matrix cores), ``pa_gather_kv`` and the pool-layout helpers. The functions below
+the matrix cores), ``pa_gather_kv``, the pool-layout helpers and step capture into HIP graphs
+(``StepGraph``). The functions below
 only marshal torch tensors into the C calls.
 """
 
@@ -11,6 +12,7 @@ from ._lib import (  # noqa: F401
     LIB_PATH,
     SIGNATURES,
     PagedKVError,
+    StepGraph,
     load,
     pa_abi_version,
     pa_block_bytes,

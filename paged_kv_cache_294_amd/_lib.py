@@ -44,6 +44,10 @@ SIGNATURES = {
     "pa_gather_kv": (ctypes.c_int, [_vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i64, _vp]),
     "pa_stream_read": (ctypes.c_int, [_vp, _i64, _vp, _vp]),
     "pa_stream_read_sink_len": (_i64, [_i64]),
+    "pa_graph_begin": (ctypes.c_int, [_vp]),
+    "pa_graph_end": (ctypes.c_int, [_vp, ctypes.POINTER(_vp)]),
+    "pa_graph_launch": (ctypes.c_int, [_vp, _vp]),
+    "pa_graph_destroy": (None, [_vp]),
 }
 
 
@@ -57,6 +61,7 @@ class PagedKVError(RuntimeError):
 
 
 _LIB = None
+_CAPTURING = 0  # graph captures in progress in this process (see StepGraph)
 
 
 def load() -> ctypes.CDLL:
@@ -196,6 +201,10 @@ def pa_decode(out, q, kv_pool, block_tables, context_lens, max_context_len, scal
     if need < 0:
         raise PagedKVError("pa_decode_workspace_bytes", PA_ERR_INVALID)
     if workspace is None and need > 0:
+        if _CAPTURING:
+            # a buffer allocated here would be freed after the call while the graph
+            # keeps writing it on every replay
+            raise ValueError("pa_decode under capture needs a caller-owned workspace")
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
     ws_p, ws_n = (0, 0) if workspace is None else (_dense(workspace, "workspace", torch.uint8),
                                                     workspace.numel())
@@ -257,3 +266,56 @@ def pa_stream_read(buf, sink, stream=None):
     st = load().pa_stream_read(buf.data_ptr(), nbytes, _dense(sink, "sink", torch.float32),
                                _stream(stream))
     _check("pa_stream_read", st)
+
+
+# ---------------------------------------------------------------------------------------
+# captured steps
+# ---------------------------------------------------------------------------------------
+
+class StepGraph:
+    """A step captured once with ``pa_graph_begin``/``pa_graph_end`` and replayed by
+    :meth:`launch`. Use as ``with StepGraph(stream) as g: <calls on stream>``; the calls
+    inside are recorded, not run. Buffers and host scalars of the recorded calls are fixed:
+    replays read and write the same tensors, which the caller keeps alive and updates in
+    place. ``stream`` must be a side stream (not the null stream)."""
+
+    def __init__(self, stream):
+        if stream is None:
+            raise ValueError("capture needs an explicit side stream")
+        self._stream = stream
+        self._handle = None
+
+    def __enter__(self):
+        global _CAPTURING
+        _check("pa_graph_begin", load().pa_graph_begin(_stream(self._stream)))
+        _CAPTURING += 1
+        return self
+
+    def __exit__(self, exc_type, exc, tb):
+        global _CAPTURING
+        _CAPTURING -= 1
+        h = _vp()
+        st = load().pa_graph_end(_stream(self._stream), ctypes.byref(h))
+        if exc_type is None:
+            _check("pa_graph_end", st)
+            self._handle = h
+        elif h.value:
+            load().pa_graph_destroy(h)
+        return False
+
+    def launch(self, stream=None):
+        if self._handle is None:
+            raise RuntimeError("nothing captured")
+        _check("pa_graph_launch",
+               load().pa_graph_launch(self._handle, _stream(self._stream if stream is None else stream)))
+
+    def close(self):
+        if self._handle is not None:
+            load().pa_graph_destroy(self._handle)
+            self._handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass

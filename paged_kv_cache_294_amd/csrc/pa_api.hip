@@ -6,6 +6,7 @@
 #include <cstdint>
 #include <cstdio>
 #include <cstring>
+#include <new>
 
 #include "../../include/pagedkv.h"
 #include "pa_launch.h"
@@ -271,4 +272,58 @@ PA_EXPORT pa_status pa_stream_read(const void* buf, int64_t bytes, float* sink, 
   if (!buf || !sink || bytes <= 0 || bytes % 16 || !aligned16(buf)) return PA_ERR_INVALID;
   if (pkv::stream_read_groups(bytes) > INT32_MAX) return PA_ERR_UNSUPPORTED;
   return hip_status(pkv::launch_stream_read(buf, bytes, sink, (hipStream_t)stream));
+}
+
+// ---------------------------------------------------------------------------------------
+// captured steps
+// ---------------------------------------------------------------------------------------
+
+struct pa_graph {
+  hipGraph_t graph;
+  hipGraphExec_t exec;
+};
+
+PA_EXPORT pa_status pa_graph_begin(void* stream) {
+  if (stream == nullptr) return PA_ERR_INVALID;  // the null stream cannot be captured
+  return hip_status(hipStreamBeginCapture(static_cast<hipStream_t>(stream),
+                                          hipStreamCaptureModeRelaxed));
+}
+
+PA_EXPORT pa_status pa_graph_end(void* stream, pa_graph** out) {
+  if (out != nullptr) *out = nullptr;
+  if (stream == nullptr) return PA_ERR_INVALID;
+  hipGraph_t graph = nullptr;
+  hipError_t e = hipStreamEndCapture(static_cast<hipStream_t>(stream), &graph);
+  if (e != hipSuccess) return hip_status(e);
+  if (out == nullptr) {
+    hipGraphDestroy(graph);
+    return PA_ERR_INVALID;
+  }
+  hipGraphExec_t exec = nullptr;
+  e = hipGraphInstantiate(&exec, graph, nullptr, nullptr, 0);
+  if (e != hipSuccess) {
+    hipGraphDestroy(graph);
+    return hip_status(e);
+  }
+  pa_graph* g = new (std::nothrow) pa_graph{graph, exec};
+  if (g == nullptr) {
+    hipGraphExecDestroy(exec);
+    hipGraphDestroy(graph);
+    std::snprintf(g_last_error, sizeof(g_last_error), "out of host memory");
+    return PA_ERR_INVALID;
+  }
+  *out = g;
+  return PA_OK;
+}
+
+PA_EXPORT pa_status pa_graph_launch(const pa_graph* g, void* stream) {
+  if (g == nullptr) return PA_ERR_INVALID;
+  return hip_status(hipGraphLaunch(g->exec, static_cast<hipStream_t>(stream)));
+}
+
+PA_EXPORT void pa_graph_destroy(pa_graph* g) {
+  if (g == nullptr) return;
+  hipGraphExecDestroy(g->exec);
+  hipGraphDestroy(g->graph);
+  delete g;
 }

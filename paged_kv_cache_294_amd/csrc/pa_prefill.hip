@@ -15,7 +15,7 @@
 // without holding registers. Ring and registers (at most 168 VGPRs) are sized for three
 // workgroups per CU at 128-dim heads, whose interleaving hides the softmax behind the
 // other waves' products. Within each token row the 16-byte pieces are XOR-swizzled by
-// the token index so that the operand reads hit distinct LDS banks.
+// the token index to spread the operand reads over the LDS banks.
 //
 // Contractions, both on v_mfma_f32_32x32x16_f16 (fp16 in, fp32 accumulate):
 //   S^T[token][row] = K[token][:] . Q[row][:]   (A = K rows from LDS, B = Q rows in

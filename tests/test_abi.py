@@ -172,3 +172,14 @@ def test_gather_and_stream_read_reject(lib):
     assert lib.pa_gather_kv(FAKE, FAKE, FAKE, FAKE, 0, 4, 64, 16, 16, None) == pkv.PA_OK
     assert lib.pa_stream_read(FAKE, 100, FAKE, None) == pkv.PA_ERR_INVALID
     assert lib.pa_stream_read_sink_len(1 << 30) > 0
+
+
+def test_graph_calls_reject_without_touching_the_gpu(lib):
+    assert lib.pa_graph_begin(None) == pkv.PA_ERR_INVALID  # the null stream cannot be captured
+    h = ctypes.c_void_p()
+    assert lib.pa_graph_end(None, ctypes.byref(h)) == pkv.PA_ERR_INVALID
+    assert h.value is None
+    assert lib.pa_graph_launch(None, None) == pkv.PA_ERR_INVALID
+    lib.pa_graph_destroy(None)  # ignored
+    with pytest.raises(ValueError):
+        pkv.StepGraph(None)

@@ -1,0 +1,112 @@
+"""A step captured into a HIP graph (StepGraph) replays to exactly the eager step's bits.
+
+The step is kv_append -> chunked prefill -> decode (grouped-query tile, several
+partitions, so the log-sum-exp reduce runs too). Replays are separated by eager work
+and host synchronisations, and the queries are changed in place between them."""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import paged_kv_cache_294_amd as pkv
+import workloads
+from gpu_util import check_attention, dev, host, note
+
+pytestmark = pytest.mark.gpu
+
+
+class Batch:
+    def __init__(self, inp, partition_size=512):
+        self.inp = inp
+        self.pool = dev(inp.pool)
+        self.key, self.value, self.slots = dev(inp.key_new), dev(inp.value_new), dev(inp.slot_mapping)
+        qd, btd, lensd = inp.decode_part()
+        self.dq, self.dbt, self.dlens = dev(qd), dev(btd), dev(lensd)
+        self.mcl = int(lensd.max())
+        self.ps = partition_size
+        ws = pkv.pa_decode_workspace_bytes(len(lensd), inp.num_q_heads, self.mcl, partition_size,
+                                           inp.head_size)
+        assert ws > 0  # several partitions: the reduce kernel is part of the step
+        self.ws = torch.empty(ws, dtype=torch.uint8, device="cuda")
+        qp, btp, qsl, lensp = inp.prefill_part()
+        self.pq, self.pbt, self.qsl, self.plens = dev(qp), dev(btp), dev(qsl), dev(lensp)
+        self.max_q, self.max_s = int(np.diff(qsl).max()), int(lensp.max())
+        self.dout = torch.full_like(self.dq, float("nan"))
+        self.pout = torch.full_like(self.pq, float("nan"))
+
+    def step(self, stream):
+        pkv.pa_kv_append(self.pool, self.key, self.value, self.slots, stream=stream)
+        pkv.pa_prefill_chunk(self.pout, self.pq, self.pool, self.pbt, self.qsl, self.plens,
+                             self.max_q, self.max_s, self.inp.scale, stream=stream)
+        pkv.pa_decode(self.dout, self.dq, self.pool, self.dbt, self.dlens, self.mcl,
+                      self.inp.scale, self.ps, self.ws, stream=stream)
+
+
+def test_captured_step_replays_bit_exact():
+    inp = workloads.mixed_case(71, [0, 300, 40], [64, 100, 33], [1, 50, 700, 2000, 1100], 8, 4, 128)
+    side = torch.cuda.Stream()
+    b = Batch(inp)
+    note("graph: eager reference step")
+    with torch.cuda.stream(side):
+        b.step(side)
+    side.synchronize()
+    ref_d, ref_p = b.dout.clone(), b.pout.clone()
+    # the eager step itself against the oracle
+    pool = oracle.kv_append(inp.pool, inp.key_new, inp.value_new, inp.slot_mapping)
+    qd, btd, lensd = inp.decode_part()
+    check_attention(host(ref_d), oracle.decode(qd, pool, btd, lensd, inp.scale), "graph eager decode")
+
+    q2_d = torch.randn(b.dq.shape, generator=torch.Generator().manual_seed(5)).half().cuda()
+    q2_p = torch.randn(b.pq.shape, generator=torch.Generator().manual_seed(6)).half().cuda()
+    b2 = Batch(inp)
+    b2.dq.copy_(q2_d)
+    b2.pq.copy_(q2_p)
+    with torch.cuda.stream(side):
+        b2.step(side)
+    side.synchronize()
+    ref2_d, ref2_p = b2.dout.clone(), b2.pout.clone()
+
+    note("graph: capture")
+    g = pkv.StepGraph(side)
+    b.dout.fill_(float("nan"))
+    b.pout.fill_(float("nan"))
+    torch.cuda.synchronize()
+    with torch.cuda.stream(side):
+        with g:
+            b.step(side)
+    torch.cuda.synchronize()
+    # captured, not run
+    assert torch.isnan(b.dout.float()).all() and torch.isnan(b.pout.float()).all()
+    try:
+        for rep, (q_d, q_p, want_d, want_p) in enumerate([
+                (None, None, ref_d, ref_p), (q2_d, q2_p, ref2_d, ref2_p), (None, None, ref2_d, ref2_p)]):
+            note(f"graph: replay {rep}")
+            b.dout.fill_(float("nan"))
+            b.pout.fill_(float("nan"))
+            if q_d is not None:
+                b.dq.copy_(q_d)
+                b.pq.copy_(q_p)
+            torch.cuda.synchronize()
+            g.launch()
+            side.synchronize()
+            assert torch.equal(b.dout.view(torch.int16), want_d.view(torch.int16)), f"decode replay {rep}"
+            assert torch.equal(b.pout.view(torch.int16), want_p.view(torch.int16)), f"prefill replay {rep}"
+            _ = (b.dout.float().sum() + 1).item()  # eager work between replays
+    finally:
+        g.close()
+
+
+def test_capture_needs_caller_workspace():
+    inp = workloads.decode_case(72, [600, 1500], 4, 4, 64)
+    side = torch.cuda.Stream()
+    q, bt, lens = (dev(a) for a in inp.decode_part())
+    pool = dev(inp.pool)
+    out = torch.empty_like(q)
+    g = pkv.StepGraph(side)
+    with pytest.raises(ValueError):
+        with torch.cuda.stream(side):
+            with g:
+                pkv.pa_decode(out, q, pool, bt, lens, 1500, inp.scale, 512, None, stream=side)
+    side.synchronize()
+    g.close()
