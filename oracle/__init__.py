@@ -5,6 +5,7 @@ this package. It is plain fp64 NumPy, shares no code with the HIP library and
 never imports it.
 """
 
+from .block_manager import BlockManager, copy_blocks, move_blocks  # noqa: F401
 from .paged_attention import (  # noqa: F401
     BlockAllocator,
     KVCacheExhausted,

@@ -328,3 +328,231 @@ def check_kv_append(inp):
         assert np.array_equal(out[blk, off, 0].view(np.uint16), inp.key_new[t].view(np.uint16))
         assert np.array_equal(out[blk, off, 1].view(np.uint16), inp.value_new[t].view(np.uint16))
     assert np.array_equal(out[~touched].view(np.uint16), inp.pool[~touched].view(np.uint16))
+
+
+# ---------------------------------------------------------------------------------------
+# block manager and block copies
+# ---------------------------------------------------------------------------------------
+
+BLOCK_TRACE = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden",
+                           "block_manager_trace.txt")
+
+
+def read_block_trace():
+    """(num_blocks, block_size, [(op, args, result_tokens, checks)]) of the golden trace."""
+    nb = bs = None
+    steps = []
+    for raw in open(BLOCK_TRACE, encoding="utf-8"):
+        line = raw.split("#", 1)[0].strip()
+        if not line:
+            continue
+        if line.startswith("num_blocks"):
+            nb = int(line.split()[1])
+            continue
+        if line.startswith("block_size"):
+            bs = int(line.split()[1])
+            continue
+        lhs, rhs = line.split("->")
+        parts = [p.strip() for p in rhs.split(";")]
+        op, *args = lhs.split()
+        steps.append((op, args, parts[0].split(), [p.split() for p in parts[1:]]))
+    return nb, bs, steps
+
+
+def run_block_trace(mgr, steps, exhausted=(opa.KVCacheExhausted,)):
+    """Replay the golden trace on ``mgr`` (oracle.BlockManager or an object with the same
+    methods and attributes ``free_list()``, ``refs_of(b)``, ``table_of(s)``, ``len_of(s)``)
+    and assert every result and check."""
+    for n, (op, args, res, checks) in enumerate(steps):
+        where = f"trace step {n}: {op} {' '.join(args)}"
+        try:
+            if op == "allocate":
+                got = ["table", *map(str, mgr.allocate(args[0], int(args[1])))]
+            elif op == "fork":
+                got = ["table", *map(str, mgr.fork(args[0], args[1]))]
+            elif op == "append":
+                slot, copy = mgr.append_token(args[0])
+                got = ["slot", str(slot)] + ([] if copy is None else ["copy", str(copy[0]), str(copy[1])])
+            elif op == "free":
+                mgr.free(args[0])
+                got = []
+            else:
+                raise AssertionError(f"unknown op {op}")
+        except exhausted:
+            got = ["OOM"]
+        assert got == res, f"{where}: got {got}, want {res}"
+        for c in checks:
+            kind, vals = c[0], c[1:]
+            if kind == "free":
+                assert list(map(int, vals)) == list(mgr.free_list()), where
+            elif kind == "table":
+                assert list(map(int, vals[1:])) == list(mgr.table_of(vals[0])), where
+            elif kind == "len":
+                assert int(vals[1]) == mgr.len_of(vals[0]), where
+            elif kind == "refs":
+                for kv in vals:
+                    b, cnt = map(int, kv.split(":"))
+                    assert mgr.refs_of(b) == cnt, f"{where}: refs of {b}"
+            elif kind == "usage":
+                assert math.isclose(mgr.usage(), float(vals[0])), where
+            elif kind == "utilisation":
+                assert math.isclose(mgr.slot_utilisation(), float(vals[0])), where
+            else:
+                raise AssertionError(f"unknown check {kind}")
+
+
+def oracle_manager(nb, bs):
+    """oracle.BlockManager with the accessors the trace replay uses."""
+    from oracle.block_manager import BlockManager
+
+    m = BlockManager(nb, bs)
+    m.free_list = lambda: list(m.free_blocks)
+    m.refs_of = lambda b: m.refs[b]
+    m.table_of = lambda s: list(m.tables[s])
+    m.len_of = lambda s: m.lengths[s]
+    return m
+
+
+def check_block_manager_golden():
+    nb, bs, steps = read_block_trace()
+    run_block_trace(oracle_manager(nb, bs), steps)
+
+
+def random_block_ops(seed, num_blocks, steps, block_size=16, forks=True):
+    """A seeded op sequence over a small pool: allocate / append / fork / free."""
+    rng = np.random.default_rng(seed)
+    live, next_id, ops = [], 0, []
+    for _ in range(steps):
+        r = rng.random()
+        if not live or r < 0.15:
+            ops.append(("allocate", next_id, int(rng.integers(0, 3 * block_size))))
+            live.append(next_id)
+            next_id += 1
+        elif forks and r < 0.25:
+            ops.append(("fork", int(rng.choice(live)), next_id))
+            live.append(next_id)
+            next_id += 1
+        elif r < 0.33:
+            s = int(rng.choice(live))
+            ops.append(("free", s))
+            live.remove(s)
+        else:
+            ops.append(("append", int(rng.choice(live))))
+    return ops
+
+
+def apply_block_op(mgr, op, exhausted=(opa.KVCacheExhausted,)):
+    """Run one op; returns its outcome (comparable across implementations). An op on a
+    sequence that does not exist (its allocation ran out of blocks) is "invalid"."""
+    try:
+        if op[0] == "allocate":
+            return ("table", tuple(mgr.allocate(op[1], op[2])))
+        if op[0] == "fork":
+            return ("table", tuple(mgr.fork(op[1], op[2])))
+        if op[0] == "free":
+            mgr.free(op[1])
+            return ("freed",)
+        slot, copy = mgr.append_token(op[1])
+        return ("slot", slot, copy)
+    except exhausted:
+        return ("OOM",)
+    except (KeyError, ValueError):
+        return ("invalid",)
+
+
+def check_block_manager_semantics(seed, num_blocks=24, steps=400, block_size=4):
+    """Token-level meaning of tables, copies and slots: every sequence must read back
+    exactly the tokens it was given (its parent's up to the fork, then its own), through
+    its table, in a pool that applies each reported copy before the token is written.
+    Also: reference counts equal the table references, free + referenced = all blocks,
+    the slot written is never shared, table lengths are ceil(len / block_size)."""
+    from oracle.block_manager import BlockManager, copy_blocks
+
+    m = BlockManager(num_blocks, block_size)
+    pool = np.full((num_blocks, block_size), -1, dtype=np.int64)  # token ids
+    history = {}
+    token = 0
+    for op in random_block_ops(seed, num_blocks, steps, block_size):
+        if op[0] != "allocate" and op[1] not in m.tables:
+            continue  # its allocation ran out of blocks
+        if op[0] == "allocate":
+            try:
+                table = m.allocate(op[1], op[2])
+            except opa.KVCacheExhausted:
+                continue
+            history[op[1]] = list(range(token, token + op[2]))
+            for pos, t in enumerate(history[op[1]]):
+                pool[table[pos // block_size], pos % block_size] = t
+            token += op[2]
+        elif op[0] == "fork":
+            m.fork(op[1], op[2])
+            history[op[2]] = list(history[op[1]])
+        elif op[0] == "free":
+            m.free(op[1])
+            del history[op[1]]
+        else:
+            try:
+                slot, copy = m.append_token(op[1])
+            except opa.KVCacheExhausted:
+                continue
+            if copy is not None:
+                pool = copy_blocks(pool, [copy])
+            blk = slot // block_size
+            assert m.refs[blk] == 1, "appended into a shared block"
+            pool[blk, slot % block_size] = token
+            history[op[1]].append(token)
+            token += 1
+        counts = np.zeros(num_blocks, dtype=np.int64)
+        for s, table in m.tables.items():
+            assert len(table) == opa.blocks_needed(m.lengths[s], block_size)
+            for b in table:
+                counts[b] += 1
+            got = [pool[table[p // block_size], p % block_size] for p in range(m.lengths[s])]
+            assert got == history[s], f"sequence {s} reads wrong tokens"
+        assert list(counts) == m.refs
+        assert len(m.free_blocks) + int((counts > 0).sum()) == num_blocks
+        assert all(counts[b] == 0 for b in m.free_blocks)
+
+
+def check_block_manager_without_forks_is_the_listing(seed, num_blocks=64, steps=300):
+    """With no forks, no frees and no exhaustion the manager hands out exactly the tables
+    and slots of the listing's allocator (oracle.BlockAllocator)."""
+    from oracle.block_manager import BlockManager
+
+    m = BlockManager(num_blocks)
+    a = opa.BlockAllocator(num_blocks)
+    for op in random_block_ops(seed, num_blocks, steps, forks=False):
+        if op[0] == "free":
+            continue
+        if op[0] == "allocate":
+            need = opa.blocks_needed(op[2])
+            if need > len(a.free_blocks):
+                break
+            assert m.allocate(op[1], op[2]) == a.allocate(op[1], op[2])
+        else:
+            t = a.block_tables[op[1]]
+            if a.lengths[op[1]] == len(t) * 16 and not a.free_blocks:
+                break
+            slot, copy = m.append_token(op[1])
+            assert copy is None and slot == a.append_token(op[1])
+
+
+def check_block_copies():
+    """copy_blocks / move_blocks against NumPy fancy indexing (disjoint pairs)."""
+    from oracle.block_manager import copy_blocks, move_blocks
+
+    rng = np.random.default_rng(3)
+    pool = rng.standard_normal((12, 16, 2, 2, 8)).astype(np.float16)
+    src = np.array([0, 5, 7]); dst = np.array([3, 9, 11])
+    want = pool.copy()
+    want[dst] = pool[src]
+    got = copy_blocks(pool, np.stack([src, dst], 1))
+    assert np.array_equal(got.view(np.uint16), want.view(np.uint16))
+    host = np.zeros((6, 16, 2, 2, 8), np.float16)
+    want_h = host.copy()
+    want_h[[4, 0, 2]] = pool[[1, 6, 8]]
+    got_h = move_blocks(host, pool, [[1, 4], [6, 0], [8, 2]])
+    assert np.array_equal(got_h.view(np.uint16), want_h.view(np.uint16))
+    # chained pairs apply in order: 0 -> 1, then 1 -> 2 carries block 0's contents
+    chain = copy_blocks(pool, [[0, 1], [1, 2]])
+    assert np.array_equal(chain[2].view(np.uint16), pool[0].view(np.uint16))

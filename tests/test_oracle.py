@@ -291,3 +291,99 @@ def test_pins_catch_append_to_wrong_half(monkeypatch):
         return out
     monkeypatch.setattr(opa, "kv_append", bad_append)
     _expect_failure(pins.check_kv_append, mha_case())
+
+
+# ---------------------------------------------------------------------------------------
+# block manager (refcounts, fork, copy-on-write, free) and block copies
+# ---------------------------------------------------------------------------------------
+
+def test_golden_block_manager_trace():
+    pins.check_block_manager_golden()
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_block_manager_semantics(seed):
+    pins.check_block_manager_semantics(seed)
+
+
+@pytest.mark.parametrize("seed", range(4))
+def test_block_manager_without_forks_is_the_listing(seed):
+    pins.check_block_manager_without_forks_is_the_listing(seed)
+
+
+def test_block_copies():
+    pins.check_block_copies()
+
+
+def test_block_manager_fresh_and_full():
+    m = oracle.BlockManager(10)
+    assert m.usage() == 0.0 and m.slot_utilisation() == 0.0
+    m.allocate("x", 48)
+    assert m.usage() == pytest.approx(0.3) and m.slot_utilisation() == 1.0
+    with pytest.raises(oracle.KVCacheExhausted):
+        m.allocate("y", 16 * 8)  # 8 blocks > 7 free: nothing taken
+    assert len(m.free_blocks) == 7
+
+
+def _bm_planted(monkeypatch, name, fn, checks):
+    from oracle import block_manager as obm
+    monkeypatch.setattr(obm.BlockManager, name, fn)
+    for check in checks:
+        with pytest.raises(AssertionError):
+            check()
+
+
+def test_pins_catch_lifo_free_list(monkeypatch):
+    def _take(self):
+        b = self.free_blocks.pop()
+        self.refs[b] = 1
+        return b
+    _bm_planted(monkeypatch, "_take", _take, [pins.check_block_manager_golden])
+
+
+def test_pins_catch_missing_copy_on_write(monkeypatch):
+    from oracle import block_manager as obm
+    orig = obm.BlockManager.append_token
+
+    def append_token(self, seq_id):
+        table, pos = self.tables[seq_id], self.lengths[seq_id]
+        if pos < len(table) * self.block_size:  # write into the last block even if shared
+            self.lengths[seq_id] = pos + 1
+            return table[pos // self.block_size] * self.block_size + pos % self.block_size, None
+        return orig(self, seq_id)
+    _bm_planted(monkeypatch, "append_token", append_token,
+                [pins.check_block_manager_golden, lambda: pins.check_block_manager_semantics(0)])
+
+
+def test_pins_catch_reversed_copy(monkeypatch):
+    from oracle import block_manager as obm
+    orig = obm.BlockManager.append_token
+
+    def append_token(self, seq_id):
+        slot, copy = orig(self, seq_id)
+        return slot, None if copy is None else (copy[1], copy[0])
+    _bm_planted(monkeypatch, "append_token", append_token,
+                [lambda: pins.check_block_manager_semantics(0)])
+
+
+def test_pins_catch_free_to_front(monkeypatch):
+    def free(self, seq_id):
+        for b in self.tables.pop(seq_id):
+            self.refs[b] -= 1
+            if self.refs[b] == 0:
+                self.free_blocks.insert(0, b)
+        del self.lengths[seq_id]
+    _bm_planted(monkeypatch, "free", free, [pins.check_block_manager_golden])
+
+
+def test_pins_catch_refcount_kept_on_copy(monkeypatch):
+    from oracle import block_manager as obm
+    orig = obm.BlockManager.append_token
+
+    def append_token(self, seq_id):
+        slot, copy = orig(self, seq_id)
+        if copy is not None:
+            self.refs[copy[0]] += 1  # forget to drop the shared block's reference
+        return slot, copy
+    _bm_planted(monkeypatch, "append_token", append_token,
+                [lambda: pins.check_block_manager_semantics(1)])
