@@ -220,6 +220,28 @@ def stream_read_gbps(torch, pkv, nbytes=4 << 30, reps=10):
     return nbytes / (ms * 1e-3) / 1e9
 
 
+def block_manager_leg(pkv, inp):
+    """The host block manager (C++, pa_bm_*) doing the bookkeeping of this batch: admit
+    every sequence with its cached tokens, then one step: reserve the slots of the step's
+    new tokens and write the padded block tables the kernels read."""
+    m = pkv.BlockManager(inp.num_blocks, inp.block_size)
+    B = inp.num_seqs
+    t0 = time.perf_counter()
+    for b in range(B):
+        m.allocate(b, int(inp.cached_lens[b]))
+    t1 = time.perf_counter()
+    ids = np.repeat(np.arange(B, dtype=np.int64), (inp.seq_lens - inp.cached_lens).astype(np.int64))
+    slots, copies = m.append_slots(ids)
+    tables, lens = m.block_tables(np.arange(B, dtype=np.int64), inp.block_tables.shape[1], pad=0)
+    t2 = time.perf_counter()
+    assert np.array_equal(lens, inp.seq_lens.astype(np.int32)) and len(copies) == 0
+    out = {"sequences": B, "new_tokens": int(len(ids)), "admit_us": (t1 - t0) * 1e6,
+           "step_us": (t2 - t1) * 1e6, "gpu_cache_usage": m.usage(),
+           "slot_utilisation": m.slot_utilisation()}
+    m.close()
+    return out
+
+
 class Step:
     """Device copies of a batch and one step of the hot path over them."""
 
@@ -409,6 +431,11 @@ def main():
         stream_gbps = stream_read_gbps(torch, pkv)
         log(f"stream_read: {stream_gbps:.0f} GB/s")
 
+    bm = None
+    if not inp.prefix_blocks:  # prefix sharing comes from the generator's own tables
+        bm = block_manager_leg(pkv, inp)
+        log(f"host block manager: admit {bm['admit_us']:.0f} us, step {bm['step_us']:.0f} us "
+            f"({bm['new_tokens']} slots + tables)")
     log("copying the batch to the GPU")
     step = Step(torch, pkv, inp, args.partition_size, kv_stream)
     for _ in range(args.warmup):
@@ -511,6 +538,7 @@ def main():
         "kernels": kernels,
         "cpu_baseline": None if cpu is None else {k: cpu[k] for k in
                                                   ("value", "unit", "cores", "kind", "sample")},
+        "block_manager": bm,
         "stream_read_gbps": stream_gbps,
         "frac_of_stream_read": None if not stream_gbps else achieved / stream_gbps,
         "context": {

@@ -50,7 +50,8 @@ typedef enum {
   PA_ERR_UNSUPPORTED = 2, /* valid request with no kernel here: block_size != 16,
                              head_size not in {64, 128}, group size not in {1,2,4,8}  */
   PA_ERR_WORKSPACE = 3,   /* workspace smaller than pa_decode_workspace_bytes         */
-  PA_ERR_HIP = 4          /* the HIP runtime refused a launch; see pa_last_error       */
+  PA_ERR_HIP = 4,         /* the HIP runtime refused a launch; see pa_last_error       */
+  PA_ERR_EXHAUSTED = 5    /* the block manager's free list cannot cover the request     */
 } pa_status;
 
 /* Static text for a status code. Never NULL. */
@@ -226,6 +227,66 @@ pa_status pa_graph_begin(void* stream);
 pa_status pa_graph_end(void* stream, pa_graph** graph);
 pa_status pa_graph_launch(const pa_graph* graph, void* stream);
 void pa_graph_destroy(pa_graph* graph);
+
+/* ---- host block manager --------------------------------------------------------------
+ * Which pool blocks each sequence holds (page "vLLM 部署深度指南", section
+ * "PagedAttention 原理", KV-cache listing: a free list that starts as 0 .. num_blocks-1
+ * and is taken from the front, ceil(n / block_size) blocks per sequence, an error when it
+ * runs dry; page "vLLM GitHub 项目 …", section 二: item 1, a new block only when the last
+ * one is full; item 4, sequences that share a prefix point at the same blocks). Host
+ * code only: no device memory, no stream. The manager owns its bookkeeping; every output
+ * array belongs to the caller. Sequence ids are any int64 values; block ids are int32.
+ *
+ *   pa_bm_create       manager of num_blocks blocks of block_size tokens
+ *   pa_bm_allocate     new sequence holding num_tokens tokens: ceil(num_tokens /
+ *                      block_size) blocks from the front of the free list, all or none
+ *                      (PA_ERR_EXHAUSTED, nothing taken); PA_ERR_INVALID if seq_id exists
+ *   pa_bm_append_slot  reserve the slot (block * block_size + offset) of the sequence's
+ *                      next token. A full last block gets a new block; a last block that
+ *                      another sequence also references and that is partly filled is
+ *                      replaced by a new block, and (*copy_src, *copy_dst) name the block
+ *                      copy that must run on the device before the token is written
+ *                      (copy-on-write; both -1 when no copy). PA_ERR_EXHAUSTED with no
+ *                      change when a block is needed and none is free
+ *   pa_bm_append_slots one token for each of seq_ids[0..n) in order, as above:
+ *                      slot_mapping[n] receives the slots, copies[2 * k], copies[2 * k + 1]
+ *                      the k-th copy pair (room for n pairs), *num_copies their count,
+ *                      *num_done the tokens appended; it stops at the first failure, whose
+ *                      slot and the following ones are -1
+ *   pa_bm_fork         child shares every block of parent (same length)
+ *   pa_bm_free         drop the sequence; each of its blocks loses a reference, in table
+ *                      order, and goes to the back of the free list when none is left
+ *   pa_bm_block_tables padded rows tables[n][max_blocks] (pad after the sequence's
+ *                      blocks) and lengths lens[n] of the listed sequences, ready for
+ *                      pa_decode / pa_prefill_chunk
+ *   queries            pa_bm_seq_len (-1: unknown), pa_bm_seq_table (writes up to cap
+ *                      entries, returns the count or -1), pa_bm_num_free, pa_bm_free_list
+ *                      (free list in order; returns its length), pa_bm_refcount,
+ *                      pa_bm_usage (fraction of blocks in use: the gpu_cache_usage_perc
+ *                      gauge of the monitoring table on the deployment page),
+ *                      pa_bm_slot_utilisation (fraction of slots in used blocks holding a
+ *                      token)
+ * Not thread-safe: one manager per thread, or the caller serialises. */
+typedef struct pa_block_manager pa_block_manager;
+pa_status pa_bm_create(int64_t num_blocks, int32_t block_size, pa_block_manager** out);
+void pa_bm_destroy(pa_block_manager* bm);
+pa_status pa_bm_allocate(pa_block_manager* bm, int64_t seq_id, int64_t num_tokens);
+pa_status pa_bm_append_slot(pa_block_manager* bm, int64_t seq_id, int64_t* slot,
+                            int64_t* copy_src, int64_t* copy_dst);
+pa_status pa_bm_append_slots(pa_block_manager* bm, const int64_t* seq_ids, int32_t n,
+                             int64_t* slot_mapping, int64_t* copies, int32_t* num_copies,
+                             int32_t* num_done);
+pa_status pa_bm_fork(pa_block_manager* bm, int64_t parent, int64_t child);
+pa_status pa_bm_free(pa_block_manager* bm, int64_t seq_id);
+pa_status pa_bm_block_tables(const pa_block_manager* bm, const int64_t* seq_ids, int32_t n,
+                             int32_t max_blocks, int32_t pad, int32_t* tables, int32_t* lens);
+int64_t pa_bm_seq_len(const pa_block_manager* bm, int64_t seq_id);
+int64_t pa_bm_seq_table(const pa_block_manager* bm, int64_t seq_id, int32_t* out, int64_t cap);
+int64_t pa_bm_num_free(const pa_block_manager* bm);
+int64_t pa_bm_free_list(const pa_block_manager* bm, int32_t* out, int64_t cap);
+int32_t pa_bm_refcount(const pa_block_manager* bm, int64_t block);
+double pa_bm_usage(const pa_block_manager* bm);
+double pa_bm_slot_utilisation(const pa_block_manager* bm);
 
 #ifdef __cplusplus
 }

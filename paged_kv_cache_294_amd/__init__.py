@@ -3,14 +3,16 @@
 The library (``libpagedkv.so``, declared in ``include/pagedkv.h``) holds the kernels:
 ``pa_kv_append`` (scatter of new tokens into pool slots), ``pa_decode`` (split-context
 paged decode with a log-sum-exp merge), ``pa_prefill_chunk`` (causal chunked prefill on
-the matrix cores), ``pa_gather_kv``, the pool-layout helpers and step capture into HIP graphs
-(``StepGraph``). The functions below
+the matrix cores), ``pa_gather_kv``, the pool-layout helpers, step capture into HIP graphs
+(``StepGraph``) and the host block manager (``BlockManager``). The functions below
 only marshal torch tensors into the C calls.
 """
 
 from ._lib import (  # noqa: F401
     LIB_PATH,
     SIGNATURES,
+    BlockManager,
+    KVCacheExhausted,
     PagedKVError,
     StepGraph,
     load,
@@ -35,4 +37,5 @@ from ._lib import (  # noqa: F401
     PA_ERR_UNSUPPORTED,
     PA_ERR_WORKSPACE,
     PA_ERR_HIP,
+    PA_ERR_EXHAUSTED,
 )

@@ -13,12 +13,13 @@ import ctypes
 import math
 import os
 
+import numpy as np
 import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libpagedkv.so")
 
-PA_OK, PA_ERR_INVALID, PA_ERR_UNSUPPORTED, PA_ERR_WORKSPACE, PA_ERR_HIP = range(5)
+PA_OK, PA_ERR_INVALID, PA_ERR_UNSUPPORTED, PA_ERR_WORKSPACE, PA_ERR_HIP, PA_ERR_EXHAUSTED = range(6)
 PA_DECODE_KV_STREAM = 1
 
 _i32, _i64, _f32, _f64, _vp = ctypes.c_int32, ctypes.c_int64, ctypes.c_float, ctypes.c_double, ctypes.c_void_p
@@ -48,6 +49,23 @@ SIGNATURES = {
     "pa_graph_end": (ctypes.c_int, [_vp, ctypes.POINTER(_vp)]),
     "pa_graph_launch": (ctypes.c_int, [_vp, _vp]),
     "pa_graph_destroy": (None, [_vp]),
+    "pa_bm_create": (ctypes.c_int, [_i64, _i32, ctypes.POINTER(_vp)]),
+    "pa_bm_destroy": (None, [_vp]),
+    "pa_bm_allocate": (ctypes.c_int, [_vp, _i64, _i64]),
+    "pa_bm_append_slot": (ctypes.c_int, [_vp, _i64, ctypes.POINTER(_i64), ctypes.POINTER(_i64),
+                                         ctypes.POINTER(_i64)]),
+    "pa_bm_append_slots": (ctypes.c_int, [_vp, _vp, _i32, _vp, _vp, ctypes.POINTER(_i32),
+                                          ctypes.POINTER(_i32)]),
+    "pa_bm_fork": (ctypes.c_int, [_vp, _i64, _i64]),
+    "pa_bm_free": (ctypes.c_int, [_vp, _i64]),
+    "pa_bm_block_tables": (ctypes.c_int, [_vp, _vp, _i32, _i32, _i32, _vp, _vp]),
+    "pa_bm_seq_len": (_i64, [_vp, _i64]),
+    "pa_bm_seq_table": (_i64, [_vp, _i64, _vp, _i64]),
+    "pa_bm_num_free": (_i64, [_vp]),
+    "pa_bm_free_list": (_i64, [_vp, _vp, _i64]),
+    "pa_bm_refcount": (_i32, [_vp, _i64]),
+    "pa_bm_usage": (_f64, [_vp]),
+    "pa_bm_slot_utilisation": (_f64, [_vp]),
 }
 
 
@@ -319,3 +337,117 @@ class StepGraph:
             self.close()
         except Exception:
             pass
+
+
+# ---------------------------------------------------------------------------------------
+# host block manager
+# ---------------------------------------------------------------------------------------
+
+class KVCacheExhausted(PagedKVError):
+    """The block manager's free list cannot cover the request (nothing was taken)."""
+
+
+def _bm_check(fn, status):
+    if status == PA_ERR_EXHAUSTED:
+        raise KVCacheExhausted(fn, status)
+    if status == PA_ERR_INVALID:
+        raise ValueError(f"{fn}: invalid argument (unknown or existing sequence, bad size)")
+    _check(fn, status)
+
+
+class BlockManager:
+    """The library's host block manager (``pa_bm_*``): sequences, their blocks, reference
+    counts, copy-on-write and the free list. Sequence ids are Python ints."""
+
+    def __init__(self, num_blocks: int, block_size: int = 16):
+        h = _vp()
+        _bm_check("pa_bm_create", load().pa_bm_create(int(num_blocks), int(block_size), ctypes.byref(h)))
+        self._h = h
+        self.num_blocks, self.block_size = int(num_blocks), int(block_size)
+
+    def close(self):
+        if getattr(self, "_h", None) is not None and self._h.value:
+            load().pa_bm_destroy(self._h)
+            self._h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def allocate(self, seq_id: int, num_tokens: int):
+        _bm_check("pa_bm_allocate", load().pa_bm_allocate(self._h, int(seq_id), int(num_tokens)))
+        return self.table_of(seq_id)
+
+    def append_token(self, seq_id: int):
+        """(slot, (src, dst) copy or None) of the sequence's next token."""
+        slot, src, dst = _i64(), _i64(), _i64()
+        _bm_check("pa_bm_append_slot", load().pa_bm_append_slot(
+            self._h, int(seq_id), ctypes.byref(slot), ctypes.byref(src), ctypes.byref(dst)))
+        return slot.value, (None if src.value < 0 else (src.value, dst.value))
+
+    def append_slots(self, seq_ids):
+        """One token per listed sequence: (slot_mapping int64 [n], copies int64 [k, 2]).
+        On exhaustion raises KVCacheExhausted; ``self.last_done`` tells how many were
+        appended before it."""
+        ids = np.ascontiguousarray(seq_ids, dtype=np.int64)
+        n = len(ids)
+        slots = np.empty(n, dtype=np.int64)
+        copies = np.empty((max(n, 1), 2), dtype=np.int64)
+        nc, nd = _i32(), _i32()
+        st = load().pa_bm_append_slots(self._h, ids.ctypes.data, n, slots.ctypes.data,
+                                       copies.ctypes.data, ctypes.byref(nc), ctypes.byref(nd))
+        self.last_done = nd.value
+        self.last_slots, self.last_copies = slots, copies[: nc.value].copy()
+        _bm_check("pa_bm_append_slots", st)
+        return slots, copies[: nc.value].copy()
+
+    def fork(self, parent: int, child: int):
+        _bm_check("pa_bm_fork", load().pa_bm_fork(self._h, int(parent), int(child)))
+        return self.table_of(child)
+
+    def free(self, seq_id: int):
+        _bm_check("pa_bm_free", load().pa_bm_free(self._h, int(seq_id)))
+
+    def block_tables(self, seq_ids, max_blocks: int, pad: int = 0):
+        """Padded int32 tables [n, max_blocks] and int32 lengths [n] of the sequences."""
+        ids = np.ascontiguousarray(seq_ids, dtype=np.int64)
+        tables = np.empty((len(ids), max_blocks), dtype=np.int32)
+        lens = np.empty(len(ids), dtype=np.int32)
+        _bm_check("pa_bm_block_tables", load().pa_bm_block_tables(
+            self._h, ids.ctypes.data, len(ids), int(max_blocks), int(pad), tables.ctypes.data,
+            lens.ctypes.data))
+        return tables, lens
+
+    def table_of(self, seq_id: int):
+        n = load().pa_bm_seq_table(self._h, int(seq_id), None, 0)
+        if n < 0:
+            raise ValueError(f"unknown sequence {seq_id}")
+        out = np.empty(max(n, 1), dtype=np.int32)
+        load().pa_bm_seq_table(self._h, int(seq_id), out.ctypes.data, n)
+        return [int(b) for b in out[:n]]
+
+    def len_of(self, seq_id: int) -> int:
+        n = load().pa_bm_seq_len(self._h, int(seq_id))
+        if n < 0:
+            raise ValueError(f"unknown sequence {seq_id}")
+        return int(n)
+
+    def free_list(self):
+        n = load().pa_bm_num_free(self._h)
+        out = np.empty(max(n, 1), dtype=np.int32)
+        load().pa_bm_free_list(self._h, out.ctypes.data, n)
+        return [int(b) for b in out[:n]]
+
+    def num_free(self) -> int:
+        return int(load().pa_bm_num_free(self._h))
+
+    def refs_of(self, block: int) -> int:
+        return int(load().pa_bm_refcount(self._h, int(block)))
+
+    def usage(self) -> float:
+        return float(load().pa_bm_usage(self._h))
+
+    def slot_utilisation(self) -> float:
+        return float(load().pa_bm_slot_utilisation(self._h))

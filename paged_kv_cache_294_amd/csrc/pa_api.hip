@@ -54,6 +54,7 @@ PA_EXPORT const char* pa_status_string(int status) {
     case PA_ERR_UNSUPPORTED: return "unsupported configuration";
     case PA_ERR_WORKSPACE: return "workspace too small";
     case PA_ERR_HIP: return "HIP runtime error";
+    case PA_ERR_EXHAUSTED: return "KV cache exhausted";
     default: return "unknown status";
   }
 }

@@ -56,7 +56,7 @@ def test_abi_version(lib):
 
 
 def test_status_strings(lib):
-    for s in range(5):
+    for s in range(6):
         assert lib.pa_status_string(s)
     assert lib.pa_status_string(99) == b"unknown status"
 
