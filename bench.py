@@ -242,6 +242,50 @@ def block_manager_leg(pkv, inp):
     return out
 
 
+def block_copy_leg(torch, pkv, num_kv_heads, head_size, reps=10):
+    """Rates of the block copies, on buffers of their own: copy-on-write copies inside a
+    2 GiB pool, half its blocks onto the other half (disjoint pairs: every byte read once
+    and written once, against HBM; 8x the 256 MB last-level cache), and swaps of 128
+    blocks to pinned host memory and back (against a torch copy of the same bytes between
+    the same memories, the host-link rate)."""
+    elems = 16 * 2 * num_kv_heads * head_size
+    block_bytes = 2 * elems
+    nb = (2 << 30) // block_bytes
+    npairs, nswap = nb // 2, min(128, nb // 4)
+    pool = torch.zeros((nb, elems), dtype=torch.float16, device="cuda")
+    perm = torch.randperm(nb, generator=torch.Generator().manual_seed(0))
+    pairs = torch.stack([perm[:npairs], perm[npairs:]], 1).contiguous().cuda()
+    host_area = torch.zeros((nswap, elems), dtype=torch.float16).pin_memory()
+    out_pairs = torch.stack([perm[:nswap], torch.arange(nswap)], 1).contiguous().cuda()
+    in_pairs = torch.stack([torch.arange(nswap), perm[npairs:npairs + nswap]], 1).contiguous().cuda()
+    flat_dev = torch.zeros((nswap, elems), dtype=torch.float16, device="cuda")
+
+    def rate(fn, nbytes):
+        fn()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(reps):
+            fn()
+        b.record()
+        torch.cuda.synchronize()
+        ms = a.elapsed_time(b) / reps
+        return {"us": ms * 1e3, "GBps": nbytes / (ms * 1e-3) / 1e9}
+
+    res = {
+        "block_bytes": block_bytes,
+        "copy_on_write": rate(lambda: pkv.pa_copy_blocks(
+            pool.view(nb, 16, 2, num_kv_heads, head_size), pairs),
+                              2 * npairs * block_bytes),
+        "swap_out": rate(lambda: pkv.pa_move_blocks(host_area, pool, out_pairs), nswap * block_bytes),
+        "swap_in": rate(lambda: pkv.pa_move_blocks(pool, host_area, in_pairs), nswap * block_bytes),
+        "torch_copy_d2h": rate(lambda: host_area.copy_(flat_dev, non_blocking=True), nswap * block_bytes),
+        "torch_copy_h2d": rate(lambda: flat_dev.copy_(host_area, non_blocking=True), nswap * block_bytes),
+    }
+    res["copy_on_write"]["frac_hbm_peak"] = res["copy_on_write"]["GBps"] / HBM_PEAK_GBPS
+    return res
+
+
 class Step:
     """Device copies of a batch and one step of the hot path over them."""
 
@@ -375,6 +419,7 @@ def main():
                          "Per-kernel times always come from eager steps")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-stream-read", action="store_true")
+    ap.add_argument("--no-block-copies", action="store_true")
     ap.add_argument("--cpu-cores", type=int, default=16)
     ap.add_argument("--mode", choices=("bench", "counters"), default="bench",
                     help="counters: a short fixed dispatch sequence for rocprofv3 --pmc passes "
@@ -481,6 +526,14 @@ def main():
         graph.close()
         log(f"graph replay: step {ms_step:.3f} ms (eager {eager_ms_step:.3f} ms)")
 
+    copies = None
+    if not args.no_block_copies:
+        copies = block_copy_leg(torch, pkv, inp.num_kv_heads, inp.head_size)
+        log("block copies: copy-on-write {:.0f} GB/s, swap out {:.1f} GB/s, swap in {:.1f} GB/s "
+            "(torch copies {:.1f} / {:.1f} GB/s)".format(
+                copies["copy_on_write"]["GBps"], copies["swap_out"]["GBps"], copies["swap_in"]["GBps"],
+                copies["torch_copy_d2h"]["GBps"], copies["torch_copy_h2d"]["GBps"]))
+
     achieved = kv_bytes / (decode_ms * 1e-3) / 1e9
     nparts = pkv.pa_num_partitions(step.mcl, args.partition_size)
     traffic = read_traffic(f"pa_decode_{args.workload}_counters.txt", source_digest(DECODE_SRC))
@@ -539,6 +592,7 @@ def main():
         "cpu_baseline": None if cpu is None else {k: cpu[k] for k in
                                                   ("value", "unit", "cores", "kind", "sample")},
         "block_manager": bm,
+        "block_copies": copies,
         "stream_read_gbps": stream_gbps,
         "frac_of_stream_read": None if not stream_gbps else achieved / stream_gbps,
         "context": {

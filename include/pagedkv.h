@@ -202,6 +202,29 @@ pa_status pa_gather_kv(void* k_out, void* v_out, const void* kv_pool,
 pa_status pa_stream_read(const void* buf, int64_t bytes, float* sink, void* stream);
 int64_t pa_stream_read_sink_len(int64_t bytes);
 
+/* ---- block copies ---------------------------------------------------------------------
+ * pa_copy_blocks: inside the pool, block pairs[2k+1] = block pairs[2k] for k < num_pairs:
+ * the device half of copy-on-write, run before the step's appends when the block manager
+ * reports copies (sequences sharing prefix blocks: page "vLLM GitHub 项目 …", section 二,
+ * item 4). Whole blocks (block_size token rows of K and V for every head) are copied.
+ *   pairs   device-accessible int64 [num_pairs][2] (source, destination); a pair naming a
+ *           block outside [0, num_blocks) is skipped. Destinations must be distinct and
+ *           must not be sources of other pairs of the same call (the pairs run
+ *           concurrently), as holds for the copies of one step of the block manager.
+ * pa_move_blocks: dst block d = src block s for each (s, d) pair, blocks of block_bytes
+ * bytes (a multiple of 16) in two buffers of dst_blocks and src_blocks blocks: swapping
+ * blocks out of the pool into a CPU swap area and back (--swap-space in the flag table of
+ * page "vLLM 部署深度指南"). dst, src and pairs may each be device memory or pinned host
+ * memory (hipHostMalloc; the kernel reads and writes it over the host link); any other
+ * host memory is refused with PA_ERR_INVALID before a launch. Same rules on pairs.
+ * Both are asynchronous on `stream`. */
+pa_status pa_copy_blocks(void* kv_pool, const int64_t* pairs, int32_t num_pairs,
+                         int32_t block_size, int32_t num_kv_heads, int32_t head_size,
+                         int64_t num_blocks, void* stream);
+pa_status pa_move_blocks(void* dst, const void* src, const int64_t* pairs, int32_t num_pairs,
+                         int64_t block_bytes, int64_t dst_blocks, int64_t src_blocks,
+                         void* stream);
+
 /* ---- captured steps (HIP graphs) ----------------------------------------------------
  * A step (append, prefill, decode, reduce) is a few launches whose host-side cost rules
  * small batches; serving engines replay such a step from a captured graph (page "vLLM

@@ -18,12 +18,14 @@ from ._lib import (  # noqa: F401
     load,
     pa_abi_version,
     pa_block_bytes,
+    pa_copy_blocks,
     pa_blocks_for_len,
     pa_decode,
     pa_decode_workspace_bytes,
     pa_gather_kv,
     pa_kv_append,
     pa_kv_elem_offset,
+    pa_move_blocks,
     pa_num_blocks_fit,
     pa_num_partitions,
     pa_pool_bytes,

@@ -45,6 +45,8 @@ SIGNATURES = {
     "pa_gather_kv": (ctypes.c_int, [_vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i64, _vp]),
     "pa_stream_read": (ctypes.c_int, [_vp, _i64, _vp, _vp]),
     "pa_stream_read_sink_len": (_i64, [_i64]),
+    "pa_copy_blocks": (ctypes.c_int, [_vp, _vp, _i32, _i32, _i32, _i32, _i64, _vp]),
+    "pa_move_blocks": (ctypes.c_int, [_vp, _vp, _vp, _i32, _i64, _i64, _i64, _vp]),
     "pa_graph_begin": (ctypes.c_int, [_vp]),
     "pa_graph_end": (ctypes.c_int, [_vp, ctypes.POINTER(_vp)]),
     "pa_graph_launch": (ctypes.c_int, [_vp, _vp]),
@@ -268,6 +270,43 @@ def pa_gather_kv(k_out, v_out, kv_pool, block_table_row, length, stream=None):
         _dense(block_table_row, "block_table_row", torch.int32), int(length), hkv, d, bs, nb,
         _stream(stream))
     _check("pa_gather_kv", st)
+
+
+def _pairs(pairs):
+    if not isinstance(pairs, torch.Tensor) or pairs.dtype != torch.int64 or not pairs.is_contiguous():
+        raise TypeError("pairs must be a contiguous int64 tensor [n, 2]")
+    if pairs.dim() != 2 or pairs.shape[1] != 2:
+        raise ValueError("pairs must be [n, 2]")
+    if not (pairs.is_cuda or pairs.is_pinned()):
+        raise ValueError("pairs must be device memory or pinned host memory")
+    return pairs.data_ptr(), int(pairs.shape[0])
+
+
+def pa_copy_blocks(kv_pool, pairs, stream=None):
+    """Copy-on-write copies inside the pool: block pairs[k, 1] = block pairs[k, 0]."""
+    nb, bs, hkv, d = _pool_geometry(kv_pool)
+    pp, n = _pairs(pairs)
+    st = load().pa_copy_blocks(_dense(kv_pool, "kv_pool", torch.float16), pp, n, bs, hkv, d, nb,
+                               _stream(stream))
+    _check("pa_copy_blocks", st)
+
+
+def pa_move_blocks(dst, src, pairs, stream=None):
+    """dst[pairs[k, 1]] = src[pairs[k, 0]] for whole blocks (leading dimension). dst and
+    src are dense tensors on the device or in pinned host memory with the same block
+    size in bytes (swap out: pool -> host; swap in: host -> pool)."""
+    for t, name in ((dst, "dst"), (src, "src")):
+        if not isinstance(t, torch.Tensor) or not t.is_contiguous() or t.dim() < 1:
+            raise TypeError(f"{name} must be a dense tensor of blocks")
+        if not (t.is_cuda or t.is_pinned()):
+            raise ValueError(f"{name} must be device memory or pinned host memory")
+    bb = dst.numel() // dst.shape[0] * dst.element_size()
+    if src.numel() // src.shape[0] * src.element_size() != bb:
+        raise ValueError("dst and src blocks differ in size")
+    pp, n = _pairs(pairs)
+    st = load().pa_move_blocks(dst.data_ptr(), src.data_ptr(), pp, n, bb, int(dst.shape[0]),
+                               int(src.shape[0]), _stream(stream))
+    _check("pa_move_blocks", st)
 
 
 def pa_stream_read_sink_len(nbytes: int) -> int:

@@ -20,7 +20,7 @@ LIB_PATH = os.path.join(HERE, LIB_NAME)
 ARCH = "gfx950"
 
 SOURCES = ["pa_api.hip", "kv_append.hip", "pa_decode.hip", "pa_prefill.hip", "pa_gather.hip",
-           "block_manager.cpp"]
+           "pa_blocks.hip", "block_manager.cpp"]
 
 HIPCC_FLAGS = [
     f"--offload-arch={ARCH}",

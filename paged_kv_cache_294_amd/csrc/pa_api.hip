@@ -276,6 +276,72 @@ PA_EXPORT pa_status pa_stream_read(const void* buf, int64_t bytes, float* sink, 
 }
 
 // ---------------------------------------------------------------------------------------
+// block copies
+// ---------------------------------------------------------------------------------------
+
+namespace {
+
+// The address kernels use for `p`: device memory as is, pinned host memory through its
+// device mapping. Anything else (pageable host memory) is refused, since a kernel access
+// to it would fault.
+pa_status device_view(const void* p, const void** out) {
+  hipPointerAttribute_t attr;
+  if (hipPointerGetAttributes(&attr, p) != hipSuccess) {
+    (void)hipGetLastError();  // do not leave the refusal for the next launch check
+    return PA_ERR_INVALID;
+  }
+  if (attr.type == hipMemoryTypeHost) {
+    void* d = nullptr;
+    if (hipHostGetDevicePointer(&d, const_cast<void*>(p), 0) != hipSuccess || d == nullptr) {
+      (void)hipGetLastError();
+      return PA_ERR_INVALID;
+    }
+    *out = d;
+    return PA_OK;
+  }
+  if (attr.type == hipMemoryTypeDevice || attr.type == hipMemoryTypeManaged ||
+      attr.type == hipMemoryTypeUnified) {
+    *out = p;
+    return PA_OK;
+  }
+  return PA_ERR_INVALID;
+}
+
+}  // namespace
+
+PA_EXPORT pa_status pa_move_blocks(void* dst, const void* src, const int64_t* pairs,
+                                   int32_t num_pairs, int64_t block_bytes, int64_t dst_blocks,
+                                   int64_t src_blocks, void* stream) {
+  if (num_pairs < 0 || block_bytes <= 0 || block_bytes % 16 != 0 || dst_blocks <= 0 ||
+      src_blocks <= 0)
+    return PA_ERR_INVALID;
+  if (num_pairs == 0) return PA_OK;
+  if (!dst || !src || !pairs || !aligned16(dst) || !aligned16(src) ||
+      (reinterpret_cast<uintptr_t>(pairs) & 7u))
+    return PA_ERR_INVALID;
+  const void *d = nullptr, *s = nullptr, *p = nullptr;
+  pa_status st;
+  if ((st = device_view(dst, &d)) != PA_OK || (st = device_view(src, &s)) != PA_OK ||
+      (st = device_view(pairs, &p)) != PA_OK)
+    return st;
+  return hip_status(pkv::launch_move_blocks(const_cast<void*>(d), s,
+                                            static_cast<const int64_t*>(p), num_pairs,
+                                            block_bytes, dst_blocks, src_blocks,
+                                            static_cast<hipStream_t>(stream)));
+}
+
+PA_EXPORT pa_status pa_copy_blocks(void* kv_pool, const int64_t* pairs, int32_t num_pairs,
+                                   int32_t block_size, int32_t num_kv_heads, int32_t head_size,
+                                   int64_t num_blocks, void* stream) {
+  pa_status st = check_geometry(block_size, num_kv_heads, head_size);
+  if (st != PA_OK) return st;
+  if (num_blocks <= 0) return PA_ERR_INVALID;
+  const int64_t block_bytes = (int64_t)block_size * 2 * num_kv_heads * head_size * 2;
+  return pa_move_blocks(kv_pool, kv_pool, pairs, num_pairs, block_bytes, num_blocks, num_blocks,
+                        stream);
+}
+
+// ---------------------------------------------------------------------------------------
 // captured steps
 // ---------------------------------------------------------------------------------------
 

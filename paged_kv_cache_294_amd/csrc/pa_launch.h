@@ -51,4 +51,8 @@ hipError_t launch_gather_kv(void* k_out, void* v_out, const void* pool, const in
 int64_t stream_read_groups(int64_t bytes);
 hipError_t launch_stream_read(const void* buf, int64_t bytes, float* sink, hipStream_t stream);
 
+hipError_t launch_move_blocks(void* dst, const void* src, const int64_t* pairs, int num_pairs,
+                              int64_t block_bytes, int64_t dst_blocks, int64_t src_blocks,
+                              hipStream_t stream);
+
 }  // namespace pkv

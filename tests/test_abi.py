@@ -183,3 +183,16 @@ def test_graph_calls_reject_without_touching_the_gpu(lib):
     lib.pa_graph_destroy(None)  # ignored
     with pytest.raises(ValueError):
         pkv.StepGraph(None)
+
+
+def test_block_copies_reject_before_any_launch(lib):
+    # block size not 16 / head size unsupported / bad counts: refused from the scalars
+    assert lib.pa_copy_blocks(FAKE, FAKE, 1, 32, 4, 64, 16, None) == pkv.PA_ERR_UNSUPPORTED
+    assert lib.pa_copy_blocks(FAKE, FAKE, 1, 16, 4, 80, 16, None) == pkv.PA_ERR_UNSUPPORTED
+    assert lib.pa_copy_blocks(FAKE, FAKE, 1, 16, 4, 64, 0, None) == pkv.PA_ERR_INVALID
+    assert lib.pa_copy_blocks(FAKE, FAKE, 0, 16, 4, 64, 16, None) == pkv.PA_OK
+    assert lib.pa_move_blocks(FAKE, FAKE, FAKE, 1, 100, 4, 4, None) == pkv.PA_ERR_INVALID  # % 16
+    assert lib.pa_move_blocks(FAKE, FAKE, FAKE, -1, 256, 4, 4, None) == pkv.PA_ERR_INVALID
+    assert lib.pa_move_blocks(0, FAKE, FAKE, 1, 256, 4, 4, None) == pkv.PA_ERR_INVALID
+    assert lib.pa_move_blocks(FAKE + 8, FAKE, FAKE, 1, 256, 4, 4, None) == pkv.PA_ERR_INVALID
+    assert lib.pa_move_blocks(FAKE, FAKE, FAKE, 0, 256, 4, 4, None) == pkv.PA_OK
