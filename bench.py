@@ -65,15 +65,15 @@ def log(msg):
 # algorithmic work
 # ---------------------------------------------------------------------------------------
 
-def kv_read_bytes(inp) -> int:
+def kv_read_bytes(inp, elem_bytes=2) -> int:
     """Decode KV bytes: each decode context token's K and V rows once (logical)."""
     lens = inp.seq_lens[inp.num_prefill:].astype(np.int64)
-    return int(lens.sum()) * 2 * inp.num_kv_heads * inp.head_size * 2
+    return int(lens.sum()) * 2 * inp.num_kv_heads * inp.head_size * elem_bytes
 
 
-def kv_unique_bytes(inp) -> int:
+def kv_unique_bytes(inp, elem_bytes=2) -> int:
     """Decode KV bytes counting each physical block's filled slots once (shared prefixes)."""
-    row = 2 * inp.num_kv_heads * inp.head_size * 2
+    row = 2 * inp.num_kv_heads * inp.head_size * elem_bytes
     seen = {}
     for b in range(inp.num_prefill, inp.num_seqs):
         L = int(inp.seq_lens[b])
@@ -93,8 +93,9 @@ def prefill_flops(inp) -> int:
     return 4 * inp.head_size * inp.num_q_heads * tot
 
 
-def append_bytes(inp) -> int:
-    return 2 * len(inp.slot_mapping) * 2 * inp.num_kv_heads * inp.head_size * 2
+def append_bytes(inp, elem_bytes=2) -> int:
+    """fp16 rows read, pool rows written (fp16 or one byte per FP8 element)."""
+    return len(inp.slot_mapping) * 2 * inp.num_kv_heads * inp.head_size * (2 + elem_bytes)
 
 
 def shares_blocks(inp) -> bool:
@@ -289,13 +290,17 @@ def block_copy_leg(torch, pkv, num_kv_heads, head_size, reps=10):
 class Step:
     """Device copies of a batch and one step of the hot path over them."""
 
-    def __init__(self, torch, pkv, inp, partition_size, kv_stream):
+    def __init__(self, torch, pkv, inp, partition_size, kv_stream, kv_fp8=False):
         self.torch, self.pkv, self.inp = torch, pkv, inp
 
         def c(a):
             return torch.from_numpy(np.ascontiguousarray(a)).cuda()
 
         self.pool = c(inp.pool)
+        self.kv_fp8 = kv_fp8
+        if kv_fp8:  # E4M3 codes of the same values (scale 1; N(0, 1) data is in range)
+            self.pool = self.pool.to(torch.float8_e4m3fn).view(torch.uint8)
+            torch.cuda.synchronize()
         self.key, self.value, self.slots = c(inp.key_new), c(inp.value_new), c(inp.slot_mapping)
         qd, btd, lensd = inp.decode_part()
         self.dq, self.dbt, self.dlens = c(qd), c(btd), c(lensd)
@@ -323,14 +328,21 @@ class Step:
 
         rec(0)
         if len(self.inp.slot_mapping):
-            pkv.pa_kv_append(self.pool, self.key, self.value, self.slots, stream=stream)
+            if self.kv_fp8:
+                pkv.pa_kv_append_fp8(self.pool, self.key, self.value, self.slots, 1.0, 1.0, stream=stream)
+            else:
+                pkv.pa_kv_append(self.pool, self.key, self.value, self.slots, stream=stream)
         rec(1)
         if self.has_prefill:
             pkv.pa_prefill_chunk(self.pout, self.pq, self.pool, self.pbt, self.qsl, self.plens,
                                  self.max_q, self.max_s, self.inp.scale, stream=stream)
         rec(2)
-        pkv.pa_decode(self.dout, self.dq, self.pool, self.dbt, self.dlens, self.mcl, self.inp.scale,
-                      self.ps, self.ws, self.flags, stream=stream)
+        if self.kv_fp8:
+            pkv.pa_decode_fp8(self.dout, self.dq, self.pool, self.dbt, self.dlens, self.mcl,
+                              self.inp.scale, 1.0, 1.0, self.ps, self.ws, self.flags, stream=stream)
+        else:
+            pkv.pa_decode(self.dout, self.dq, self.pool, self.dbt, self.dlens, self.mcl,
+                          self.inp.scale, self.ps, self.ws, self.flags, stream=stream)
         rec(3)
 
 
@@ -420,6 +432,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-stream-read", action="store_true")
     ap.add_argument("--no-block-copies", action="store_true")
+    ap.add_argument("--kv-dtype", choices=("fp16", "fp8"), default="fp16",
+                    help="cache element: fp16, or FP8 E4M3 codes (decode-only workloads; the "
+                         "prefill kernel reads fp16 caches only)")
     ap.add_argument("--cpu-cores", type=int, default=16)
     ap.add_argument("--mode", choices=("bench", "counters"), default="bench",
                     help="counters: a short fixed dispatch sequence for rocprofv3 --pmc passes "
@@ -451,14 +466,22 @@ def main():
         f"{inp.num_seqs} sequences, sum L = {int(inp.seq_lens.sum())}")
     shared = shares_blocks(inp)
     kv_stream = {"on": True, "off": False, "auto": not shared}[args.kv_stream]
-    kv_bytes = kv_read_bytes(inp)
+    kv_fp8 = args.kv_dtype == "fp8"
+    elem_bytes = 1 if kv_fp8 else 2
+    if kv_fp8 and inp.num_prefill:
+        print("--kv-dtype fp8 runs decode-only workloads (c1-c4): pa_prefill_chunk reads fp16 "
+              "caches only", file=sys.stderr)
+        sys.exit(2)
+    kv_bytes = kv_read_bytes(inp, elem_bytes)
 
     if args.mode == "counters":
         run_counter_sequence(inp, args.partition_size, kv_stream)
         return
 
     cpu = None
-    if not args.no_cpu_baseline:
+    if kv_fp8 and not args.no_cpu_baseline:
+        log("CPU baseline skipped for the FP8 cache (the oracle's fp16 run is the reference)")
+    elif not args.no_cpu_baseline:
         log("CPU baseline: oracle on the host cores")
         cpu = cpu_baseline(inp, args.cpu_cores, decode_seqs=4 if args.workload == "c3" else None)
         log(f"CPU baseline done in {cpu['seconds']:.1f}s on {cpu['cores']} cores")
@@ -482,7 +505,7 @@ def main():
         log(f"host block manager: admit {bm['admit_us']:.0f} us, step {bm['step_us']:.0f} us "
             f"({bm['new_tokens']} slots + tables)")
     log("copying the batch to the GPU")
-    step = Step(torch, pkv, inp, args.partition_size, kv_stream)
+    step = Step(torch, pkv, inp, args.partition_size, kv_stream, kv_fp8)
     for _ in range(args.warmup):
         step.run()
     torch.cuda.synchronize()
@@ -536,21 +559,21 @@ def main():
 
     achieved = kv_bytes / (decode_ms * 1e-3) / 1e9
     nparts = pkv.pa_num_partitions(step.mcl, args.partition_size)
-    traffic = read_traffic(f"pa_decode_{args.workload}_counters.txt", source_digest(DECODE_SRC))
+    traffic = read_traffic(f"pa_decode_{args.workload}{'_fp8' if kv_fp8 else ''}_counters.txt", source_digest(DECODE_SRC))
     used_blocks = int(sum(-(-int(L) // 16) for L in inp.seq_lens))
     kernels = {"decode": {"ms": decode_ms, "kv_read_GBps": achieved,
                           "frac_hbm_peak": achieved / HBM_PEAK_GBPS, "partitions": nparts,
                           "kv_stream": kv_stream}}
     if len(inp.slot_mapping):
         kernels["append"] = {"us": append_ms * 1e3, "tokens": len(inp.slot_mapping),
-                             "GBps": append_bytes(inp) / (append_ms * 1e-3) / 1e9}
+                             "GBps": append_bytes(inp, elem_bytes) / (append_ms * 1e-3) / 1e9}
     if inp.num_prefill:
         fl = prefill_flops(inp)
         tf = fl / (prefill_ms * 1e-3) / 1e12
         kernels["prefill"] = {"us": prefill_ms * 1e3, "gflop": fl / 1e9, "TFLOPs": tf,
                               "frac_mfma_peak": tf / MFMA_F16_PEAK_TFLOPS}
     if shared:
-        ub = kv_unique_bytes(inp)
+        ub = kv_unique_bytes(inp, elem_bytes)
         kernels["decode"]["unique_kv_bytes"] = ub
         kernels["decode"]["unique_kv_GBps"] = ub / (decode_ms * 1e-3) / 1e9
     result = {
@@ -564,7 +587,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f16",
+        "dtype": "f16, fp8 e4m3 cache" if kv_fp8 else "f16",
         "data": "synthetic",
         "config": {
             "workload": desc,
@@ -573,6 +596,7 @@ def main():
             "block_size": inp.block_size, "partition_size": args.partition_size,
             "sum_context_tokens": int(inp.seq_lens.sum()), "seed": seed,
             "launch": "hip graph replay" if args.launch == "graph" else "eager",
+            "kv_dtype": args.kv_dtype,
         },
         "eager_ms_per_step": eager_ms_step,
         "pct_of_hbm_peak": 100.0 * kv_bytes / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBPS,

@@ -158,6 +158,34 @@ pa_status pa_decode(void* out, const void* q, const void* kv_pool, const int32_t
                     float scale, int32_t partition_size, void* workspace,
                     int64_t workspace_bytes, uint32_t flags, void* stream);
 
+/* ---- FP8 KV cache ---------------------------------------------------------------------
+ * The pool may hold OCP FP8 E4M3 codes, one byte per element, in the same layout
+ * [num_blocks][block_size][2][num_kv_heads][head_size] (page "vLLM 部署深度指南": the FP8
+ * deployment command's --kv-cache-dtype fp8; FP8 halves memory in the quantisation
+ * table). One fp32 scale per tensor: a key element x is stored as the E4M3 code of
+ * fp32(x) * fp32(1 / k_scale) (the product rounded once in fp32), rounded to nearest
+ * even, magnitudes of 448 and more saturated to 448, NaN kept NaN; values likewise with
+ * v_scale. Attention reads code value * scale. Both scales must be finite and > 0.
+ *
+ * pa_kv_append_fp8: pa_kv_append into an E4M3 pool (key and value are fp16 as before;
+ *   the pool's element is one byte). Writes exactly the codes above.
+ * pa_decode_fp8: pa_decode over an E4M3 pool, same arguments and results plus the two
+ *   scales; each code is widened exactly to fp16 and the scales applied in fp32 (the key
+ *   scale with the softmax scale, the value scale with the final normalisation). */
+pa_status pa_kv_append_fp8(void* kv_pool, const void* key, const void* value,
+                           const int64_t* slot_mapping, int32_t num_tokens,
+                           int32_t num_kv_heads, int32_t head_size, int32_t block_size,
+                           int64_t num_blocks, int64_t key_token_stride,
+                           int64_t value_token_stride, float k_scale, float v_scale,
+                           void* stream);
+pa_status pa_decode_fp8(void* out, const void* q, const void* kv_pool,
+                        const int32_t* block_tables, const int32_t* context_lens,
+                        int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                        int32_t head_size, int32_t block_size, int32_t max_blocks_per_seq,
+                        int64_t num_blocks, int32_t max_context_len, float scale,
+                        float k_scale, float v_scale, int32_t partition_size, void* workspace,
+                        int64_t workspace_bytes, uint32_t flags, void* stream);
+
 /* Causal attention of prefill chunks over their paged context (the scheduler on
  * page "vLLM 部署深度指南" puts prefills and decodes into one step). Request r owns
  * query rows [query_start_loc[r], query_start_loc[r+1]) and seq_lens[r] tokens in

@@ -21,9 +21,11 @@ from ._lib import (  # noqa: F401
     pa_copy_blocks,
     pa_blocks_for_len,
     pa_decode,
+    pa_decode_fp8,
     pa_decode_workspace_bytes,
     pa_gather_kv,
     pa_kv_append,
+    pa_kv_append_fp8,
     pa_kv_elem_offset,
     pa_move_blocks,
     pa_num_blocks_fit,

@@ -40,6 +40,11 @@ SIGNATURES = {
     "pa_kv_append": (ctypes.c_int, [_vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i64, _i64, _i64, _vp]),
     "pa_decode": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _i64,
                                  _i32, _f32, _i32, _vp, _i64, ctypes.c_uint32, _vp]),
+    "pa_kv_append_fp8": (ctypes.c_int, [_vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i64, _i64, _i64,
+                                        _f32, _f32, _vp]),
+    "pa_decode_fp8": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32,
+                                     _i64, _i32, _f32, _f32, _f32, _i32, _vp, _i64, ctypes.c_uint32,
+                                     _vp]),
     "pa_prefill_chunk": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32,
                                         _i32, _i32, _i32, _i32, _i64, _f32, _vp]),
     "pa_gather_kv": (ctypes.c_int, [_vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i64, _vp]),
@@ -185,30 +190,36 @@ def pa_decode_workspace_bytes(num_seqs: int, num_q_heads: int, max_context_len: 
 # device operations
 # ---------------------------------------------------------------------------------------
 
-def pa_kv_append(kv_pool, key, value, slot_mapping, stream=None):
-    """Write key[t] / value[t] ([T, Hkv, D] fp16) into pool slot slot_mapping[t] (int64)."""
+def _append_args(kv_pool, key, value, slot_mapping, pool_dtype):
     nb, bs, hkv, d = _pool_geometry(kv_pool)
-    pool_p = _dense(kv_pool, "kv_pool", torch.float16)
+    pool_p = _dense(kv_pool, "kv_pool", pool_dtype)
     slots_p = _dense(slot_mapping, "slot_mapping", torch.int64)
     T = int(slot_mapping.shape[0])
     for t, name in ((key, "key"), (value, "value")):
         _dev(t, name, torch.float16)
         if tuple(t.shape) != (T, hkv, d) or t.stride(2) != 1 or t.stride(1) != d:
             raise ValueError(f"{name} must be [T, num_kv_heads, head_size] with dense rows")
-    st = load().pa_kv_append(pool_p, key.data_ptr(), value.data_ptr(), slots_p, T, hkv, d, bs, nb,
-                             key.stride(0), value.stride(0), _stream(stream))
+    return (pool_p, key.data_ptr(), value.data_ptr(), slots_p, T, hkv, d, bs, nb, key.stride(0),
+            value.stride(0))
+
+
+def pa_kv_append(kv_pool, key, value, slot_mapping, stream=None):
+    """Write key[t] / value[t] ([T, Hkv, D] fp16) into pool slot slot_mapping[t] (int64)."""
+    st = load().pa_kv_append(*_append_args(kv_pool, key, value, slot_mapping, torch.float16),
+                             _stream(stream))
     _check("pa_kv_append", st)
 
 
-def pa_decode(out, q, kv_pool, block_tables, context_lens, max_context_len, scale=None,
-              partition_size=512, workspace=None, flags=0, stream=None):
-    """Paged decode: out[b] = attention of q[b] ([B, Hq, D]) over its first context_lens[b] tokens.
+def pa_kv_append_fp8(kv_pool, key, value, slot_mapping, k_scale=1.0, v_scale=1.0, stream=None):
+    """pa_kv_append into an FP8 (E4M3) pool held as a uint8 tensor: each element is stored
+    as the E4M3 code of x / scale (per-tensor k_scale, v_scale)."""
+    st = load().pa_kv_append_fp8(*_append_args(kv_pool, key, value, slot_mapping, torch.uint8),
+                                 float(k_scale), float(v_scale), _stream(stream))
+    _check("pa_kv_append_fp8", st)
 
-    ``max_context_len`` is a host upper bound of context_lens. ``workspace`` is a device
-    uint8 tensor of at least :func:`pa_decode_workspace_bytes` bytes; one is allocated
-    here when it is None. ``flags``: 0 or ``PA_DECODE_KV_STREAM`` (no block is shared
-    between the sequences of the call; K/V loads bypass cache retention).
-    """
+
+def _decode_args(out, q, kv_pool, block_tables, context_lens, max_context_len, scale,
+                 partition_size, workspace, pool_dtype):
     nb, bs, hkv, d = _pool_geometry(kv_pool)
     B, hq, dq = q.shape
     if dq != d or tuple(out.shape) != (B, hq, d):
@@ -228,13 +239,37 @@ def pa_decode(out, q, kv_pool, block_tables, context_lens, max_context_len, scal
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
     ws_p, ws_n = (0, 0) if workspace is None else (_dense(workspace, "workspace", torch.uint8),
                                                     workspace.numel())
-    st = load().pa_decode(
-        _dense(out, "out", torch.float16), _dense(q, "q", torch.float16),
-        _dense(kv_pool, "kv_pool", torch.float16), _dense(block_tables, "block_tables", torch.int32),
-        _dense(context_lens, "context_lens", torch.int32), B, hq, hkv, d, bs,
-        int(block_tables.shape[1]), nb, int(max_context_len), float(scale), int(partition_size),
-        ws_p, ws_n, int(flags), _stream(stream))
+    head = (_dense(out, "out", torch.float16), _dense(q, "q", torch.float16),
+            _dense(kv_pool, "kv_pool", pool_dtype), _dense(block_tables, "block_tables", torch.int32),
+            _dense(context_lens, "context_lens", torch.int32), B, hq, hkv, d, bs,
+            int(block_tables.shape[1]), nb, int(max_context_len), float(scale))
+    return head, (int(partition_size), ws_p, ws_n), workspace
+
+
+def pa_decode(out, q, kv_pool, block_tables, context_lens, max_context_len, scale=None,
+              partition_size=512, workspace=None, flags=0, stream=None):
+    """Paged decode: out[b] = attention of q[b] ([B, Hq, D]) over its first context_lens[b] tokens.
+
+    ``max_context_len`` is a host upper bound of context_lens. ``workspace`` is a device
+    uint8 tensor of at least :func:`pa_decode_workspace_bytes` bytes; one is allocated
+    here when it is None. ``flags``: 0 or ``PA_DECODE_KV_STREAM`` (no block is shared
+    between the sequences of the call; K/V loads bypass cache retention).
+    """
+    head, tail, ws = _decode_args(out, q, kv_pool, block_tables, context_lens, max_context_len,
+                                  scale, partition_size, workspace, torch.float16)
+    st = load().pa_decode(*head, *tail, int(flags), _stream(stream))
     _check("pa_decode", st)
+
+
+def pa_decode_fp8(out, q, kv_pool, block_tables, context_lens, max_context_len, scale=None,
+                  k_scale=1.0, v_scale=1.0, partition_size=512, workspace=None, flags=0,
+                  stream=None):
+    """pa_decode over an FP8 (E4M3) pool held as a uint8 tensor, with its per-tensor scales."""
+    head, tail, ws = _decode_args(out, q, kv_pool, block_tables, context_lens, max_context_len,
+                                  scale, partition_size, workspace, torch.uint8)
+    st = load().pa_decode_fp8(*head, float(k_scale), float(v_scale), *tail, int(flags),
+                              _stream(stream))
+    _check("pa_decode_fp8", st)
 
 
 def pa_prefill_chunk(out, q, kv_pool, block_tables, query_start_loc, seq_lens, max_q_len,

@@ -133,13 +133,17 @@ PA_EXPORT int64_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_head
 // device operations
 // ---------------------------------------------------------------------------------------
 
-PA_EXPORT pa_status pa_kv_append(void* kv_pool, const void* key, const void* value,
-                                 const int64_t* slot_mapping, int32_t num_tokens,
-                                 int32_t num_kv_heads, int32_t head_size, int32_t block_size,
-                                 int64_t num_blocks, int64_t key_token_stride,
-                                 int64_t value_token_stride, void* stream) {
+namespace {
+
+pa_status kv_append_impl(void* kv_pool, const void* key, const void* value,
+                         const int64_t* slot_mapping, int32_t num_tokens, int32_t num_kv_heads,
+                         int32_t head_size, int32_t block_size, int64_t num_blocks,
+                         int64_t key_token_stride, int64_t value_token_stride, bool fp8,
+                         float k_scale, float v_scale, void* stream) {
   if (num_tokens < 0 || num_blocks <= 0) return PA_ERR_INVALID;
   if (pa_status s = check_geometry(block_size, num_kv_heads, head_size)) return s;
+  if (fp8 && !(std::isfinite(k_scale) && k_scale > 0.0f && std::isfinite(v_scale) && v_scale > 0.0f))
+    return PA_ERR_INVALID;
   if (num_tokens == 0) return PA_OK;
   if (!kv_pool || !key || !value || !slot_mapping) return PA_ERR_INVALID;
   const int64_t row = (int64_t)num_kv_heads * head_size;
@@ -149,18 +153,49 @@ PA_EXPORT pa_status pa_kv_append(void* kv_pool, const void* key, const void* val
   if (key_token_stride % 8 || value_token_stride % 8) return PA_ERR_INVALID;  // 16-byte rows
   if (!aligned16(kv_pool) || !aligned16(key) || !aligned16(value)) return PA_ERR_INVALID;
   if (row > INT32_MAX / 2) return PA_ERR_INVALID;
+  if (fp8)
+    return hip_status(pkv::launch_kv_append_fp8(
+        kv_pool, key, value, slot_mapping, num_tokens, (int)row, num_blocks * block_size,
+        key_token_stride, value_token_stride, 1.0f / k_scale, 1.0f / v_scale, (hipStream_t)stream));
   return hip_status(pkv::launch_kv_append(kv_pool, key, value, slot_mapping, num_tokens, (int)row,
                                           num_blocks * block_size, key_token_stride,
                                           value_token_stride, (hipStream_t)stream));
 }
 
-PA_EXPORT pa_status pa_decode(void* out, const void* q, const void* kv_pool,
-                              const int32_t* block_tables, const int32_t* context_lens,
-                              int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
-                              int32_t head_size, int32_t block_size, int32_t max_blocks_per_seq,
-                              int64_t num_blocks, int32_t max_context_len, float scale,
-                              int32_t partition_size, void* workspace, int64_t workspace_bytes,
-                              uint32_t flags, void* stream) {
+}  // namespace
+
+PA_EXPORT pa_status pa_kv_append(void* kv_pool, const void* key, const void* value,
+                                 const int64_t* slot_mapping, int32_t num_tokens,
+                                 int32_t num_kv_heads, int32_t head_size, int32_t block_size,
+                                 int64_t num_blocks, int64_t key_token_stride,
+                                 int64_t value_token_stride, void* stream) {
+  return kv_append_impl(kv_pool, key, value, slot_mapping, num_tokens, num_kv_heads, head_size,
+                        block_size, num_blocks, key_token_stride, value_token_stride, false, 1.0f,
+                        1.0f, stream);
+}
+
+PA_EXPORT pa_status pa_kv_append_fp8(void* kv_pool, const void* key, const void* value,
+                                     const int64_t* slot_mapping, int32_t num_tokens,
+                                     int32_t num_kv_heads, int32_t head_size, int32_t block_size,
+                                     int64_t num_blocks, int64_t key_token_stride,
+                                     int64_t value_token_stride, float k_scale, float v_scale,
+                                     void* stream) {
+  return kv_append_impl(kv_pool, key, value, slot_mapping, num_tokens, num_kv_heads, head_size,
+                        block_size, num_blocks, key_token_stride, value_token_stride, true,
+                        k_scale, v_scale, stream);
+}
+
+namespace {
+
+pa_status decode_impl(void* out, const void* q, const void* kv_pool, const int32_t* block_tables,
+                      const int32_t* context_lens, int32_t num_seqs, int32_t num_q_heads,
+                      int32_t num_kv_heads, int32_t head_size, int32_t block_size,
+                      int32_t max_blocks_per_seq, int64_t num_blocks, int32_t max_context_len,
+                      float scale, int32_t partition_size, void* workspace,
+                      int64_t workspace_bytes, uint32_t flags, bool fp8, float k_scale,
+                      float v_scale, void* stream) {
+  if (fp8 && !(std::isfinite(k_scale) && k_scale > 0.0f && std::isfinite(v_scale) && v_scale > 0.0f))
+    return PA_ERR_INVALID;
   if (num_seqs < 0 || max_blocks_per_seq <= 0 || num_blocks <= 0 || max_context_len < 0)
     return PA_ERR_INVALID;
   if (pa_status s = check_geometry(block_size, num_kv_heads, head_size)) return s;
@@ -192,7 +227,9 @@ PA_EXPORT pa_status pa_decode(void* out, const void* q, const void* kv_pool,
   a.partition_blocks = partition_size / block_size;
   a.num_partitions = pa_num_partitions(max_context_len, partition_size);
   if (a.num_partitions > 65535) return PA_ERR_UNSUPPORTED;
-  a.scale_log2 = (float)((double)scale * kLog2e);
+  a.scale_log2 = (float)((double)scale * kLog2e * (double)k_scale);
+  a.v_scale = v_scale;
+  a.kv_fp8 = fp8;
   a.stream_kv = (flags & PA_DECODE_KV_STREAM) != 0;
   if (a.num_partitions > 1) {
     const int64_t need = pa_decode_workspace_bytes(num_seqs, num_q_heads, max_context_len,
@@ -205,6 +242,35 @@ PA_EXPORT pa_status pa_decode(void* out, const void* q, const void* kv_pool,
     a.ws_ml = reinterpret_cast<float*>(static_cast<char*>(workspace) + o_bytes);
   }
   return hip_status(pkv::launch_decode(a, (hipStream_t)stream));
+}
+
+}  // namespace
+
+PA_EXPORT pa_status pa_decode(void* out, const void* q, const void* kv_pool,
+                              const int32_t* block_tables, const int32_t* context_lens,
+                              int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                              int32_t head_size, int32_t block_size, int32_t max_blocks_per_seq,
+                              int64_t num_blocks, int32_t max_context_len, float scale,
+                              int32_t partition_size, void* workspace, int64_t workspace_bytes,
+                              uint32_t flags, void* stream) {
+  return decode_impl(out, q, kv_pool, block_tables, context_lens, num_seqs, num_q_heads,
+                     num_kv_heads, head_size, block_size, max_blocks_per_seq, num_blocks,
+                     max_context_len, scale, partition_size, workspace, workspace_bytes, flags,
+                     false, 1.0f, 1.0f, stream);
+}
+
+PA_EXPORT pa_status pa_decode_fp8(void* out, const void* q, const void* kv_pool,
+                                  const int32_t* block_tables, const int32_t* context_lens,
+                                  int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                                  int32_t head_size, int32_t block_size,
+                                  int32_t max_blocks_per_seq, int64_t num_blocks,
+                                  int32_t max_context_len, float scale, float k_scale,
+                                  float v_scale, int32_t partition_size, void* workspace,
+                                  int64_t workspace_bytes, uint32_t flags, void* stream) {
+  return decode_impl(out, q, kv_pool, block_tables, context_lens, num_seqs, num_q_heads,
+                     num_kv_heads, head_size, block_size, max_blocks_per_seq, num_blocks,
+                     max_context_len, scale, partition_size, workspace, workspace_bytes, flags,
+                     true, k_scale, v_scale, stream);
 }
 
 PA_EXPORT pa_status pa_prefill_chunk(void* out, const void* q, const void* kv_pool,

@@ -20,6 +20,11 @@
 // accumulator over the tokens it sees (online softmax); the rows are merged once at the
 // end of the partition. Scores use exp2 with the scale pre-multiplied by log2(e).
 //
+// FP8 cache. With an E4M3 pool (one byte per element) each lane loads 8 codes instead of
+// 8 fp16 values and widens them exactly to fp16 (v_cvt_scalef32_pk_f16_fp8); the key
+// scale is folded into the softmax scale and the value scale into the final 1 / l, so the
+// arithmetic after the load is the fp16 cache's.
+//
 // Output. A sequence with one partition writes its fp16 row directly. Otherwise every
 // partition writes (m, l, o = acc / l) to the workspace and the reduce kernel merges
 // them: M = max m_p, w_p = l_p * 2^(m_p - M), out = sum w_p o_p / sum w_p.
@@ -82,7 +87,7 @@ __device__ __forceinline__ void write_const_rows(const DecodeArgs& a, int b, int
   }
 }
 
-template <int D, int G, bool Stream>
+template <int D, int G, bool Stream, typename KV>
 __global__ __launch_bounds__(kThreads) void decode_partition_kernel(const DecodeArgs a) {
   using Gm = Geo<D>;
   constexpr int LPT = Gm::kLanesPerToken;
@@ -123,7 +128,7 @@ __global__ __launch_bounds__(kThreads) void decode_partition_kernel(const Decode
   const int64_t block_elems = (int64_t)kBlockSize * tok_stride;
   // element offset of this lane's piece of load i inside a block: + i * TPL * tok_stride
   const int lane_off = row * tok_stride + kvh * D + col * 8;
-  const half_t* pool = static_cast<const half_t*>(a.pool);
+  const KV* pool = static_cast<const KV*>(a.pool);
   const int32_t* bt = a.block_tables + (int64_t)b * a.max_blocks_per_seq;
 
   float m[G], l[G], acc[G][8];
@@ -143,11 +148,11 @@ __global__ __launch_bounds__(kThreads) void decode_partition_kernel(const Decode
   {
     const int phys = __builtin_amdgcn_readfirstlane(bt_vec);
     bad_table = phys < 0 || phys >= a.num_blocks;
-    const half_t* base = pool + (bad_table ? 0 : (int64_t)phys * block_elems) + lane_off;
+    const KV* base = pool + (bad_table ? 0 : (int64_t)phys * block_elems) + lane_off;
 #pragma unroll
     for (int i = 0; i < LPB; ++i) {
-      kc[i] = load16<Stream>(base + i * TPL * tok_stride);
-      vc[i] = load16<Stream>(base + i * TPL * tok_stride + kv_row);
+      kc[i] = load_kv8<KV, Stream>(base + i * TPL * tok_stride);
+      vc[i] = load_kv8<KV, Stream>(base + i * TPL * tok_stride + kv_row);
     }
   }
 
@@ -160,11 +165,11 @@ __global__ __launch_bounds__(kThreads) void decode_partition_kernel(const Decode
       if (k64 == 0) bt_vec = (lane < blk_end - jn) ? bt[jn + lane] : 0;
       const int phys = __builtin_amdgcn_readlane(bt_vec, k64);
       bad_table = phys < 0 || phys >= a.num_blocks;
-      const half_t* base = pool + (bad_table ? 0 : (int64_t)phys * block_elems) + lane_off;
+      const KV* base = pool + (bad_table ? 0 : (int64_t)phys * block_elems) + lane_off;
 #pragma unroll
       for (int i = 0; i < LPB; ++i) {
-        kn[i] = load16<Stream>(base + i * TPL * tok_stride);
-        vn[i] = load16<Stream>(base + i * TPL * tok_stride + kv_row);
+        kn[i] = load_kv8<KV, Stream>(base + i * TPL * tok_stride);
+        vn[i] = load_kv8<KV, Stream>(base + i * TPL * tok_stride + kv_row);
       }
     }
 
@@ -257,7 +262,7 @@ __global__ __launch_bounds__(kThreads) void decode_partition_kernel(const Decode
     if (row == 0) {
       const int64_t h = (int64_t)kvh * G + g;
       const int64_t bh = (int64_t)b * a.num_q_heads + h;
-      const float inv = 1.0f / lt;
+      const float inv = a.v_scale / lt;
       if (nparts == 1) {
         half8_t o;
 #pragma unroll
@@ -304,7 +309,7 @@ struct GqaGeo {
   static constexpr int VPITCH = D + 16;      // LDS row pitch (halves): 8 rows fill 64 banks
 };
 
-template <int D, int G, bool Stream>
+template <int D, int G, bool Stream, typename KV>
 __global__ __launch_bounds__(kThreads) void decode_gqa_kernel(const DecodeArgs a) {
   static_assert(G >= 1 && G <= 16, "query heads per KV head must fit 16 columns");
   using Gm = GqaGeo<D>;
@@ -355,7 +360,7 @@ __global__ __launch_bounds__(kThreads) void decode_gqa_kernel(const DecodeArgs a
   const int kv_row = a.num_kv_heads * D;
   const int tok_stride = 2 * kv_row;
   const int64_t block_elems = (int64_t)kBlockSize * tok_stride;
-  const half_t* pool = static_cast<const half_t*>(a.pool);
+  const KV* pool = static_cast<const KV*>(a.pool);
   const int32_t* bt = a.block_tables + (int64_t)b * a.max_blocks_per_seq;
   // per-lane element offsets inside a block
   const int koff = n * tok_stride + kvh * D + 8 * q4;  // + 32 ks
@@ -381,11 +386,11 @@ __global__ __launch_bounds__(kThreads) void decode_gqa_kernel(const DecodeArgs a
   {
     const int phys = __builtin_amdgcn_readfirstlane(bt_vec);
     bad_table = phys < 0 || phys >= a.num_blocks;
-    const half_t* base = pool + (bad_table ? 0 : (int64_t)phys * block_elems);
+    const KV* base = pool + (bad_table ? 0 : (int64_t)phys * block_elems);
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) kc[ks] = load16<Stream>(base + koff + 32 * ks);
+    for (int ks = 0; ks < KS; ++ks) kc[ks] = load_kv8<KV, Stream>(base + koff + 32 * ks);
 #pragma unroll
-    for (int j = 0; j < VLOADS; ++j) vc[j] = load16<Stream>(base + voff[j]);
+    for (int j = 0; j < VLOADS; ++j) vc[j] = load_kv8<KV, Stream>(base + voff[j]);
   }
 
   for (int jb = blk_begin; jb < blk_end && !bad_table; ++jb) {
@@ -396,11 +401,11 @@ __global__ __launch_bounds__(kThreads) void decode_gqa_kernel(const DecodeArgs a
       if (k64 == 0) bt_vec = (lane < blk_end - jn) ? bt[jn + lane] : 0;
       const int phys = __builtin_amdgcn_readlane(bt_vec, k64);
       bad_table = phys < 0 || phys >= a.num_blocks;
-      const half_t* base = pool + (bad_table ? 0 : (int64_t)phys * block_elems);
+      const KV* base = pool + (bad_table ? 0 : (int64_t)phys * block_elems);
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) kn[ks] = load16<Stream>(base + koff + 32 * ks);
+      for (int ks = 0; ks < KS; ++ks) kn[ks] = load_kv8<KV, Stream>(base + koff + 32 * ks);
 #pragma unroll
-      for (int j = 0; j < VLOADS; ++j) vn[j] = load16<Stream>(base + voff[j]);
+      for (int j = 0; j < VLOADS; ++j) vn[j] = load_kv8<KV, Stream>(base + voff[j]);
     }
     const int tok0 = jb * kBlockSize;
     const bool tail = tok0 + kBlockSize > L;
@@ -481,7 +486,7 @@ __global__ __launch_bounds__(kThreads) void decode_gqa_kernel(const DecodeArgs a
     }
     return;
   }
-  const float inv = 1.0f / l;
+  const float inv = a.v_scale / l;
   if (nparts == 1) {
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) {
@@ -538,7 +543,7 @@ __global__ __launch_bounds__(kThreads) void decode_reduce_kernel(const DecodeArg
   for (int k = 0; k < PER_LANE; ++k) out[k] = (half_t)(acc[k] * inv);
 }
 
-template <int D, int G>
+template <int D, int G, typename KV>
 hipError_t launch_decode_dg(const DecodeArgs& a, hipStream_t stream) {
   const int64_t groups = (a.num_kv_heads + kWavesPerGroup - 1) / kWavesPerGroup;
   const int64_t quads = (int64_t)((a.num_seqs + kSeqQuad - 1) / kSeqQuad) * a.num_partitions * groups;
@@ -547,14 +552,14 @@ hipError_t launch_decode_dg(const DecodeArgs& a, hipStream_t stream) {
   const dim3 grid((unsigned)wgs);
   if constexpr (G == 1) {  // one query head per KV head: vector ALUs
     if (a.stream_kv)
-      hipLaunchKernelGGL((decode_partition_kernel<D, 1, true>), grid, dim3(kThreads), 0, stream, a);
+      hipLaunchKernelGGL((decode_partition_kernel<D, 1, true, KV>), grid, dim3(kThreads), 0, stream, a);
     else
-      hipLaunchKernelGGL((decode_partition_kernel<D, 1, false>), grid, dim3(kThreads), 0, stream, a);
+      hipLaunchKernelGGL((decode_partition_kernel<D, 1, false, KV>), grid, dim3(kThreads), 0, stream, a);
   } else {  // a query-head group per KV head: matrix cores
     if (a.stream_kv)
-      hipLaunchKernelGGL((decode_gqa_kernel<D, G, true>), grid, dim3(kThreads), 0, stream, a);
+      hipLaunchKernelGGL((decode_gqa_kernel<D, G, true, KV>), grid, dim3(kThreads), 0, stream, a);
     else
-      hipLaunchKernelGGL((decode_gqa_kernel<D, G, false>), grid, dim3(kThreads), 0, stream, a);
+      hipLaunchKernelGGL((decode_gqa_kernel<D, G, false, KV>), grid, dim3(kThreads), 0, stream, a);
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.num_partitions == 1) return e;
@@ -563,13 +568,13 @@ hipError_t launch_decode_dg(const DecodeArgs& a, hipStream_t stream) {
   return hipGetLastError();
 }
 
-template <int D>
+template <int D, typename KV>
 hipError_t launch_decode_d(const DecodeArgs& a, hipStream_t stream) {
   switch (a.num_q_heads / a.num_kv_heads) {
-    case 1: return launch_decode_dg<D, 1>(a, stream);
-    case 2: return launch_decode_dg<D, 2>(a, stream);
-    case 4: return launch_decode_dg<D, 4>(a, stream);
-    case 8: return launch_decode_dg<D, 8>(a, stream);
+    case 1: return launch_decode_dg<D, 1, KV>(a, stream);
+    case 2: return launch_decode_dg<D, 2, KV>(a, stream);
+    case 4: return launch_decode_dg<D, 4, KV>(a, stream);
+    case 8: return launch_decode_dg<D, 8, KV>(a, stream);
     default: return hipErrorInvalidValue;
   }
 }
@@ -578,8 +583,13 @@ hipError_t launch_decode_d(const DecodeArgs& a, hipStream_t stream) {
 
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream) {
   if (a.num_seqs == 0) return hipSuccess;
-  if (a.head_size == 128) return launch_decode_d<128>(a, stream);
-  if (a.head_size == 64) return launch_decode_d<64>(a, stream);
+  if (a.kv_fp8) {
+    if (a.head_size == 128) return launch_decode_d<128, fp8_t>(a, stream);
+    if (a.head_size == 64) return launch_decode_d<64, fp8_t>(a, stream);
+  } else {
+    if (a.head_size == 128) return launch_decode_d<128, half_t>(a, stream);
+    if (a.head_size == 64) return launch_decode_d<64, half_t>(a, stream);
+  }
   return hipErrorInvalidValue;
 }
 

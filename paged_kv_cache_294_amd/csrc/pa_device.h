@@ -65,6 +65,50 @@ __device__ __forceinline__ half8_t load16(const half_t* p) {
     return *gp;
 }
 
+// FP8 (OCP E4M3) cache elements are stored as bytes.
+typedef uint8_t fp8_t;
+typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(1))) const u32x2_t gconst_u32x2_t;
+
+// Eight consecutive cache elements as fp16: a 16-byte load of fp16 elements, or an 8-byte
+// load of E4M3 codes widened exactly to fp16 (every E4M3 value is an fp16 value;
+// v_cvt_scalef32_pk_f16_fp8 with scale 1 converts two codes).
+template <typename KV, bool Stream = false>
+__device__ __forceinline__ half8_t load_kv8(const KV* p) {
+  if constexpr (sizeof(KV) == 2) {
+    return load16<Stream>(reinterpret_cast<const half_t*>(p));
+  } else {
+    gconst_u32x2_t* gp = (gconst_u32x2_t*)(p);
+    u32x2_t w;
+    if constexpr (Stream)
+      w = __builtin_nontemporal_load(gp);
+    else
+      w = *gp;
+    const half2_t a = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w[0], 1.0f, false);
+    const half2_t b = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w[0], 1.0f, true);
+    const half2_t c = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w[1], 1.0f, false);
+    const half2_t d = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w[1], 1.0f, true);
+    return half8_t{a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
+  }
+}
+
+// E4M3 code of a NaN: the NaN pattern with the input's sign.
+__device__ __forceinline__ unsigned int fp8_nan(float x) {
+  return 0x7Fu | ((__builtin_bit_cast(unsigned int, x) >> 24) & 0x80u);
+}
+
+// Two fp32 values as E4M3 codes in the low 16 bits, round to nearest even. The hardware
+// conversion turns magnitudes past the 448 / 480 midpoint into NaN, so values are first
+// clamped to +-448 (saturation); it also gives every NaN the negative NaN code, so NaN
+// inputs get their sign back.
+__device__ __forceinline__ unsigned int fp8x2(float x, float y) {
+  const unsigned int c = (unsigned int)__builtin_amdgcn_cvt_pk_fp8_f32(
+      fminf(fmaxf(x, -448.0f), 448.0f), fminf(fmaxf(y, -448.0f), 448.0f), 0, false);
+  const unsigned int lo = (x != x) ? fp8_nan(x) : (c & 0xFFu);
+  const unsigned int hi = (y != y) ? fp8_nan(y) : ((c >> 8) & 0xFFu);
+  return lo | (hi << 8);
+}
+
 __device__ __forceinline__ float dot8(half8_t a, half8_t b, float acc) {
   acc = __builtin_amdgcn_fdot2(half2_t{a[0], a[1]}, half2_t{b[0], b[1]}, acc, false);
   acc = __builtin_amdgcn_fdot2(half2_t{a[2], a[3]}, half2_t{b[2], b[3]}, acc, false);

@@ -10,6 +10,10 @@ namespace pkv {
 hipError_t launch_kv_append(void* pool, const void* key, const void* value, const int64_t* slots,
                             int num_tokens, int kv_row_elems, int64_t num_slots,
                             int64_t key_stride, int64_t value_stride, hipStream_t stream);
+hipError_t launch_kv_append_fp8(void* pool, const void* key, const void* value,
+                                const int64_t* slots, int num_tokens, int kv_row_elems,
+                                int64_t num_slots, int64_t key_stride, int64_t value_stride,
+                                float k_inv, float v_inv, hipStream_t stream);
 
 struct DecodeArgs {
   void* out;
@@ -25,8 +29,10 @@ struct DecodeArgs {
   int max_context_len;
   int partition_blocks;  // partition size in blocks
   int num_partitions;    // partitions the grid covers
-  float scale_log2;      // softmax scale * log2(e)
+  float scale_log2;      // softmax scale * log2(e), times the key scale of an FP8 cache
+  float v_scale;         // value scale of an FP8 cache (1 for fp16)
   bool stream_kv;        // K/V loads carry the non-temporal hint (blocks read once per step)
+  bool kv_fp8;           // the pool holds E4M3 codes (1 byte per element) instead of fp16
 };
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
 

@@ -196,3 +196,16 @@ def test_block_copies_reject_before_any_launch(lib):
     assert lib.pa_move_blocks(0, FAKE, FAKE, 1, 256, 4, 4, None) == pkv.PA_ERR_INVALID
     assert lib.pa_move_blocks(FAKE + 8, FAKE, FAKE, 1, 256, 4, 4, None) == pkv.PA_ERR_INVALID
     assert lib.pa_move_blocks(FAKE, FAKE, FAKE, 0, 256, 4, 4, None) == pkv.PA_OK
+
+
+def test_fp8_calls_reject_bad_scales(lib):
+    assert lib.pa_kv_append_fp8(FAKE, FAKE, FAKE, FAKE, 1, 4, 64, 16, 16, 0, 0, 0.0, 1.0,
+                                None) == pkv.PA_ERR_INVALID
+    assert lib.pa_kv_append_fp8(FAKE, FAKE, FAKE, FAKE, 1, 4, 64, 16, 16, 0, 0, 1.0,
+                                float("inf"), None) == pkv.PA_ERR_INVALID
+    assert lib.pa_decode_fp8(FAKE, FAKE, FAKE, FAKE, FAKE, 1, 4, 4, 64, 16, 4, 16, 64, 0.125, 1.0,
+                             float("nan"), 512, 0, 0, 0, None) == pkv.PA_ERR_INVALID
+    assert lib.pa_decode_fp8(FAKE, FAKE, FAKE, FAKE, FAKE, 1, 4, 4, 64, 32, 4, 16, 64, 0.125, 1.0,
+                             1.0, 512, 0, 0, 0, None) == pkv.PA_ERR_UNSUPPORTED
+    assert lib.pa_decode_fp8(FAKE, FAKE, FAKE, FAKE, FAKE, 0, 4, 4, 64, 16, 4, 16, 64, 0.125, 1.0,
+                             1.0, 512, 0, 0, 0, None) == pkv.PA_OK
