@@ -422,7 +422,9 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", choices=sorted(WORKLOADS), default="c2")
-    ap.add_argument("--partition-size", type=int, default=256)
+    ap.add_argument("--partition-size", type=int, default=0,
+                    help="decode partition in tokens; 0 (default): 512 when the longest "
+                         "context exceeds 8192 tokens, else 256")
     ap.add_argument("--kv-stream", choices=("auto", "on", "off"), default="auto",
                     help="non-temporal K/V loads in decode; auto: on unless blocks are shared")
     ap.add_argument("--launch", choices=("graph", "eager"), default="graph",
@@ -472,7 +474,12 @@ def main():
         print("--kv-dtype fp8 runs decode-only workloads (c1-c4): pa_prefill_chunk reads fp16 "
               "caches only", file=sys.stderr)
         sys.exit(2)
-    kv_bytes = kv_read_bytes(inp, elem_bytes)
+    if args.partition_size <= 0:
+        args.partition_size = 512 if int(inp.seq_lens.max()) > 8192 else 256
+    # algorithmic bytes: every decode context token's K and V once; with shared prefix
+    # blocks, every physical block's filled slots once (the logical count is reported too)
+    logical_bytes = kv_read_bytes(inp, elem_bytes)
+    kv_bytes = kv_unique_bytes(inp, elem_bytes) if shared else logical_bytes
 
     if args.mode == "counters":
         run_counter_sequence(inp, args.partition_size, kv_stream)
@@ -573,9 +580,8 @@ def main():
         kernels["prefill"] = {"us": prefill_ms * 1e3, "gflop": fl / 1e9, "TFLOPs": tf,
                               "frac_mfma_peak": tf / MFMA_F16_PEAK_TFLOPS}
     if shared:
-        ub = kv_unique_bytes(inp, elem_bytes)
-        kernels["decode"]["unique_kv_bytes"] = ub
-        kernels["decode"]["unique_kv_GBps"] = ub / (decode_ms * 1e-3) / 1e9
+        kernels["decode"]["logical_kv_bytes"] = logical_bytes
+        kernels["decode"]["logical_kv_GBps"] = logical_bytes / (decode_ms * 1e-3) / 1e9
     result = {
         "metric": "paged-attn decode KV-read GB/s (% of HBM peak) + seq-steps/s, 1 GPU",
         "value": kv_bytes / (ms_step * 1e-3) / 1e9,
