@@ -9,6 +9,7 @@ into their pool slots, ``pa_prefill_chunk`` for prefill chunks (mixed workload o
   c2 (default)  256 decode sequences, context U{128..2048}, 32 heads x 128, + append
   c3            8 sequences x 32768 tokens, 32 x 128 (64 partitions of 512)
   c4            64 prompt groups x 4 samples sharing 64 blocks, 32q / 8kv heads x 128
+  c4p           c4 with private copies of the shared blocks (grouped-query decode from HBM)
   c5            8 prefill chunks of 512 over priors U{0..3584} + 248 decodes U{256..4096},
                 append of all 4344 new tokens
 
@@ -52,6 +53,8 @@ WORKLOADS = {
               "fp16, split-context partitions"),
     "c4": (4, "prefix-shared GQA decode: 64 groups x 4 samples, 1024-token shared prompt "
               "(64 blocks) + 64..256 private tokens, 32 q / 8 kv heads x 128, fp16"),
+    "c4p": (4, "config 4 with private copies of every shared prefix block (no sharing): "
+               "256 GQA sequences of 1088..1280 tokens, 32 q / 8 kv heads x 128, fp16"),
     "c5": (5, "mixed step: kv_append of 4344 tokens + 8 prefill chunks of 512 over priors "
               "U{0..3584} + 248 decodes U{256..4096}, 32 heads x 128, fp16"),
 }
@@ -290,7 +293,8 @@ def block_copy_leg(torch, pkv, num_kv_heads, head_size, reps=10):
 class Step:
     """Device copies of a batch and one step of the hot path over them."""
 
-    def __init__(self, torch, pkv, inp, partition_size, kv_stream, kv_fp8=False):
+    def __init__(self, torch, pkv, inp, partition_size, kv_stream, kv_fp8=False,
+                 shared_prefix=False):
         self.torch, self.pkv, self.inp = torch, pkv, inp
 
         def c(a):
@@ -310,6 +314,18 @@ class Step:
         self.flags = pkv.PA_DECODE_KV_STREAM if kv_stream else 0
         ws = pkv.pa_decode_workspace_bytes(len(lensd), inp.num_q_heads, self.mcl, partition_size,
                                            inp.head_size)
+        self.shared_prefix = shared_prefix
+        if shared_prefix:  # the generator's groups: consecutive sequences sharing prefix blocks
+            g = inp.groups[inp.num_prefill:]
+            starts = np.flatnonzero(np.r_[True, g[1:] != g[:-1]])
+            gs = np.r_[starts, len(g)].astype(np.int32)
+            self.gs = c(gs)
+            self.pl = c(np.full(len(starts), inp.prefix_blocks * inp.block_size, np.int32))
+            self.max_group = int(np.diff(gs).max())
+            self.max_prefix = inp.prefix_blocks * inp.block_size
+            ws = pkv.pa_decode_shared_prefix_workspace_bytes(len(lensd), inp.num_q_heads, self.mcl,
+                                                             self.max_prefix, partition_size,
+                                                             inp.head_size)
         self.ws = torch.empty(max(ws, 256), dtype=torch.uint8, device="cuda")
         self.has_prefill = inp.num_prefill > 0
         if self.has_prefill:
@@ -337,7 +353,11 @@ class Step:
             pkv.pa_prefill_chunk(self.pout, self.pq, self.pool, self.pbt, self.qsl, self.plens,
                                  self.max_q, self.max_s, self.inp.scale, stream=stream)
         rec(2)
-        if self.kv_fp8:
+        if self.shared_prefix:
+            pkv.pa_decode_shared_prefix(self.dout, self.dq, self.pool, self.dbt, self.dlens, self.mcl,
+                                        self.gs, self.pl, self.max_group, self.max_prefix,
+                                        self.inp.scale, self.ps, self.ws, stream=stream)
+        elif self.kv_fp8:
             pkv.pa_decode_fp8(self.dout, self.dq, self.pool, self.dbt, self.dlens, self.mcl,
                               self.inp.scale, 1.0, 1.0, self.ps, self.ws, self.flags, stream=stream)
         else:
@@ -434,6 +454,10 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-stream-read", action="store_true")
     ap.add_argument("--no-block-copies", action="store_true")
+    ap.add_argument("--decode", choices=("auto", "plain", "shared-prefix"), default="auto",
+                    help="shared-prefix: pa_decode_shared_prefix over the workload's prompt "
+                         "groups (reads each shared prefix once); auto: that when the workload "
+                         "has prompt groups and an fp16 cache, else plain")
     ap.add_argument("--kv-dtype", choices=("fp16", "fp8"), default="fp16",
                     help="cache element: fp16, or FP8 E4M3 codes (decode-only workloads; the "
                          "prefill kernel reads fp16 caches only)")
@@ -464,6 +488,8 @@ def main():
     log(f"generating workload {args.workload} (seed {seed})")
     t0 = time.perf_counter()
     inp = workloads.CONFIGS[seed]()
+    if args.workload == "c4p":
+        inp = workloads.unshare_prefix(inp)
     log(f"generated in {time.perf_counter() - t0:.1f}s: {inp.num_blocks} blocks, "
         f"{inp.num_seqs} sequences, sum L = {int(inp.seq_lens.sum())}")
     shared = shares_blocks(inp)
@@ -512,7 +538,12 @@ def main():
         log(f"host block manager: admit {bm['admit_us']:.0f} us, step {bm['step_us']:.0f} us "
             f"({bm['new_tokens']} slots + tables)")
     log("copying the batch to the GPU")
-    step = Step(torch, pkv, inp, args.partition_size, kv_stream, kv_fp8)
+    shared_prefix = {"plain": False, "shared-prefix": True,
+                     "auto": bool(inp.prefix_blocks) and not kv_fp8}[args.decode]
+    if shared_prefix and (kv_fp8 or not inp.prefix_blocks):
+        print("--decode shared-prefix needs prompt groups and an fp16 cache", file=sys.stderr)
+        sys.exit(2)
+    step = Step(torch, pkv, inp, args.partition_size, kv_stream, kv_fp8, shared_prefix)
     for _ in range(args.warmup):
         step.run()
     torch.cuda.synchronize()
@@ -603,13 +634,17 @@ def main():
             "sum_context_tokens": int(inp.seq_lens.sum()), "seed": seed,
             "launch": "hip graph replay" if args.launch == "graph" else "eager",
             "kv_dtype": args.kv_dtype,
+            "decode": "shared-prefix" if shared_prefix else "plain",
         },
         "eager_ms_per_step": eager_ms_step,
         "pct_of_hbm_peak": 100.0 * kv_bytes / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBPS,
         "seq_steps_per_s": inp.num_seqs / (ms_step * 1e-3),
         "roofline": {
-            "kernel": "pa_decode" + (" (partition + log-sum-exp reduce kernels)" if nparts > 1
-                                     else " (partition kernel)"),
+            "kernel": ("pa_decode_shared_prefix (prefix, own-token and log-sum-exp reduce kernels)"
+                       if shared_prefix else
+                       ("pa_decode_fp8" if kv_fp8 else "pa_decode") +
+                       (" (partition + log-sum-exp reduce kernels)" if nparts > 1
+                        else " (partition kernel)")),
             "bound": "hbm",
             "achieved": achieved,
             "peak": HBM_PEAK_GBPS,

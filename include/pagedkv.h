@@ -158,6 +158,42 @@ pa_status pa_decode(void* out, const void* q, const void* kv_pool, const int32_t
                     float scale, int32_t partition_size, void* workspace,
                     int64_t workspace_bytes, uint32_t flags, void* stream);
 
+/* ---- shared-prefix decode ------------------------------------------------------------
+ * Sequences that share a prompt point their tables at the same blocks, which avoids
+ * storing and computing the prompt twice (page "vLLM GitHub 项目 …", section 二, item 4:
+ * parallel sampling and beam search). pa_decode_shared_prefix computes exactly what
+ * pa_decode computes, reading each group's shared prefix once: the prefix is one pass per
+ * (group, KV head) whose matrix-core tile columns are the group's (sample, query head)
+ * pairs (16 / (num_q_heads / num_kv_heads) samples per tile), then every sequence's own
+ * tokens are one pass each, and a log-sum-exp reduction merges the two.
+ *
+ *   group_start     device int32 [num_groups + 1]: sequences group_start[g] ..
+ *                   group_start[g + 1] - 1 form group g (non-decreasing, 0 .. num_seqs;
+ *                   a sequence with nothing shared is a group of its own)
+ *   prefix_lens     device int32 [num_groups]: tokens every member of group g shares, a
+ *                   multiple of block_size, at most each member's context length; the
+ *                   first prefix_lens[g] / block_size entries of every member's table row
+ *                   are the same (the call reads them from the group's first member)
+ *   max_group_size  host bound on the group sizes; max_prefix_len host bound on
+ *                   prefix_lens (a multiple of block_size, at most max_context_len)
+ *   workspace       pa_decode_shared_prefix_workspace_bytes(...) bytes, 256-byte aligned
+ * Other arguments as pa_decode (fp16 pool; K/V loads keep the cache hint, since blocks are
+ * shared). A row whose group, prefix or length breaks these bounds is NaN; a length of 0
+ * gives zeros. */
+pa_status pa_decode_shared_prefix(void* out, const void* q, const void* kv_pool,
+                                  const int32_t* block_tables, const int32_t* context_lens,
+                                  int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                                  int32_t head_size, int32_t block_size,
+                                  int32_t max_blocks_per_seq, int64_t num_blocks,
+                                  int32_t max_context_len, float scale, int32_t partition_size,
+                                  const int32_t* group_start, const int32_t* prefix_lens,
+                                  int32_t num_groups, int32_t max_group_size,
+                                  int32_t max_prefix_len, void* workspace,
+                                  int64_t workspace_bytes, void* stream);
+int64_t pa_decode_shared_prefix_workspace_bytes(int32_t num_seqs, int32_t num_q_heads,
+                                                int32_t max_context_len, int32_t max_prefix_len,
+                                                int32_t partition_size, int32_t head_size);
+
 /* ---- FP8 KV cache ---------------------------------------------------------------------
  * The pool may hold OCP FP8 E4M3 codes, one byte per element, in the same layout
  * [num_blocks][block_size][2][num_kv_heads][head_size] (page "vLLM 部署深度指南": the FP8

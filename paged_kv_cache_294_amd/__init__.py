@@ -22,6 +22,8 @@ from ._lib import (  # noqa: F401
     pa_blocks_for_len,
     pa_decode,
     pa_decode_fp8,
+    pa_decode_shared_prefix,
+    pa_decode_shared_prefix_workspace_bytes,
     pa_decode_workspace_bytes,
     pa_gather_kv,
     pa_kv_append,

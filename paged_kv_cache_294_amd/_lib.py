@@ -45,6 +45,10 @@ SIGNATURES = {
     "pa_decode_fp8": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32,
                                      _i64, _i32, _f32, _f32, _f32, _i32, _vp, _i64, ctypes.c_uint32,
                                      _vp]),
+    "pa_decode_shared_prefix": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32,
+                                               _i32, _i64, _i32, _f32, _i32, _vp, _vp, _i32, _i32,
+                                               _i32, _vp, _i64, _vp]),
+    "pa_decode_shared_prefix_workspace_bytes": (_i64, [_i32, _i32, _i32, _i32, _i32, _i32]),
     "pa_prefill_chunk": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32,
                                         _i32, _i32, _i32, _i32, _i64, _f32, _vp]),
     "pa_gather_kv": (ctypes.c_int, [_vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i64, _vp]),
@@ -259,6 +263,48 @@ def pa_decode(out, q, kv_pool, block_tables, context_lens, max_context_len, scal
                                   scale, partition_size, workspace, torch.float16)
     st = load().pa_decode(*head, *tail, int(flags), _stream(stream))
     _check("pa_decode", st)
+
+
+def pa_decode_shared_prefix_workspace_bytes(num_seqs, num_q_heads, max_context_len,
+                                            max_prefix_len, partition_size, head_size) -> int:
+    return load().pa_decode_shared_prefix_workspace_bytes(num_seqs, num_q_heads, max_context_len,
+                                                          max_prefix_len, partition_size, head_size)
+
+
+def pa_decode_shared_prefix(out, q, kv_pool, block_tables, context_lens, max_context_len,
+                            group_start, prefix_lens, max_group_size, max_prefix_len,
+                            scale=None, partition_size=256, workspace=None, stream=None):
+    """pa_decode for groups of sequences sharing prefix blocks: group g is sequences
+    group_start[g] .. group_start[g+1]-1 (device int32), sharing prefix_lens[g] tokens
+    (device int32, multiples of the block size). Same result as pa_decode."""
+    nb, bs, hkv, d = _pool_geometry(kv_pool)
+    B, hq, dq = q.shape
+    if dq != d or tuple(out.shape) != (B, hq, d):
+        raise ValueError("q and out must be [num_seqs, num_q_heads, head_size]")
+    if block_tables.dim() != 2 or block_tables.shape[0] != B or tuple(context_lens.shape) != (B,):
+        raise ValueError("block_tables must be [num_seqs, max_blocks], context_lens [num_seqs]")
+    G = int(prefix_lens.shape[0])
+    if tuple(group_start.shape) != (G + 1,):
+        raise ValueError("group_start must be [num_groups + 1]")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    need = pa_decode_shared_prefix_workspace_bytes(B, hq, max_context_len, max_prefix_len,
+                                                   partition_size, d)
+    if need < 0:
+        raise ValueError("bad sizes for the shared-prefix workspace")
+    if workspace is None:
+        if _CAPTURING:
+            raise ValueError("pa_decode_shared_prefix under capture needs a caller-owned workspace")
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
+    st = load().pa_decode_shared_prefix(
+        _dense(out, "out", torch.float16), _dense(q, "q", torch.float16),
+        _dense(kv_pool, "kv_pool", torch.float16), _dense(block_tables, "block_tables", torch.int32),
+        _dense(context_lens, "context_lens", torch.int32), B, hq, hkv, d, bs,
+        int(block_tables.shape[1]), nb, int(max_context_len), float(scale), int(partition_size),
+        _dense(group_start, "group_start", torch.int32), _dense(prefix_lens, "prefix_lens", torch.int32),
+        G, int(max_group_size), int(max_prefix_len), _dense(workspace, "workspace", torch.uint8),
+        workspace.numel(), _stream(stream))
+    _check("pa_decode_shared_prefix", st)
 
 
 def pa_decode_fp8(out, q, kv_pool, block_tables, context_lens, max_context_len, scale=None,

@@ -129,6 +129,21 @@ PA_EXPORT int64_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_head
   return (bytes + 255) / 256 * 256;
 }
 
+PA_EXPORT int64_t pa_decode_shared_prefix_workspace_bytes(int32_t num_seqs, int32_t num_q_heads,
+                                                          int32_t max_context_len,
+                                                          int32_t max_prefix_len,
+                                                          int32_t partition_size,
+                                                          int32_t head_size) {
+  if (num_seqs < 0 || num_q_heads <= 0 || max_context_len < 0 || max_prefix_len < 0 ||
+      max_prefix_len > max_context_len || partition_size <= 0 || head_size <= 0)
+    return -1;
+  const int64_t parts = (int64_t)pa_num_partitions(max_context_len, partition_size) +
+                        (max_prefix_len == 0 ? 0 : pa_num_partitions(max_prefix_len, partition_size));
+  const int64_t rows = (int64_t)num_seqs * num_q_heads * parts;
+  const int64_t o_bytes = (rows * head_size * 4 + 255) / 256 * 256;
+  return (o_bytes + rows * 8 + 255) / 256 * 256;
+}
+
 // ---------------------------------------------------------------------------------------
 // device operations
 // ---------------------------------------------------------------------------------------
@@ -193,7 +208,13 @@ pa_status decode_impl(void* out, const void* q, const void* kv_pool, const int32
                       int32_t max_blocks_per_seq, int64_t num_blocks, int32_t max_context_len,
                       float scale, int32_t partition_size, void* workspace,
                       int64_t workspace_bytes, uint32_t flags, bool fp8, float k_scale,
-                      float v_scale, void* stream) {
+                      float v_scale, void* stream, const int32_t* group_start = nullptr,
+                      const int32_t* prefix_lens = nullptr, int32_t num_groups = 0,
+                      int32_t max_group_size = 0, int32_t max_prefix_len = 0) {
+  const bool cascade = group_start != nullptr;
+  if (cascade && (prefix_lens == nullptr || num_groups <= 0 || max_group_size <= 0 ||
+                  max_prefix_len < 0 || max_prefix_len % 16 || max_prefix_len > max_context_len))
+    return PA_ERR_INVALID;
   if (fp8 && !(std::isfinite(k_scale) && k_scale > 0.0f && std::isfinite(v_scale) && v_scale > 0.0f))
     return PA_ERR_INVALID;
   if (num_seqs < 0 || max_blocks_per_seq <= 0 || num_blocks <= 0 || max_context_len < 0)
@@ -227,20 +248,34 @@ pa_status decode_impl(void* out, const void* q, const void* kv_pool, const int32
   a.partition_blocks = partition_size / block_size;
   a.num_partitions = pa_num_partitions(max_context_len, partition_size);
   if (a.num_partitions > 65535) return PA_ERR_UNSUPPORTED;
+  a.ws_parts = a.num_partitions;
+  if (cascade) {
+    a.group_start = group_start;
+    a.prefix_lens = prefix_lens;
+    a.num_groups = num_groups;
+    a.group_cap = max_group_size;
+    a.prefix_parts = pa_num_partitions(max_prefix_len, partition_size);
+    if (max_prefix_len == 0) a.prefix_parts = 0;
+    a.ws_parts = a.prefix_parts + a.num_partitions;
+  }
   a.scale_log2 = (float)((double)scale * kLog2e * (double)k_scale);
   a.v_scale = v_scale;
   a.kv_fp8 = fp8;
   a.stream_kv = (flags & PA_DECODE_KV_STREAM) != 0;
-  if (a.num_partitions > 1) {
-    const int64_t need = pa_decode_workspace_bytes(num_seqs, num_q_heads, max_context_len,
-                                                   partition_size, head_size);
+  if (a.num_partitions > 1 || cascade) {
+    const int64_t need =
+        cascade ? pa_decode_shared_prefix_workspace_bytes(num_seqs, num_q_heads, max_context_len,
+                                                          max_prefix_len, partition_size, head_size)
+                : pa_decode_workspace_bytes(num_seqs, num_q_heads, max_context_len,
+                                            partition_size, head_size);
     if (!workspace || workspace_bytes < need) return PA_ERR_WORKSPACE;
     if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return PA_ERR_INVALID;
-    const int64_t rows = (int64_t)num_seqs * num_q_heads * a.num_partitions;
+    const int64_t rows = (int64_t)num_seqs * num_q_heads * a.ws_parts;
     const int64_t o_bytes = (rows * head_size * 4 + 255) / 256 * 256;
     a.ws_o = static_cast<float*>(workspace);
     a.ws_ml = reinterpret_cast<float*>(static_cast<char*>(workspace) + o_bytes);
   }
+  if (cascade) return hip_status(pkv::launch_decode_shared_prefix(a, (hipStream_t)stream));
   return hip_status(pkv::launch_decode(a, (hipStream_t)stream));
 }
 
@@ -257,6 +292,21 @@ PA_EXPORT pa_status pa_decode(void* out, const void* q, const void* kv_pool,
                      num_kv_heads, head_size, block_size, max_blocks_per_seq, num_blocks,
                      max_context_len, scale, partition_size, workspace, workspace_bytes, flags,
                      false, 1.0f, 1.0f, stream);
+}
+
+PA_EXPORT pa_status pa_decode_shared_prefix(
+    void* out, const void* q, const void* kv_pool, const int32_t* block_tables,
+    const int32_t* context_lens, int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+    int32_t head_size, int32_t block_size, int32_t max_blocks_per_seq, int64_t num_blocks,
+    int32_t max_context_len, float scale, int32_t partition_size, const int32_t* group_start,
+    const int32_t* prefix_lens, int32_t num_groups, int32_t max_group_size,
+    int32_t max_prefix_len, void* workspace, int64_t workspace_bytes, void* stream) {
+  if (group_start == nullptr && num_seqs > 0) return PA_ERR_INVALID;
+  return decode_impl(out, q, kv_pool, block_tables, context_lens, num_seqs, num_q_heads,
+                     num_kv_heads, head_size, block_size, max_blocks_per_seq, num_blocks,
+                     max_context_len, scale, partition_size, workspace, workspace_bytes, 0u,
+                     false, 1.0f, 1.0f, stream, group_start, prefix_lens, num_groups,
+                     max_group_size, max_prefix_len);
 }
 
 PA_EXPORT pa_status pa_decode_fp8(void* out, const void* q, const void* kv_pool,

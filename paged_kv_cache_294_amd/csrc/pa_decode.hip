@@ -58,18 +58,19 @@ struct DecodeItem {
   bool valid;
 };
 
-__device__ __forceinline__ DecodeItem decode_item(const DecodeArgs& a) {
+__device__ __forceinline__ DecodeItem decode_item(const DecodeArgs& a, int num_seqs, int num_parts,
+                                                  int block) {
   const int groups = (a.num_kv_heads + kWavesPerGroup - 1) / kWavesPerGroup;
-  const int64_t quads = (int64_t)((a.num_seqs + kSeqQuad - 1) / kSeqQuad) * a.num_partitions * groups;
-  const int xcd = blockIdx.x % kXcds;
-  const int slot = blockIdx.x / kXcds;
+  const int64_t quads = (int64_t)((num_seqs + kSeqQuad - 1) / kSeqQuad) * num_parts * groups;
+  const int xcd = block % kXcds;
+  const int slot = block / kXcds;
   const int64_t quad = (int64_t)(slot / kSeqQuad) * kXcds + xcd;
   DecodeItem it;
   it.hg = (int)(quad % groups);
   const int64_t rest = quad / groups;
-  it.p = (int)(rest % a.num_partitions);
-  it.b = (int)(rest / a.num_partitions) * kSeqQuad + slot % kSeqQuad;
-  it.valid = quad < quads && it.b < a.num_seqs;
+  it.p = (int)(rest % num_parts);
+  it.b = (int)(rest / num_parts) * kSeqQuad + slot % kSeqQuad;
+  it.valid = quad < quads && it.b < num_seqs;
   return it;
 }
 
@@ -95,7 +96,7 @@ __global__ __launch_bounds__(kThreads) void decode_partition_kernel(const Decode
   constexpr int LPB = Gm::kLoadsPerBlock;
 
   const int lane = threadIdx.x & (kWave - 1);
-  const DecodeItem item = decode_item(a);
+  const DecodeItem item = decode_item(a, a.num_seqs, a.num_partitions, blockIdx.x);
   if (!item.valid) return;
   const int kvh = item.hg * kWavesPerGroup + (threadIdx.x >> 6);
   const int p = item.p;
@@ -233,7 +234,7 @@ __global__ __launch_bounds__(kThreads) void decode_partition_kernel(const Decode
 #pragma unroll
         for (int g = 0; g < G; ++g) {
           const int64_t bh = (int64_t)b * a.num_q_heads + (int64_t)kvh * G + g;
-          float* wml = a.ws_ml + (bh * a.num_partitions + p) * 2;
+          float* wml = a.ws_ml + (bh * a.ws_parts + p) * 2;
           wml[0] = qnan();
           wml[1] = qnan();
         }
@@ -275,11 +276,11 @@ __global__ __launch_bounds__(kThreads) void decode_partition_kernel(const Decode
           o0[d] = acc[g][d] * inv;
           o1[d] = acc[g][d + 4] * inv;
         }
-        float* wo = a.ws_o + (bh * a.num_partitions + p) * D + col * 8;
+        float* wo = a.ws_o + (bh * a.ws_parts + p) * D + col * 8;
         *reinterpret_cast<float4_t*>(wo) = o0;
         *reinterpret_cast<float4_t*>(wo + 4) = o1;
         if (col == 0) {
-          float* wml = a.ws_ml + (bh * a.num_partitions + p) * 2;
+          float* wml = a.ws_ml + (bh * a.ws_parts + p) * 2;
           wml[0] = M;
           wml[1] = lt;
         }
@@ -309,9 +310,27 @@ struct GqaGeo {
   static constexpr int VPITCH = D + 16;      // LDS row pitch (halves): 8 rows fill 64 banks
 };
 
-template <int D, int G, bool Stream, typename KV>
+// The group of sequence b: g with group_start[g] <= b < group_start[g + 1], or -1.
+__device__ __forceinline__ int group_of(const DecodeArgs& a, int b) {
+  int lo = 0, hi = a.num_groups;
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (a.group_start[mid] <= b) lo = mid; else hi = mid;
+  }
+  return (a.group_start[lo] <= b && b < a.group_start[lo + 1]) ? lo : -1;
+}
+
+// Shared-prefix decode splits each context at its group's prefix length P: one pass over
+// the prefix per group, whose 16 tile columns are (sample, query head) pairs of the
+// group's sequences (the prefix's K/V read once for all of them), and one pass over each
+// sequence's own tokens P .. L - 1. Both write partitions to the workspace and the reduce
+// merges them. Plain decode is mode 0.
+constexpr int kModePlain = 0, kModeShared = 1;
+
+template <int D, int G, bool Stream, typename KV, int Mode = kModePlain>
 __global__ __launch_bounds__(kThreads) void decode_gqa_kernel(const DecodeArgs a) {
   static_assert(G >= 1 && G <= 16, "query heads per KV head must fit 16 columns");
+  constexpr int S = 16 / G;  // samples of a group per tile in the prefix pass
   using Gm = GqaGeo<D>;
   constexpr int KS = Gm::KS, DT = Gm::DT, PIECES = Gm::PIECES, VLOADS = Gm::VLOADS;
   constexpr int VPITCH = Gm::VPITCH;
@@ -320,42 +339,76 @@ __global__ __launch_bounds__(kThreads) void decode_gqa_kernel(const DecodeArgs a
 
   const int lane = threadIdx.x & (kWave - 1);
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const DecodeItem item = decode_item(a);
+  // shared-prefix decode runs both passes in one launch: the first prefix_grid workgroups
+  // take the prefix items, the rest each sequence's own tokens
+  const bool pre = Mode == kModeShared && (int)blockIdx.x < a.prefix_grid;
+  const DecodeItem item =
+      pre ? decode_item(a, a.num_groups * a.group_chunks, a.prefix_parts, blockIdx.x)
+          : decode_item(a, a.num_seqs, a.num_partitions, blockIdx.x - (Mode == kModeShared ? a.prefix_grid : 0));
   if (!item.valid) return;
   const int kvh = item.hg * kWavesPerGroup + w;
   const int p = item.p;
-  const int b = item.b;
   if (kvh >= a.num_kv_heads) return;
-  const int n = lane & 15;   // token row of K / query-head column
+  const int n = lane & 15;   // token row of K / tile column
   const int q4 = lane >> 4;  // 16-lane group
   half_t* vs = vstage[w];
 
-  const int L = a.context_lens[b];
-  const bool bad_len = L < 0 || L > a.max_context_len || L > a.max_blocks_per_seq * kBlockSize;
+  // b: the sequence whose table the wave reads; [tok_lo, L): the tokens of this pass;
+  // column n stands for query head (col_seq, col_head) when col_ok
+  int b = item.b, tok_lo = 0, L, col_seq = b, col_head = kvh * G + n, slot0 = 0;
+  bool col_ok = n < G;
   half_t* out = static_cast<half_t*>(a.out);
-  if (bad_len || L == 0) {
-    if (p == 0 && lane < G * PIECES) {
-      const int h = kvh * G + lane / PIECES;
-      half8_t v;
+  if constexpr (Mode == kModePlain) {
+    L = a.context_lens[b];
+    const bool bad_len = L < 0 || L > a.max_context_len || L > a.max_blocks_per_seq * kBlockSize;
+    if (bad_len || L == 0) {
+      if (p == 0 && lane < G * PIECES) {
+        const int h = kvh * G + lane / PIECES;
+        half8_t v;
 #pragma unroll
-      for (int d = 0; d < 8; ++d) v[d] = (half_t)(bad_len ? qnan() : 0.0f);
-      *reinterpret_cast<half8_t*>(out + ((int64_t)b * a.num_q_heads + h) * D + 8 * (lane % PIECES)) = v;
+        for (int d = 0; d < 8; ++d) v[d] = (half_t)(bad_len ? qnan() : 0.0f);
+        *reinterpret_cast<half8_t*>(out + ((int64_t)b * a.num_q_heads + h) * D + 8 * (lane % PIECES)) = v;
+      }
+      return;
     }
-    return;
+  } else if (pre) {
+    // item.b enumerates (group, chunk of S samples)
+    const int grp = b / a.group_chunks, chunk = b % a.group_chunks;
+    const int seq0 = a.group_start[grp], nseq = a.group_start[grp + 1] - seq0;
+    if (chunk * S >= nseq) return;
+    L = a.prefix_lens[grp];
+    // a prefix or group the arguments cannot hold is left out; the reduce turns its rows
+    // into NaN
+    if (L <= 0 || L % kBlockSize || L > a.max_context_len || L > a.max_blocks_per_seq * kBlockSize ||
+        seq0 < 0 || seq0 + nseq > a.num_seqs)
+      return;
+    b = seq0;  // every table of the group holds the prefix blocks: read the first
+    col_seq = seq0 + chunk * S + n / G;
+    col_head = kvh * G + n % G;
+    col_ok = n < S * G && chunk * S + n / G < nseq;
+  } else {
+    const int grp = group_of(a, b);
+    L = a.context_lens[b];
+    if (grp < 0) return;
+    tok_lo = a.prefix_lens[grp];
+    if (L < 0 || L > a.max_context_len || L > a.max_blocks_per_seq * kBlockSize || tok_lo < 0 ||
+        tok_lo % kBlockSize || tok_lo > L)
+      return;
+    slot0 = a.prefix_parts;
   }
   const int part_tokens = a.partition_blocks * kBlockSize;
-  const int nparts = (L + part_tokens - 1) / part_tokens;
+  const int nparts = (L - tok_lo + part_tokens - 1) / part_tokens;
   if (p >= nparts) return;
-  const int blk_begin = p * a.partition_blocks;
+  const int blk_begin = tok_lo / kBlockSize + p * a.partition_blocks;
   const int blk_end = min(blk_begin + a.partition_blocks, (L + kBlockSize - 1) / kBlockSize);
 
-  // B operand of S^T: query head n's dims 32ks + 8q4 .. +8, zero past the group
+  // B operand of S^T: column n's query dims 32ks + 8q4 .. +8, zero past the used columns
   const half_t* qp = static_cast<const half_t*>(a.q);
   half8_t qb[KS];
 #pragma unroll
   for (int ks = 0; ks < KS; ++ks)
-    qb[ks] = n < G ? load16(qp + ((int64_t)b * a.num_q_heads + (int64_t)kvh * G + n) * D + 32 * ks + 8 * q4)
-                   : half8_t{};
+    qb[ks] = col_ok ? load16(qp + ((int64_t)col_seq * a.num_q_heads + col_head) * D + 32 * ks + 8 * q4)
+                    : half8_t{};
 
   const int kv_row = a.num_kv_heads * D;
   const int tok_stride = 2 * kv_row;
@@ -468,10 +521,11 @@ __global__ __launch_bounds__(kThreads) void decode_gqa_kernel(const DecodeArgs a
   // column sums over the four 16-lane groups
   l += __shfl_xor(l, 16, kWave);
   l += __shfl_xor(l, 32, kWave);
-  if (n >= G) return;
-  const int64_t bh = (int64_t)b * a.num_q_heads + (int64_t)kvh * G + n;
+  if (!col_ok) return;
+  const int64_t bh = (int64_t)col_seq * a.num_q_heads + col_head;
+  const int slot = slot0 + p;  // workspace partition slot
   if (bad_table) {
-    if (nparts == 1) {
+    if (Mode == kModePlain && nparts == 1) {
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt) {
         half4_t x;
@@ -480,14 +534,14 @@ __global__ __launch_bounds__(kThreads) void decode_gqa_kernel(const DecodeArgs a
         *reinterpret_cast<half4_t*>(out + bh * D + 16 * dt + 4 * q4) = x;
       }
     } else if (q4 == 0) {
-      float* wml = a.ws_ml + (bh * a.num_partitions + p) * 2;
+      float* wml = a.ws_ml + (bh * a.ws_parts + slot) * 2;
       wml[0] = qnan();
       wml[1] = qnan();
     }
     return;
   }
   const float inv = a.v_scale / l;
-  if (nparts == 1) {
+  if (Mode == kModePlain && nparts == 1) {
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) {
       half4_t x;
@@ -496,19 +550,22 @@ __global__ __launch_bounds__(kThreads) void decode_gqa_kernel(const DecodeArgs a
       *reinterpret_cast<half4_t*>(out + bh * D + 16 * dt + 4 * q4) = x;
     }
   } else {
-    float* wo = a.ws_o + (bh * a.num_partitions + p) * D;
+    float* wo = a.ws_o + (bh * a.ws_parts + slot) * D;
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) *reinterpret_cast<float4_t*>(wo + 16 * dt + 4 * q4) = o[dt] * inv;
     if (q4 == 0) {
-      float* wml = a.ws_ml + (bh * a.num_partitions + p) * 2;
+      float* wml = a.ws_ml + (bh * a.ws_parts + slot) * 2;
       wml[0] = m;
       wml[1] = l;
     }
   }
 }
 
-// Merge the partitions of every (sequence, query head) that has more than one.
-template <int D>
+// Merge the partitions of every (sequence, query head) that has more than one. With
+// Cascade (shared-prefix decode) every row is merged here from its prefix partitions
+// (slots 0 ..) and its own partitions (slots prefix_parts ..), and rows whose length or
+// group is out of bounds become NaN (no partition kernel writes rows in that mode).
+template <int D, bool Cascade>
 __global__ __launch_bounds__(kThreads) void decode_reduce_kernel(const DecodeArgs a) {
   constexpr int PER_LANE = D / kWave;  // 2 (D=128) or 1 (D=64)
   const int lane = threadIdx.x & (kWave - 1);
@@ -516,29 +573,49 @@ __global__ __launch_bounds__(kThreads) void decode_reduce_kernel(const DecodeArg
   const int b = blockIdx.y;
   if (h >= a.num_q_heads) return;
   const int L = a.context_lens[b];
-  if (L < 0 || L > a.max_context_len || L > a.max_blocks_per_seq * kBlockSize) return;
+  const bool bad_len = L < 0 || L > a.max_context_len || L > a.max_blocks_per_seq * kBlockSize;
   const int part_tokens = a.partition_blocks * kBlockSize;
-  const int nparts = (L + part_tokens - 1) / part_tokens;
-  if (nparts <= 1) return;
-
   const int64_t bh = (int64_t)b * a.num_q_heads + h;
-  const float* ml = a.ws_ml + bh * a.num_partitions * 2;
-  const float* o = a.ws_o + bh * a.num_partitions * D + lane * PER_LANE;
+  half_t* out = static_cast<half_t*>(a.out) + bh * D + lane * PER_LANE;
+  int n_pre = 0, n_own;
+  if constexpr (Cascade) {
+    const int grp = group_of(a, b);
+    const int P = grp < 0 ? -1 : a.prefix_lens[grp];
+    const bool bad = bad_len || grp < 0 || a.group_start[grp] < 0 ||
+                     a.group_start[grp + 1] > a.num_seqs || b - a.group_start[grp] >= a.group_cap ||
+                     P < 0 || P % kBlockSize || P > L ||
+                     (P + part_tokens - 1) / part_tokens > a.prefix_parts;
+    if (bad || L == 0) {
+#pragma unroll
+      for (int k = 0; k < PER_LANE; ++k) out[k] = (half_t)(bad ? qnan() : 0.0f);
+      return;
+    }
+    n_pre = (P + part_tokens - 1) / part_tokens;
+    n_own = (L - P + part_tokens - 1) / part_tokens;
+  } else {
+    if (bad_len) return;
+    n_own = (L + part_tokens - 1) / part_tokens;
+    if (n_own <= 1) return;
+  }
+  const int n_all = n_pre + n_own;
+  const float* ml = a.ws_ml + bh * a.ws_parts * 2;
+  const float* o = a.ws_o + bh * a.ws_parts * D + lane * PER_LANE;
+  auto slot_of = [&](int k) { return k < n_pre ? k : a.prefix_parts * Cascade + (k - n_pre); };
 
   float M = neg_inf();
-  for (int p = 0; p < nparts; ++p) M = fmaxf(M, ml[2 * p]);
+  for (int k = 0; k < n_all; ++k) M = fmaxf(M, ml[2 * slot_of(k)]);
   float den = 0.0f, acc[PER_LANE];
 #pragma unroll
   for (int k = 0; k < PER_LANE; ++k) acc[k] = 0.0f;
 #pragma unroll 8
-  for (int p = 0; p < nparts; ++p) {
-    const float w = ml[2 * p + 1] * fast_exp2(ml[2 * p] - M);
+  for (int k = 0; k < n_all; ++k) {
+    const int sl = slot_of(k);
+    const float w = ml[2 * sl + 1] * fast_exp2(ml[2 * sl] - M);
     den += w;
 #pragma unroll
-    for (int k = 0; k < PER_LANE; ++k) acc[k] = fmaf(w, o[(int64_t)p * D + k], acc[k]);
+    for (int e = 0; e < PER_LANE; ++e) acc[e] = fmaf(w, o[(int64_t)sl * D + e], acc[e]);
   }
   const float inv = 1.0f / den;
-  half_t* out = static_cast<half_t*>(a.out) + bh * D + lane * PER_LANE;
 #pragma unroll
   for (int k = 0; k < PER_LANE; ++k) out[k] = (half_t)(acc[k] * inv);
 }
@@ -564,7 +641,7 @@ hipError_t launch_decode_dg(const DecodeArgs& a, hipStream_t stream) {
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.num_partitions == 1) return e;
   dim3 rgrid((a.num_q_heads + kWavesPerGroup - 1) / kWavesPerGroup, a.num_seqs);
-  hipLaunchKernelGGL((decode_reduce_kernel<D>), rgrid, dim3(kThreads), 0, stream, a);
+  hipLaunchKernelGGL((decode_reduce_kernel<D, false>), rgrid, dim3(kThreads), 0, stream, a);
   return hipGetLastError();
 }
 
@@ -579,7 +656,58 @@ hipError_t launch_decode_d(const DecodeArgs& a, hipStream_t stream) {
   }
 }
 
+template <int D, int G, typename KV>
+hipError_t launch_shared_prefix_dg(const DecodeArgs& a, hipStream_t stream) {
+  constexpr int S = 16 / G;  // samples per prefix tile
+  const int64_t hgroups = (a.num_kv_heads + kWavesPerGroup - 1) / kWavesPerGroup;
+  auto grid_of = [&](int64_t seqs, int64_t parts) {
+    const int64_t quads = (seqs + kSeqQuad - 1) / kSeqQuad * parts * hgroups;
+    return (quads + kXcds - 1) / kXcds * kXcds * kSeqQuad;
+  };
+  // a.group_cap holds the caller's largest group size on entry
+  DecodeArgs k = a;
+  k.group_chunks = (a.group_cap + S - 1) / S;
+  k.group_cap = k.group_chunks * S;
+  const int64_t wpre =
+      a.prefix_parts > 0 ? grid_of((int64_t)a.num_groups * k.group_chunks, a.prefix_parts) : 0;
+  const int64_t wown = grid_of(a.num_seqs, a.num_partitions);
+  if (wpre + wown > INT32_MAX) return hipErrorInvalidValue;
+  k.prefix_grid = (int)wpre;
+  // one launch: prefix items, then every sequence's own tokens (independent outputs)
+  hipLaunchKernelGGL((decode_gqa_kernel<D, G, false, KV, kModeShared>), dim3((unsigned)(wpre + wown)),
+                     dim3(kThreads), 0, stream, k);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  DecodeArgs own = k;
+  dim3 rgrid((a.num_q_heads + kWavesPerGroup - 1) / kWavesPerGroup, a.num_seqs);
+  hipLaunchKernelGGL((decode_reduce_kernel<D, true>), rgrid, dim3(kThreads), 0, stream, own);
+  return hipGetLastError();
+}
+
+template <int D, typename KV>
+hipError_t launch_shared_prefix_d(const DecodeArgs& a, hipStream_t stream) {
+  switch (a.num_q_heads / a.num_kv_heads) {
+    case 1: return launch_shared_prefix_dg<D, 1, KV>(a, stream);
+    case 2: return launch_shared_prefix_dg<D, 2, KV>(a, stream);
+    case 4: return launch_shared_prefix_dg<D, 4, KV>(a, stream);
+    case 8: return launch_shared_prefix_dg<D, 8, KV>(a, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
 }  // namespace
+
+hipError_t launch_decode_shared_prefix(const DecodeArgs& a, hipStream_t stream) {
+  if (a.num_seqs == 0) return hipSuccess;
+  if (a.kv_fp8) {
+    if (a.head_size == 128) return launch_shared_prefix_d<128, fp8_t>(a, stream);
+    if (a.head_size == 64) return launch_shared_prefix_d<64, fp8_t>(a, stream);
+  } else {
+    if (a.head_size == 128) return launch_shared_prefix_d<128, half_t>(a, stream);
+    if (a.head_size == 64) return launch_shared_prefix_d<64, half_t>(a, stream);
+  }
+  return hipErrorInvalidValue;
+}
 
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream) {
   if (a.num_seqs == 0) return hipSuccess;

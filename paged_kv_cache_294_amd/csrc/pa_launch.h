@@ -29,12 +29,23 @@ struct DecodeArgs {
   int max_context_len;
   int partition_blocks;  // partition size in blocks
   int num_partitions;    // partitions the grid covers
+  int ws_parts;          // partition slots per (sequence, query head) in the workspace
+  // Shared-prefix decode: sequences group_start[g] .. group_start[g + 1] - 1 share their
+  // first prefix_lens[g] tokens (whole blocks, same table entries). Null: plain decode.
+  const int32_t* group_start;
+  const int32_t* prefix_lens;
+  int num_groups;
+  int group_chunks;      // prefix pass: chunks of samples per group
+  int group_cap;         // samples per group the prefix pass covers (chunks * samples per tile)
+  int prefix_parts;      // workspace slots 0 .. prefix_parts - 1 hold prefix partitions
+  int prefix_grid;       // workgroups of the prefix pass (they come first in the launch)
   float scale_log2;      // softmax scale * log2(e), times the key scale of an FP8 cache
   float v_scale;         // value scale of an FP8 cache (1 for fp16)
   bool stream_kv;        // K/V loads carry the non-temporal hint (blocks read once per step)
   bool kv_fp8;           // the pool holds E4M3 codes (1 byte per element) instead of fp16
 };
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
+hipError_t launch_decode_shared_prefix(const DecodeArgs& a, hipStream_t stream);
 
 struct PrefillArgs {
   void* out;
