@@ -430,7 +430,7 @@ def summarize_counters(fetch_csv, write_csv, command):
         wb = sum(x[1] for x in v) / len(v)
         print(f"{name[:72]:<72} {len(v):>3} {rb:>14.0f} {wb:>14.0f}")
     dec = [sum(x[0] + x[1] for x in v) / len(v) for n, v in per.items()
-           if "decode_partition_kernel" in n or "decode_reduce_kernel" in n]
+           if "decode_partition_kernel" in n or "decode_gqa_kernel" in n or "decode_reduce_kernel" in n]
     print(f"hbm_bytes_per_launch: {sum(dec):.0f}")
     print(f"kernel_source_sha256_16: {source_digest(DECODE_SRC)}")
 
