@@ -479,19 +479,19 @@ PA_EXPORT pa_status pa_graph_end(void* stream, pa_graph** out) {
   hipError_t e = hipStreamEndCapture(static_cast<hipStream_t>(stream), &graph);
   if (e != hipSuccess) return hip_status(e);
   if (out == nullptr) {
-    hipGraphDestroy(graph);
+    (void)hipGraphDestroy(graph);  // releasing on an error path: its status adds nothing
     return PA_ERR_INVALID;
   }
   hipGraphExec_t exec = nullptr;
   e = hipGraphInstantiate(&exec, graph, nullptr, nullptr, 0);
   if (e != hipSuccess) {
-    hipGraphDestroy(graph);
+    (void)hipGraphDestroy(graph);
     return hip_status(e);
   }
   pa_graph* g = new (std::nothrow) pa_graph{graph, exec};
   if (g == nullptr) {
-    hipGraphExecDestroy(exec);
-    hipGraphDestroy(graph);
+    (void)hipGraphExecDestroy(exec);
+    (void)hipGraphDestroy(graph);
     std::snprintf(g_last_error, sizeof(g_last_error), "out of host memory");
     return PA_ERR_INVALID;
   }
@@ -506,7 +506,8 @@ PA_EXPORT pa_status pa_graph_launch(const pa_graph* g, void* stream) {
 
 PA_EXPORT void pa_graph_destroy(pa_graph* g) {
   if (g == nullptr) return;
-  hipGraphExecDestroy(g->exec);
-  hipGraphDestroy(g->graph);
+  // a destroy call has no caller to report to: the handle is gone either way
+  (void)hipGraphExecDestroy(g->exec);
+  (void)hipGraphDestroy(g->graph);
   delete g;
 }
