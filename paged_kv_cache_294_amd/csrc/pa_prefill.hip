@@ -32,6 +32,8 @@
 // the accumulator rescale is rare and fp16 P stays <= 256. Causal mask: chunk row i
 // (position P + i) sees tokens 0 .. P + i; only stages crossing that diagonal or the end
 // of the context are masked, and stages past every row of a wave are skipped by it.
+#include <type_traits>
+
 #include "pa_device.h"
 #include "pa_launch.h"
 
@@ -234,7 +236,7 @@ __global__ __launch_bounds__(kThreads, 3) void prefill_kernel(const PrefillArgs 
       tab[v] = own;
     }
   };
-  auto issue_stage = [&](int st) {
+  auto issue_stage = [&](int st, int ring) {
     if (st > 0 && st % (64 * kTabRegs) == 0) load_table(st / (64 * kTabRegs));  // uniform
     const int v = (st >> 6) % kTabRegs;
     int cand = tab[0];
@@ -242,7 +244,7 @@ __global__ __launch_bounds__(kThreads, 3) void prefill_kernel(const PrefillArgs 
     for (int u = 1; u < kTabRegs; ++u) cand = (v == u) ? tab[u] : cand;
     const int phys = __builtin_amdgcn_readlane(cand, st & 63);
     const char* block = pool + (uint64_t)phys * block_bytes;
-    const uint32_t kdst = lds_k0 + (uint32_t)(st % kStages) * kStageBytes;
+    const uint32_t kdst = lds_k0 + (uint32_t)ring * kStageBytes;  // ring == st % kStages
 #pragma unroll
     for (int j = 0; j < INST; ++j)
       load_kv_lds16(block, koff[j], voff[j], kdst + j * kInstBytes, kdst + kVBytes + j * kInstBytes);
@@ -262,7 +264,7 @@ __global__ __launch_bounds__(kThreads, 3) void prefill_kernel(const PrefillArgs 
   const int vtok = 4 * g + li / 4;  // token (within a 16-token k-step half) of this source lane
 
   load_table(0);
-  for (int st = 0; st < kStages - 1 && st < nst; ++st) issue_stage(st);
+  for (int st = 0; st < kStages - 1 && st < nst; ++st) issue_stage(st, st);
   // the query rows come in behind the first stages, and one wait covers both: the compiler
   // then knows of no load in flight inside the loop and leaves the waiting to the loop's
   // own counted waits
@@ -275,16 +277,19 @@ __global__ __launch_bounds__(kThreads, 3) void prefill_kernel(const PrefillArgs 
   }
   wait_vm<0>();
 
-  for (int it = 0; it < nst; ++it) {
+  // One stage of the context. The ring slot is a compile-time constant (the loop below is
+  // unrolled by the ring depth), so every LDS address of the stage is a per-lane base plus
+  // an immediate offset.
+  auto stage = [&](auto ring_c, const int it) {
+    constexpr int ring = decltype(ring_c)::value;
+    constexpr int kRing = ring;
+
     // this wave's loads of stage `it` have landed once at most the loads of the stages
     // issued after it are outstanding; the barrier makes every wave's loads visible and
     // frees ring slot (it - 1) % kStages for stage it + kStages - 1
-    static_assert(kStages == 3 || kStages == 4, "waits below cover up to two stages ahead");
-    if (kStages == 4 && it + 2 < nst) wait_vm<4 * INST>();
-    else if (it + 1 < nst) wait_vm<2 * INST>();
+    if (it + 1 < nst) wait_vm<2 * INST>();
     else wait_vm<0>();
     lds_barrier();
-    const int ring = it % kStages;
     const int t0 = it * kBN;
     if (__builtin_amdgcn_readfirstlane(t0 + kBN > S)) {
       // the context's last stage: V rows past the end become zeros (their slots may hold
@@ -296,7 +301,7 @@ __global__ __launch_bounds__(kThreads, 3) void prefill_kernel(const PrefillArgs 
       }
       lds_barrier();
     }
-    if (it + kStages - 1 < nst) issue_stage(it + kStages - 1);
+    if (it + kStages - 1 < nst) issue_stage(it + kStages - 1, (kRing + kStages - 1) % kStages);
 
     if (t0 < wave_end) {
       // S^T for the stage's 32 tokens
@@ -376,7 +381,19 @@ __global__ __launch_bounds__(kThreads, 3) void prefill_kernel(const PrefillArgs 
         for (int dt = 0; dt < DT; ++dt)
           o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(va[k][dt], pb[k], o[dt], 0, 0, 0);
     }
+    };
+  using R0 = std::integral_constant<int, 0>;
+  using R1 = std::integral_constant<int, 1>;
+  using R2 = std::integral_constant<int, 2>;
+  static_assert(kStages == 3, "the stage loop is unrolled by a ring of three");
+  int it = 0;
+  for (; it + 3 <= nst; it += 3) {
+    stage(R0{}, it);
+    stage(R1{}, it + 1);
+    stage(R2{}, it + 2);
   }
+  if (it < nst) stage(R0{}, it++);
+  if (it < nst) stage(R1{}, it++);
 
   l += __shfl_xor(l, 32, kWave);
   const bool bad_table = __builtin_amdgcn_ballot_w64(bad_lanes) != 0;
