@@ -401,6 +401,35 @@ def summarize_trace(path, command):
               f"{float(r['Percentage']):>6.2f}")
 
 
+def summarize_pmc(paths, kernel, command):
+    """Median per-dispatch value of each counter for the dispatches of `kernel`, and the
+    matrix-core busy fraction: SQ_VALU_MFMA_BUSY_CYCLES over all SIMD cycles, where
+    GRBM_GUI_ACTIVE sums the active cycles of the 8 XCDs (128 SIMDs each)."""
+    import csv
+    import statistics
+    per = {}  # counter -> {(pass, dispatch): value summed over the pass's rows}
+    for k, path in enumerate(paths):
+        for r in csv.DictReader(open(path)):
+            if kernel not in r["Kernel_Name"]:
+                continue
+            d = per.setdefault(r["Counter_Name"], {})
+            key = (k, r["Dispatch_Id"])
+            d[key] = d.get(key, 0.0) + float(r["Counter_Value"])
+    print(f"# rocprofv3 --pmc counters of kernels matching '{kernel}' (median per dispatch)")
+    print(f"# command: {command}")
+    med = {}
+    for name in sorted(per):
+        vals = list(per[name].values())
+        med[name] = statistics.median(vals)
+        print(f"{name:32s} {med[name]:16.0f}   ({len(vals)} dispatches)")
+    if "SQ_VALU_MFMA_BUSY_CYCLES" in med and "GRBM_GUI_ACTIVE" in med:
+        print(f"mfma_busy_fraction: {med['SQ_VALU_MFMA_BUSY_CYCLES'] / (med['GRBM_GUI_ACTIVE'] * 128):.3f}")
+    if "SQ_INSTS_VALU" in med and "SQ_INSTS_MFMA" in med:
+        print(f"valu_per_mfma: {med['SQ_INSTS_VALU'] / med['SQ_INSTS_MFMA']:.2f}")
+    if "SQ_LDS_BANK_CONFLICT" in med and "SQ_LDS_IDX_ACTIVE" in med:
+        print(f"lds_bank_conflict_fraction: {med['SQ_LDS_BANK_CONFLICT'] / med['SQ_LDS_IDX_ACTIVE']:.3f}")
+
+
 def summarize_counters(fetch_csv, write_csv, command):
     """Per-dispatch FETCH_SIZE / WRITE_SIZE (KiB) of the --mode counters sequence, scaled by
     the reading of the 1 GiB copy."""
@@ -470,10 +499,18 @@ def main():
     ap.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="print the HBM traffic summary of two rocprofv3 --pmc passes of "
                          "--mode counters (FETCH_SIZE, then WRITE_SIZE) and exit")
+    ap.add_argument("--summarize-pmc", nargs="+", metavar="COUNTER_CSV",
+                    help="print the median per-dispatch counters of --kernel from rocprofv3 "
+                         "--pmc passes (one CSV per pass) and exit")
+    ap.add_argument("--kernel", default="prefill_kernel",
+                    help="kernel-name substring for --summarize-pmc")
     ap.add_argument("--command", default="", help="command line recorded in a summary")
     args = ap.parse_args()
     if args.summarize_trace:
         summarize_trace(args.summarize_trace, args.command)
+        return
+    if args.summarize_pmc:
+        summarize_pmc(args.summarize_pmc, args.kernel, args.command)
         return
     if args.summarize_counters:
         summarize_counters(*args.summarize_counters, args.command)
