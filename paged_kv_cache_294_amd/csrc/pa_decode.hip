@@ -38,12 +38,41 @@ constexpr int kWavesPerGroup = 4;
 constexpr int kThreads = kWavesPerGroup * kWave;
 constexpr int kXcds = 8;  // accelerator dies of an MI355X
 
-template <int D>
+// Lane geometry of the MHA kernel: each lane holds EPL consecutive elements of a token row
+// (one 16-byte load: 8 fp16 values or 16 E4M3 codes).
+template <int D, int EPL>
 struct Geo {
-  static constexpr int kLanesPerToken = D / 8;                          // 16 or 8
-  static constexpr int kTokensPerLoad = kWave / kLanesPerToken;         // 4 or 8
-  static constexpr int kLoadsPerBlock = kBlockSize / kTokensPerLoad;    // 4 or 2
+  static constexpr int kLanesPerToken = D / EPL;                        // 16, 8 or 4
+  static constexpr int kTokensPerLoad = kWave / kLanesPerToken;         // 4, 8 or 16
+  static constexpr int kLoadsPerBlock = kBlockSize / kTokensPerLoad;    // 4, 2 or 1
 };
+
+// EPL cache elements at p (16 bytes) as NV = EPL / 8 fp16 vectors.
+template <typename KV, bool Stream, int NV>
+__device__ __forceinline__ void load_row_piece(const KV* p, half8_t (&x)[NV]) {
+  if constexpr (sizeof(KV) == 2) {
+    static_assert(NV == 1, "16 bytes of fp16 are 8 elements");
+    x[0] = load16<Stream>(reinterpret_cast<const half_t*>(p));
+  } else {
+    static_assert(NV == 2, "16 bytes of E4M3 are 16 elements");
+    typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+    typedef __attribute__((address_space(1))) const u32x4_t gconst_u32x4_t;
+    gconst_u32x4_t* gp = (gconst_u32x4_t*)(p);
+    u32x4_t w;
+    if constexpr (Stream)
+      w = __builtin_nontemporal_load(gp);
+    else
+      w = *gp;
+#pragma unroll
+    for (int v = 0; v < 2; ++v) {
+      const half2_t a = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w[2 * v], 1.0f, false);
+      const half2_t b = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w[2 * v], 1.0f, true);
+      const half2_t c = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w[2 * v + 1], 1.0f, false);
+      const half2_t d = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w[2 * v + 1], 1.0f, true);
+      x[v] = half8_t{a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
+    }
+  }
+}
 
 // Work item (KV-head group, partition, sequence) of a workgroup. Workgroups reach the 8
 // XCDs round-robin in launch order (workgroup i to XCD i % 8), each XCD with its own L2.
@@ -74,7 +103,7 @@ __device__ __forceinline__ DecodeItem decode_item(const DecodeArgs& a, int num_s
   return it;
 }
 
-template <int D, int G>
+template <int D, int G, int EPL>
 __device__ __forceinline__ void write_const_rows(const DecodeArgs& a, int b, int kvh, int col,
                                                  float value) {
   half_t* out = static_cast<half_t*>(a.out);
@@ -84,13 +113,17 @@ __device__ __forceinline__ void write_const_rows(const DecodeArgs& a, int b, int
 #pragma unroll
   for (int g = 0; g < G; ++g) {
     const int64_t h = (int64_t)kvh * G + g;
-    *reinterpret_cast<half8_t*>(out + ((int64_t)b * a.num_q_heads + h) * D + col * 8) = v;
+#pragma unroll
+    for (int u = 0; u < EPL / 8; ++u)
+      *reinterpret_cast<half8_t*>(out + ((int64_t)b * a.num_q_heads + h) * D + col * EPL + 8 * u) = v;
   }
 }
 
 template <int D, int G, bool Stream, typename KV>
 __global__ __launch_bounds__(kThreads) void decode_partition_kernel(const DecodeArgs a) {
-  using Gm = Geo<D>;
+  constexpr int EPL = 16 / sizeof(KV);  // elements per lane and load
+  constexpr int NV = EPL / 8;           // fp16 vectors per lane
+  using Gm = Geo<D, EPL>;
   constexpr int LPT = Gm::kLanesPerToken;
   constexpr int TPL = Gm::kTokensPerLoad;
   constexpr int LPB = Gm::kLoadsPerBlock;
@@ -108,7 +141,7 @@ __global__ __launch_bounds__(kThreads) void decode_partition_kernel(const Decode
   const int L = a.context_lens[b];
   const bool bad_len = L < 0 || L > a.max_context_len || L > a.max_blocks_per_seq * kBlockSize;
   if (bad_len || L == 0) {
-    if (p == 0 && row == 0) write_const_rows<D, G>(a, b, kvh, col, bad_len ? qnan() : 0.0f);
+    if (p == 0 && row == 0) write_const_rows<D, G, EPL>(a, b, kvh, col, bad_len ? qnan() : 0.0f);
     return;
   }
   const int part_tokens = a.partition_blocks * kBlockSize;
@@ -118,48 +151,50 @@ __global__ __launch_bounds__(kThreads) void decode_partition_kernel(const Decode
   const int blk_end = min(blk_begin + a.partition_blocks, (L + kBlockSize - 1) / kBlockSize);
 
   const half_t* qp = static_cast<const half_t*>(a.q);
-  half8_t qv[G];
+  half8_t qv[G][NV];
 #pragma unroll
   for (int g = 0; g < G; ++g)
-    qv[g] = *reinterpret_cast<const half8_t*>(
-        qp + ((int64_t)b * a.num_q_heads + (int64_t)kvh * G + g) * D + col * 8);
+#pragma unroll
+    for (int u = 0; u < NV; ++u)
+      qv[g][u] = *reinterpret_cast<const half8_t*>(
+          qp + ((int64_t)b * a.num_q_heads + (int64_t)kvh * G + g) * D + col * EPL + 8 * u);
 
   const int kv_row = a.num_kv_heads * D;  // elements of one K (or V) row over all heads
   const int tok_stride = 2 * kv_row;       // elements between consecutive tokens of a block
   const int64_t block_elems = (int64_t)kBlockSize * tok_stride;
   // element offset of this lane's piece of load i inside a block: + i * TPL * tok_stride
-  const int lane_off = row * tok_stride + kvh * D + col * 8;
+  const int lane_off = row * tok_stride + kvh * D + col * EPL;
   const KV* pool = static_cast<const KV*>(a.pool);
   const int32_t* bt = a.block_tables + (int64_t)b * a.max_blocks_per_seq;
 
-  float m[G], l[G], acc[G][8];
+  float m[G], l[G], acc[G][EPL];
 #pragma unroll
   for (int g = 0; g < G; ++g) {
     m[g] = neg_inf();
     l[g] = 0.0f;
 #pragma unroll
-    for (int d = 0; d < 8; ++d) acc[g][d] = 0.0f;
+    for (int d = 0; d < EPL; ++d) acc[g][d] = 0.0f;
   }
 
   // Block-table entries of the partition, one per lane, fetched 64 at a time.
   int bt_vec = (lane < blk_end - blk_begin) ? bt[blk_begin + lane] : 0;
   bool bad_table = false;
 
-  half8_t kc[LPB], vc[LPB];
+  half8_t kc[LPB][NV], vc[LPB][NV];
   {
     const int phys = __builtin_amdgcn_readfirstlane(bt_vec);
     bad_table = phys < 0 || phys >= a.num_blocks;
     const KV* base = pool + (bad_table ? 0 : (int64_t)phys * block_elems) + lane_off;
 #pragma unroll
     for (int i = 0; i < LPB; ++i) {
-      kc[i] = load_kv8<KV, Stream>(base + i * TPL * tok_stride);
-      vc[i] = load_kv8<KV, Stream>(base + i * TPL * tok_stride + kv_row);
+      load_row_piece<KV, Stream>(base + i * TPL * tok_stride, kc[i]);
+      load_row_piece<KV, Stream>(base + i * TPL * tok_stride + kv_row, vc[i]);
     }
   }
 
   for (int j = blk_begin; j < blk_end && !bad_table; ++j) {
     // prefetch block j+1 while block j is consumed
-    half8_t kn[LPB], vn[LPB];
+    half8_t kn[LPB][NV], vn[LPB][NV];
     const int jn = j + 1;
     if (jn < blk_end) {
       const int k64 = (jn - blk_begin) & 63;
@@ -169,8 +204,8 @@ __global__ __launch_bounds__(kThreads) void decode_partition_kernel(const Decode
       const KV* base = pool + (bad_table ? 0 : (int64_t)phys * block_elems) + lane_off;
 #pragma unroll
       for (int i = 0; i < LPB; ++i) {
-        kn[i] = load_kv8<KV, Stream>(base + i * TPL * tok_stride);
-        vn[i] = load_kv8<KV, Stream>(base + i * TPL * tok_stride + kv_row);
+        load_row_piece<KV, Stream>(base + i * TPL * tok_stride, kn[i]);
+        load_row_piece<KV, Stream>(base + i * TPL * tok_stride + kv_row, vn[i]);
       }
     }
 
@@ -179,7 +214,12 @@ __global__ __launch_bounds__(kThreads) void decode_partition_kernel(const Decode
 #pragma unroll
     for (int i = 0; i < LPB; ++i)
 #pragma unroll
-      for (int g = 0; g < G; ++g) s[g][i] = group_sum<LPT>(dot8(qv[g], kc[i], 0.0f)) * a.scale_log2;
+      for (int g = 0; g < G; ++g) {
+        float dot = 0.0f;
+#pragma unroll
+        for (int u = 0; u < NV; ++u) dot = dot8(qv[g][u], kc[i][u], dot);
+        s[g][i] = group_sum<LPT>(dot) * a.scale_log2;
+      }
 
     const int tok0 = j * kBlockSize;
     if (tok0 + kBlockSize > L) {  // the sequence's last, partly filled block
@@ -188,7 +228,8 @@ __global__ __launch_bounds__(kThreads) void decode_partition_kernel(const Decode
         if (tok0 + i * TPL + row >= L) {
 #pragma unroll
           for (int g = 0; g < G; ++g) s[g][i] = neg_inf();
-          vc[i] = half8_t{};
+#pragma unroll
+          for (int u = 0; u < NV; ++u) vc[i][u] = half8_t{};
         }
       }
     }
@@ -208,20 +249,22 @@ __global__ __launch_bounds__(kThreads) void decode_partition_kernel(const Decode
       }
       l[g] = l[g] * alpha + psum;
 #pragma unroll
-      for (int d = 0; d < 8; ++d) {
+      for (int d = 0; d < EPL; ++d) {
         float x = acc[g][d] * alpha;
 #pragma unroll
-        for (int i = 0; i < LPB; ++i) x = fmaf(pr[i], (float)vc[i][d], x);
+        for (int i = 0; i < LPB; ++i) x = fmaf(pr[i], (float)vc[i][d / 8][d % 8], x);
         acc[g][d] = x;
       }
       m[g] = mx;
     }
 
 #pragma unroll
-    for (int i = 0; i < LPB; ++i) {
-      kc[i] = kn[i];
-      vc[i] = vn[i];
-    }
+    for (int i = 0; i < LPB; ++i)
+#pragma unroll
+      for (int u = 0; u < NV; ++u) {
+        kc[i][u] = kn[i][u];
+        vc[i][u] = vn[i][u];
+      }
   }
 
   if (bad_table) {
@@ -229,7 +272,7 @@ __global__ __launch_bounds__(kThreads) void decode_partition_kernel(const Decode
     // partitions the reduce kernel writes the row, so poison this partition's partial.
     if (row == 0) {
       if (nparts == 1) {
-        write_const_rows<D, G>(a, b, kvh, col, qnan());
+        write_const_rows<D, G, EPL>(a, b, kvh, col, qnan());
       } else if (col == 0) {
 #pragma unroll
         for (int g = 0; g < G; ++g) {
@@ -254,7 +297,7 @@ __global__ __launch_bounds__(kThreads) void decode_partition_kernel(const Decode
 #pragma unroll
     for (int o = LPT; o < kWave; o <<= 1) lt += __shfl_xor(lt, o, kWave);
 #pragma unroll
-    for (int d = 0; d < 8; ++d) {
+    for (int d = 0; d < EPL; ++d) {
       float x = acc[g][d] * f;
 #pragma unroll
       for (int o = LPT; o < kWave; o <<= 1) x += __shfl_xor(x, o, kWave);
@@ -265,20 +308,22 @@ __global__ __launch_bounds__(kThreads) void decode_partition_kernel(const Decode
       const int64_t bh = (int64_t)b * a.num_q_heads + h;
       const float inv = a.v_scale / lt;
       if (nparts == 1) {
-        half8_t o;
 #pragma unroll
-        for (int d = 0; d < 8; ++d) o[d] = (half_t)(acc[g][d] * inv);
-        *reinterpret_cast<half8_t*>(static_cast<half_t*>(a.out) + bh * D + col * 8) = o;
-      } else {
-        float4_t o0, o1;
+        for (int u = 0; u < NV; ++u) {
+          half8_t o;
 #pragma unroll
-        for (int d = 0; d < 4; ++d) {
-          o0[d] = acc[g][d] * inv;
-          o1[d] = acc[g][d + 4] * inv;
+          for (int d = 0; d < 8; ++d) o[d] = (half_t)(acc[g][8 * u + d] * inv);
+          *reinterpret_cast<half8_t*>(static_cast<half_t*>(a.out) + bh * D + col * EPL + 8 * u) = o;
         }
-        float* wo = a.ws_o + (bh * a.ws_parts + p) * D + col * 8;
-        *reinterpret_cast<float4_t*>(wo) = o0;
-        *reinterpret_cast<float4_t*>(wo + 4) = o1;
+      } else {
+        float* wo = a.ws_o + (bh * a.ws_parts + p) * D + col * EPL;
+#pragma unroll
+        for (int u = 0; u < 2 * NV; ++u) {
+          float4_t o4;
+#pragma unroll
+          for (int d = 0; d < 4; ++d) o4[d] = acc[g][4 * u + d] * inv;
+          *reinterpret_cast<float4_t*>(wo + 4 * u) = o4;
+        }
         if (col == 0) {
           float* wml = a.ws_ml + (bh * a.ws_parts + p) * 2;
           wml[0] = M;

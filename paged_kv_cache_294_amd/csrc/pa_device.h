@@ -36,14 +36,14 @@ __device__ __forceinline__ float dpp_mov(float x) {
       float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), Ctrl, 0xF, 0xF, false));
 }
 
-// Sum over groups of N consecutive lanes (N in {8, 16}) aligned to N; every lane of the
+// Sum over groups of N consecutive lanes (N in {4, 8, 16}) aligned to N; every lane of the
 // group gets the group's sum.
 template <int N>
 __device__ __forceinline__ float group_sum(float x) {
-  static_assert(N == 8 || N == 16, "row-local sums only");
+  static_assert(N == 4 || N == 8 || N == 16, "row-local sums only");
   x += dpp_mov<kDppXor1>(x);
   x += dpp_mov<kDppXor2>(x);
-  x += dpp_mov<kDppHalfMirror>(x);
+  if constexpr (N >= 8) x += dpp_mov<kDppHalfMirror>(x);
   if constexpr (N == 16) x += dpp_mov<kDppMirror>(x);
   return x;
 }
