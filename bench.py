@@ -349,7 +349,10 @@ class Step:
             else:
                 pkv.pa_kv_append(self.pool, self.key, self.value, self.slots, stream=stream)
         rec(1)
-        if self.has_prefill:
+        if self.has_prefill and self.kv_fp8:
+            pkv.pa_prefill_chunk_fp8(self.pout, self.pq, self.pool, self.pbt, self.qsl, self.plens,
+                                     self.max_q, self.max_s, self.inp.scale, 1.0, 1.0, stream=stream)
+        elif self.has_prefill:
             pkv.pa_prefill_chunk(self.pout, self.pq, self.pool, self.pbt, self.qsl, self.plens,
                                  self.max_q, self.max_s, self.inp.scale, stream=stream)
         rec(2)
@@ -533,10 +536,6 @@ def main():
     kv_stream = {"on": True, "off": False, "auto": not shared}[args.kv_stream]
     kv_fp8 = args.kv_dtype == "fp8"
     elem_bytes = 1 if kv_fp8 else 2
-    if kv_fp8 and inp.num_prefill:
-        print("--kv-dtype fp8 runs decode-only workloads (c1-c4): pa_prefill_chunk reads fp16 "
-              "caches only", file=sys.stderr)
-        sys.exit(2)
     if args.partition_size <= 0:
         args.partition_size = 512 if int(inp.seq_lens.max()) > 8192 else 256
     # algorithmic bytes: every decode context token's K and V once; with shared prefix

@@ -34,6 +34,7 @@ from ._lib import (  # noqa: F401
     pa_num_partitions,
     pa_pool_bytes,
     pa_prefill_chunk,
+    pa_prefill_chunk_fp8,
     pa_slot,
     pa_stream_read,
     pa_stream_read_sink_len,

@@ -51,6 +51,9 @@ SIGNATURES = {
     "pa_decode_shared_prefix_workspace_bytes": (_i64, [_i32, _i32, _i32, _i32, _i32, _i32]),
     "pa_prefill_chunk": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32,
                                         _i32, _i32, _i32, _i32, _i64, _f32, _vp]),
+    "pa_prefill_chunk_fp8": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32,
+                                            _i32, _i32, _i32, _i32, _i32, _i64, _f32, _f32, _f32,
+                                            _vp]),
     "pa_gather_kv": (ctypes.c_int, [_vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i64, _vp]),
     "pa_stream_read": (ctypes.c_int, [_vp, _i64, _vp, _vp]),
     "pa_stream_read_sink_len": (_i64, [_i64]),
@@ -318,9 +321,8 @@ def pa_decode_fp8(out, q, kv_pool, block_tables, context_lens, max_context_len, 
     _check("pa_decode_fp8", st)
 
 
-def pa_prefill_chunk(out, q, kv_pool, block_tables, query_start_loc, seq_lens, max_q_len,
-                     max_seq_len, scale=None, stream=None):
-    """Causal attention of prefill chunks (rows of q [total_q, Hq, D]) over their paged context."""
+def _prefill_args(out, q, kv_pool, block_tables, query_start_loc, seq_lens, max_q_len,
+                  max_seq_len, scale, pool_dtype):
     nb, bs, hkv, d = _pool_geometry(kv_pool)
     total_q, hq, dq = q.shape
     R = int(seq_lens.shape[0])
@@ -330,13 +332,30 @@ def pa_prefill_chunk(out, q, kv_pool, block_tables, query_start_loc, seq_lens, m
         raise ValueError("query_start_loc must be [num_reqs+1], block_tables [num_reqs, max_blocks]")
     if scale is None:
         scale = 1.0 / math.sqrt(d)
-    st = load().pa_prefill_chunk(
-        _dense(out, "out", torch.float16), _dense(q, "q", torch.float16),
-        _dense(kv_pool, "kv_pool", torch.float16), _dense(block_tables, "block_tables", torch.int32),
-        _dense(query_start_loc, "query_start_loc", torch.int32),
-        _dense(seq_lens, "seq_lens", torch.int32), R, total_q, int(max_q_len), int(max_seq_len), hq,
-        hkv, d, bs, int(block_tables.shape[1]), nb, float(scale), _stream(stream))
+    return (_dense(out, "out", torch.float16), _dense(q, "q", torch.float16),
+            _dense(kv_pool, "kv_pool", pool_dtype), _dense(block_tables, "block_tables", torch.int32),
+            _dense(query_start_loc, "query_start_loc", torch.int32),
+            _dense(seq_lens, "seq_lens", torch.int32), R, total_q, int(max_q_len), int(max_seq_len),
+            hq, hkv, d, bs, int(block_tables.shape[1]), nb, float(scale))
+
+
+def pa_prefill_chunk(out, q, kv_pool, block_tables, query_start_loc, seq_lens, max_q_len,
+                     max_seq_len, scale=None, stream=None):
+    """Causal attention of prefill chunks (rows of q [total_q, Hq, D]) over their paged context."""
+    st = load().pa_prefill_chunk(*_prefill_args(out, q, kv_pool, block_tables, query_start_loc,
+                                                seq_lens, max_q_len, max_seq_len, scale,
+                                                torch.float16), _stream(stream))
     _check("pa_prefill_chunk", st)
+
+
+def pa_prefill_chunk_fp8(out, q, kv_pool, block_tables, query_start_loc, seq_lens, max_q_len,
+                         max_seq_len, scale=None, k_scale=1.0, v_scale=1.0, stream=None):
+    """pa_prefill_chunk over an FP8 (E4M3) pool held as a uint8 tensor, with its scales."""
+    st = load().pa_prefill_chunk_fp8(*_prefill_args(out, q, kv_pool, block_tables, query_start_loc,
+                                                    seq_lens, max_q_len, max_seq_len, scale,
+                                                    torch.uint8), float(k_scale), float(v_scale),
+                                     _stream(stream))
+    _check("pa_prefill_chunk_fp8", st)
 
 
 def pa_gather_kv(k_out, v_out, kv_pool, block_table_row, length, stream=None):

@@ -323,13 +323,16 @@ PA_EXPORT pa_status pa_decode_fp8(void* out, const void* q, const void* kv_pool,
                      true, k_scale, v_scale, stream);
 }
 
-PA_EXPORT pa_status pa_prefill_chunk(void* out, const void* q, const void* kv_pool,
-                                     const int32_t* block_tables, const int32_t* query_start_loc,
-                                     const int32_t* seq_lens, int32_t num_reqs, int32_t total_q,
-                                     int32_t max_q_len, int32_t max_seq_len, int32_t num_q_heads,
-                                     int32_t num_kv_heads, int32_t head_size, int32_t block_size,
-                                     int32_t max_blocks_per_seq, int64_t num_blocks, float scale,
-                                     void* stream) {
+namespace {
+
+pa_status prefill_impl(void* out, const void* q, const void* kv_pool, const int32_t* block_tables,
+                       const int32_t* query_start_loc, const int32_t* seq_lens, int32_t num_reqs,
+                       int32_t total_q, int32_t max_q_len, int32_t max_seq_len,
+                       int32_t num_q_heads, int32_t num_kv_heads, int32_t head_size,
+                       int32_t block_size, int32_t max_blocks_per_seq, int64_t num_blocks,
+                       float scale, bool fp8, float k_scale, float v_scale, void* stream) {
+  if (fp8 && !(std::isfinite(k_scale) && k_scale > 0.0f && std::isfinite(v_scale) && v_scale > 0.0f))
+    return PA_ERR_INVALID;
   if (num_reqs < 0 || total_q < 0 || max_q_len < 0 || max_seq_len < 0 ||
       max_blocks_per_seq <= 0 || num_blocks <= 0)
     return PA_ERR_INVALID;
@@ -359,10 +362,40 @@ PA_EXPORT pa_status pa_prefill_chunk(void* out, const void* q, const void* kv_po
   a.head_size = head_size;
   a.max_blocks_per_seq = max_blocks_per_seq;
   a.num_blocks = num_blocks;
-  a.scale_log2 = (float)((double)scale * kLog2e);
+  a.scale_log2 = (float)((double)scale * kLog2e * (double)k_scale);
+  a.v_scale = v_scale;
+  a.kv_fp8 = fp8;
   hipError_t e = pkv::launch_prefill(a, (hipStream_t)stream);
   if (e == hipErrorNotSupported) return PA_ERR_UNSUPPORTED;
   return hip_status(e);
+}
+
+}  // namespace
+
+PA_EXPORT pa_status pa_prefill_chunk(void* out, const void* q, const void* kv_pool,
+                                     const int32_t* block_tables, const int32_t* query_start_loc,
+                                     const int32_t* seq_lens, int32_t num_reqs, int32_t total_q,
+                                     int32_t max_q_len, int32_t max_seq_len, int32_t num_q_heads,
+                                     int32_t num_kv_heads, int32_t head_size, int32_t block_size,
+                                     int32_t max_blocks_per_seq, int64_t num_blocks, float scale,
+                                     void* stream) {
+  return prefill_impl(out, q, kv_pool, block_tables, query_start_loc, seq_lens, num_reqs, total_q,
+                      max_q_len, max_seq_len, num_q_heads, num_kv_heads, head_size, block_size,
+                      max_blocks_per_seq, num_blocks, scale, false, 1.0f, 1.0f, stream);
+}
+
+PA_EXPORT pa_status pa_prefill_chunk_fp8(void* out, const void* q, const void* kv_pool,
+                                         const int32_t* block_tables,
+                                         const int32_t* query_start_loc, const int32_t* seq_lens,
+                                         int32_t num_reqs, int32_t total_q, int32_t max_q_len,
+                                         int32_t max_seq_len, int32_t num_q_heads,
+                                         int32_t num_kv_heads, int32_t head_size,
+                                         int32_t block_size, int32_t max_blocks_per_seq,
+                                         int64_t num_blocks, float scale, float k_scale,
+                                         float v_scale, void* stream) {
+  return prefill_impl(out, q, kv_pool, block_tables, query_start_loc, seq_lens, num_reqs, total_q,
+                      max_q_len, max_seq_len, num_q_heads, num_kv_heads, head_size, block_size,
+                      max_blocks_per_seq, num_blocks, scale, true, k_scale, v_scale, stream);
 }
 
 PA_EXPORT pa_status pa_gather_kv(void* k_out, void* v_out, const void* kv_pool,

@@ -70,9 +70,18 @@ typedef uint8_t fp8_t;
 typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(1))) const u32x2_t gconst_u32x2_t;
 
+// Eight E4M3 codes (in memory order) widened exactly to fp16: every E4M3 value is an fp16
+// value, and v_cvt_scalef32_pk_f16_fp8 with scale 1 converts two codes.
+__device__ __forceinline__ half8_t widen_fp8x8(u32x2_t w) {
+  const half2_t a = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w[0], 1.0f, false);
+  const half2_t b = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w[0], 1.0f, true);
+  const half2_t c = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w[1], 1.0f, false);
+  const half2_t d = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w[1], 1.0f, true);
+  return half8_t{a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
+}
+
 // Eight consecutive cache elements as fp16: a 16-byte load of fp16 elements, or an 8-byte
-// load of E4M3 codes widened exactly to fp16 (every E4M3 value is an fp16 value;
-// v_cvt_scalef32_pk_f16_fp8 with scale 1 converts two codes).
+// load of E4M3 codes widened to fp16.
 template <typename KV, bool Stream = false>
 __device__ __forceinline__ half8_t load_kv8(const KV* p) {
   if constexpr (sizeof(KV) == 2) {
@@ -84,11 +93,7 @@ __device__ __forceinline__ half8_t load_kv8(const KV* p) {
       w = __builtin_nontemporal_load(gp);
     else
       w = *gp;
-    const half2_t a = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w[0], 1.0f, false);
-    const half2_t b = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w[0], 1.0f, true);
-    const half2_t c = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w[1], 1.0f, false);
-    const half2_t d = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w[1], 1.0f, true);
-    return half8_t{a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
+    return widen_fp8x8(w);
   }
 }
 

@@ -58,7 +58,9 @@ struct PrefillArgs {
   int num_q_heads, num_kv_heads, head_size;
   int max_blocks_per_seq;
   int64_t num_blocks;
-  float scale_log2;
+  float scale_log2;  // softmax scale * log2(e), times the key scale of an FP8 cache
+  float v_scale;     // value scale of an FP8 cache (1 for fp16)
+  bool kv_fp8;       // the pool holds E4M3 codes (1 byte per element)
 };
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream);
 

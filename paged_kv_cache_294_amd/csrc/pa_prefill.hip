@@ -98,13 +98,18 @@ template <int D>
 __device__ __forceinline__ int kswz(int t) { return t & 7; }
 template <int D>
 __device__ __forceinline__ int vswz(int t) { return D >= 128 ? 4 * (t & 3) : 4 * (t & 1); }
-
+// K rows of an FP8 cache: 16-byte pieces of E4M3 codes (D / 16 per row)
 template <int D>
+__device__ __forceinline__ int kswz8(int t) { return D >= 128 ? ((t >> 1) & 7) : ((t >> 2) & 3); }
+
+template <int D, typename KV>
 struct PrefillSmem {
-  static constexpr int ROW = D;                 // halves per token row (no padding)
-  static constexpr int TILE = kBN * ROW;        // halves per K (or V) stage
-  half_t k[kStages][TILE];
-  half_t v[kStages][TILE];
+  static constexpr int ROW = D;                 // elements per token row (no padding)
+  static constexpr int TILE = kBN * ROW;        // elements per K (or V) stage
+  KV k[kStages][TILE];
+  KV v[kStages][TILE];
+  // FP8 cache: the current stage's V widened to fp16, in the fp16 stage layout
+  half_t v16[sizeof(KV) == 1 ? TILE : 8];
 };
 
 template <int D>
@@ -133,15 +138,17 @@ __device__ int request_of_rank(const PrefillArgs& a, int rank, int* slot) {
   return *slot;
 }
 
-template <int D>
+template <int D, typename KV>
 __global__ __launch_bounds__(kThreads, 3) void prefill_kernel(const PrefillArgs a) {
+  constexpr bool kFp8 = sizeof(KV) == 1;  // E4M3 cache: codes staged, widened on reading
   constexpr int KS = D / 16;          // k-steps of S^T (16 dims each)
   constexpr int DT = D / 32;          // 32-dim tiles of O^T
-  constexpr int PIECES = D / 8;       // 16-byte pieces per token row of one head
-  constexpr int TOK_PER_INST = kWave / PIECES;                   // token rows per wave load
+  constexpr int PIECES = D * (int)sizeof(KV) / 16;  // 16-byte pieces per token row of one head
+  constexpr int TOK_PER_INST = kWave / PIECES < 8 ? kWave / PIECES : 8;  // rows per wave load
+  constexpr int LANES = TOK_PER_INST * PIECES;  // lanes of a load that move data (64 or 32)
   constexpr int INST = kBN / TOK_PER_INST / (kThreads / kWave);  // K (or V) loads per wave/stage
   static_assert(INST >= 1 && INST * TOK_PER_INST * (kThreads / kWave) == kBN, "stage split");
-  using Smem = PrefillSmem<D>;
+  using Smem = PrefillSmem<D, KV>;
   constexpr int ROW = Smem::ROW;
   extern __shared__ __align__(16) unsigned char smem_raw[];
   Smem& sm = *reinterpret_cast<Smem*>(smem_raw);
@@ -191,7 +198,7 @@ __global__ __launch_bounds__(kThreads, 3) void prefill_kernel(const PrefillArgs 
 
   const int kv_row = a.num_kv_heads * D;
   const int tok_stride = 2 * kv_row;
-  const uint64_t block_bytes = (uint64_t)kBlockSize * tok_stride * sizeof(half_t);
+  const uint64_t block_bytes = (uint64_t)kBlockSize * tok_stride * sizeof(KV);
   const char* pool = static_cast<const char*>(a.pool);
   const int32_t* bt = a.block_tables + (int64_t)r * a.max_blocks_per_seq;
   const int nblk = (S + kBlockSize - 1) / kBlockSize;
@@ -203,15 +210,16 @@ __global__ __launch_bounds__(kThreads, 3) void prefill_kernel(const PrefillArgs 
   uint32_t koff[INST], voff[INST];
 #pragma unroll
   for (int j = 0; j < INST; ++j) {
-    const int t = (w * INST + j) * TOK_PER_INST + lane / PIECES;
+    const int t = (w * INST + j) * TOK_PER_INST + (lane % LANES) / PIECES;
     const int sl = lane % PIECES;
-    koff[j] = 2u * ((t % kBlockSize) * tok_stride + kvh * D + 8 * (sl ^ kswz<D>(t)));
-    voff[j] = 2u * ((t % kBlockSize) * tok_stride + kv_row + kvh * D + 8 * (sl ^ vswz<D>(t)));
+    const int ks = kFp8 ? kswz8<D>(t) : kswz<D>(t), vs = kFp8 ? 0 : vswz<D>(t);
+    koff[j] = sizeof(KV) * ((t % kBlockSize) * tok_stride + kvh * D) + 16u * (sl ^ ks);
+    voff[j] = sizeof(KV) * ((t % kBlockSize) * tok_stride + kv_row + kvh * D) + 16u * (sl ^ vs);
   }
-  const uint32_t lds_k0 = lds_addr(&sm.k[0][0]) + 2u * (w * INST * TOK_PER_INST * ROW);
-  constexpr uint32_t kStageBytes = 2u * Smem::TILE;
+  const uint32_t lds_k0 = lds_addr(&sm.k[0][0]) + sizeof(KV) * (w * INST * TOK_PER_INST * ROW);
+  constexpr uint32_t kStageBytes = sizeof(KV) * Smem::TILE;
   constexpr uint32_t kVBytes = kStages * kStageBytes;  // from sm.k to sm.v
-  constexpr uint32_t kInstBytes = 2u * TOK_PER_INST * ROW;
+  constexpr uint32_t kInstBytes = sizeof(KV) * TOK_PER_INST * ROW;
 
   // Table entries of this wave's block in each stage, one stage per lane: register v of
   // chunk c holds, in lane L, the entry for stage 64 (kTabRegs c + v) + L. Each lane also
@@ -247,7 +255,8 @@ __global__ __launch_bounds__(kThreads, 3) void prefill_kernel(const PrefillArgs 
     const uint32_t kdst = lds_k0 + (uint32_t)ring * kStageBytes;  // ring == st % kStages
 #pragma unroll
     for (int j = 0; j < INST; ++j)
-      load_kv_lds16(block, koff[j], voff[j], kdst + j * kInstBytes, kdst + kVBytes + j * kInstBytes);
+      if (LANES == kWave || lane < LANES)  // 64-dim FP8 rows fill half a wave per load
+        load_kv_lds16(block, koff[j], voff[j], kdst + j * kInstBytes, kdst + kVBytes + j * kInstBytes);
   };
 
   const float c2 = a.scale_log2;
@@ -291,7 +300,23 @@ __global__ __launch_bounds__(kThreads, 3) void prefill_kernel(const PrefillArgs 
     else wait_vm<0>();
     lds_barrier();
     const int t0 = it * kBN;
-    if (__builtin_amdgcn_readfirstlane(t0 + kBN > S)) {
+    if constexpr (kFp8) {
+      // widen the stage's V codes to fp16 in the layout the transposing reads expect; rows
+      // past the context's end become zeros (their slots may hold anything, and 0 * NaN
+      // would reach the output). The previous stage's readers are past the barrier above.
+      for (int e = tid; e < kBN * PIECES; e += kThreads) {
+        const int t = e / PIECES, pc = e % PIECES;  // 16 codes: dims 16 pc .. 16 pc + 15
+        half8_t lo = half8_t{}, hi = half8_t{};
+        if (t0 + t < S) {
+          const u32x2_t* src = reinterpret_cast<const u32x2_t*>(&sm.v[ring][t * ROW + 16 * pc]);
+          lo = widen_fp8x8(src[0]);
+          hi = widen_fp8x8(src[1]);
+        }
+        *reinterpret_cast<half8_t*>(&sm.v16[t * ROW + 8 * ((2 * pc) ^ vswz<D>(t))]) = lo;
+        *reinterpret_cast<half8_t*>(&sm.v16[t * ROW + 8 * ((2 * pc + 1) ^ vswz<D>(t))]) = hi;
+      }
+      lds_barrier();
+    } else if (__builtin_amdgcn_readfirstlane(t0 + kBN > S)) {
       // the context's last stage: V rows past the end become zeros (their slots may hold
       // anything, and 0 * NaN would reach the output)
       keep_branch();
@@ -307,9 +332,14 @@ __global__ __launch_bounds__(kThreads, 3) void prefill_kernel(const PrefillArgs 
       // S^T for the stage's 32 tokens
       half8_t ka[KS];
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks)
-        ka[ks] = *reinterpret_cast<const half8_t*>(
-            &sm.k[ring][krow * ROW + 8 * ((2 * ks + g) ^ kswz<D>(krow))]);
+      for (int ks = 0; ks < KS; ++ks) {
+        if constexpr (kFp8)
+          ka[ks] = widen_fp8x8(*reinterpret_cast<const u32x2_t*>(
+              &sm.k[ring][krow * ROW + 16 * (ks ^ kswz8<D>(krow)) + 8 * g]));
+        else
+          ka[ks] = *reinterpret_cast<const half8_t*>(
+              &sm.k[ring][krow * ROW + 8 * ((2 * ks + g) ^ kswz<D>(krow))]);
+      }
       float16_t sacc = float16_t{};
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks)
@@ -369,8 +399,9 @@ __global__ __launch_bounds__(kThreads, 3) void prefill_kernel(const PrefillArgs 
             const int t = 16 * k + 8 * hh + vtok;
             const int dim = 32 * dt + 16 * dh + 4 * (li % 4);
             const int piece = (dim / 8) ^ vswz<D>(t);
+            const half_t* vsrc = kFp8 ? &sm.v16[0] : reinterpret_cast<const half_t*>(&sm.v[ring][0]);
             const short4_t x = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                (__attribute__((address_space(3))) short4_t*)&sm.v[ring][t * ROW + 8 * piece + (dim & 4)]);
+                (__attribute__((address_space(3))) short4_t*)(vsrc + t * ROW + 8 * piece + (dim & 4)));
             const half4_t y = __builtin_bit_cast(half4_t, x);
 #pragma unroll
             for (int e = 0; e < 4; ++e) va[k][dt][4 * hh + e] = y[e];
@@ -399,7 +430,7 @@ __global__ __launch_bounds__(kThreads, 3) void prefill_kernel(const PrefillArgs 
   const bool bad_table = __builtin_amdgcn_ballot_w64(bad_lanes) != 0;
   if (qrow >= C) return;
   half_t* out = static_cast<half_t*>(a.out) + ((int64_t)(q0 + qrow) * a.num_q_heads + h) * D;
-  const float inv = bad_table ? qnan() : 1.0f / l;
+  const float inv = bad_table ? qnan() : a.v_scale / l;
 #pragma unroll
   for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
@@ -411,12 +442,12 @@ __global__ __launch_bounds__(kThreads, 3) void prefill_kernel(const PrefillArgs 
     }
 }
 
-template <int D>
+template <int D, typename KV>
 hipError_t launch_prefill_d(const PrefillArgs& a, hipStream_t stream) {
-  const size_t smem = sizeof(PrefillSmem<D>);
+  const size_t smem = sizeof(PrefillSmem<D, KV>);
   static bool attr_set = false;  // the attribute is per function, set once per process
   if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&prefill_kernel<D>),
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&prefill_kernel<D, KV>),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
     if (e != hipSuccess) return e;
     attr_set = true;
@@ -425,15 +456,20 @@ hipError_t launch_prefill_d(const PrefillArgs& a, hipStream_t stream) {
   const int64_t tiles = (a.max_q_len + kBM - 1) / kBM;
   const int64_t wgs = (groups + kXcds - 1) / kXcds * kXcds * tiles;
   if (wgs > INT32_MAX) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((prefill_kernel<D>), dim3((unsigned)wgs), dim3(kThreads), smem, stream, a);
+  hipLaunchKernelGGL((prefill_kernel<D, KV>), dim3((unsigned)wgs), dim3(kThreads), smem, stream, a);
   return hipGetLastError();
 }
 
 }  // namespace
 
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream) {
-  if (a.head_size == 128) return launch_prefill_d<128>(a, stream);
-  if (a.head_size == 64) return launch_prefill_d<64>(a, stream);
+  if (a.kv_fp8) {
+    if (a.head_size == 128) return launch_prefill_d<128, fp8_t>(a, stream);
+    if (a.head_size == 64) return launch_prefill_d<64, fp8_t>(a, stream);
+  } else {
+    if (a.head_size == 128) return launch_prefill_d<128, half_t>(a, stream);
+    if (a.head_size == 64) return launch_prefill_d<64, half_t>(a, stream);
+  }
   return hipErrorInvalidValue;
 }
 

@@ -138,3 +138,39 @@ def test_decode_fp8_bad_rows_are_nan():
                                       dtype=torch.uint8, device="cuda"))
     got = host(out)
     assert np.isnan(got[1]).all() and np.isnan(got[2]).all() and np.isfinite(got[0]).all()
+
+
+def quantized_step_pool(inp, k_scale, v_scale):
+    """E4M3 pool of the case after this step's appends (quantized by the oracle)."""
+    pool = oracle.kv_append(inp.pool, inp.key_new, inp.value_new, inp.slot_mapping)
+    return np.concatenate([fp8.quantize(pool[:, :, 0:1], k_scale),
+                           fp8.quantize(pool[:, :, 1:2], v_scale)], axis=2)
+
+
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("G", [1, 4])
+def test_prefill_fp8_small_ragged(D, G):
+    inp = workloads.mixed_case(120 + D + G, [0, 5, 100, 700, 31], [1, 17, 64, 130, 300], [9],
+                               4 * G, 4, D)
+    ks, vs = 0.03, 0.02
+    pool = quantized_step_pool(inp, ks, vs)
+    q, bt, qsl, lens = inp.prefill_part()
+    out = torch.empty(q.shape, dtype=torch.float16, device="cuda")
+    note(f"prefill fp8 D={D} G={G}")
+    pkv.pa_prefill_chunk_fp8(out, dev(q), dev(pool), dev(bt), dev(qsl), dev(lens),
+                             int(np.diff(qsl).max()), int(lens.max()), inp.scale, ks, vs)
+    want = oracle.prefill_chunk(q, fp8.dequantize_pool(pool, ks, vs), bt, qsl, lens, inp.scale)
+    check_attention(host(out), want, f"prefill fp8 D{D} G{G}")
+
+
+def test_prefill_fp8_long_prior_sampled_rows():
+    inp = workloads.mixed_case(125, [3584, 1000], [512, 77], [], 32, 8, 128)
+    pool = quantized_step_pool(inp, 0.05, 0.04)
+    q, bt, qsl, lens = inp.prefill_part()
+    out = torch.empty(q.shape, dtype=torch.float16, device="cuda")
+    pkv.pa_prefill_chunk_fp8(out, dev(q), dev(pool), dev(bt), dev(qsl), dev(lens),
+                             int(np.diff(qsl).max()), int(lens.max()), inp.scale, 0.05, 0.04)
+    rows = np.arange(0, q.shape[0], 7)
+    want = oracle.prefill_chunk(q, fp8.dequantize_pool(pool, 0.05, 0.04), bt, qsl, lens,
+                                inp.scale, rows=set(rows.tolist()))
+    check_attention(host(out)[rows], want[rows], "prefill fp8 long prior")
