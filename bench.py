@@ -369,7 +369,7 @@ class Step:
         rec(3)
 
 
-def run_counter_sequence(inp, partition_size, kv_stream):
+def run_counter_sequence(inp, partition_size, kv_stream, kv_fp8=False):
     """Dispatches for counter passes, in a fixed order: a torch copy of 1 GiB (reads and
     writes exactly 1 GiB: the calibration of FETCH_SIZE / WRITE_SIZE), pa_stream_read of
     1 GiB (reads 1 GiB), then three steps of the workload."""
@@ -380,7 +380,7 @@ def run_counter_sequence(inp, partition_size, kv_stream):
     src = torch.ones(nbytes, dtype=torch.uint8, device="cuda")
     dst = torch.empty_like(src)
     sink = torch.zeros(pkv.pa_stream_read_sink_len(nbytes), dtype=torch.float32, device="cuda")
-    step = Step(torch, pkv, inp, partition_size, kv_stream)
+    step = Step(torch, pkv, inp, partition_size, kv_stream, kv_fp8)
     torch.cuda.synchronize()
     dst.copy_(src)
     torch.cuda.synchronize()
@@ -390,7 +390,7 @@ def run_counter_sequence(inp, partition_size, kv_stream):
         step.run()
         torch.cuda.synchronize()
     log(f"counter sequence done: copy {nbytes} B, stream_read {nbytes} B, 3 steps; "
-        f"decode algorithmic KV bytes per launch {kv_read_bytes(inp)}")
+        f"decode algorithmic KV bytes per launch {kv_read_bytes(inp, 1 if kv_fp8 else 2)}")
 
 
 def summarize_trace(path, command):
@@ -544,7 +544,7 @@ def main():
     kv_bytes = kv_unique_bytes(inp, elem_bytes) if shared else logical_bytes
 
     if args.mode == "counters":
-        run_counter_sequence(inp, args.partition_size, kv_stream)
+        run_counter_sequence(inp, args.partition_size, kv_stream, kv_fp8)
         return
 
     cpu = None
