@@ -475,8 +475,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", choices=sorted(WORKLOADS), default="c2")
     ap.add_argument("--partition-size", type=int, default=0,
-                    help="decode partition in tokens; 0 (default): 512 when the longest "
-                         "context exceeds 8192 tokens, else 256")
+                    help="decode partition in tokens; 0 (default): the library's "
+                         "pa_decode_default_partition_size for the workload")
     ap.add_argument("--kv-stream", choices=("auto", "on", "off"), default="auto",
                     help="non-temporal K/V loads in decode; auto: on unless blocks are shared")
     ap.add_argument("--launch", choices=("graph", "eager"), default="graph",
@@ -536,8 +536,10 @@ def main():
     kv_stream = {"on": True, "off": False, "auto": not shared}[args.kv_stream]
     kv_fp8 = args.kv_dtype == "fp8"
     elem_bytes = 1 if kv_fp8 else 2
-    if args.partition_size <= 0:
-        args.partition_size = 512 if int(inp.seq_lens.max()) > 8192 else 256
+    if args.partition_size <= 0:  # the library's choice for its kernels (a host-only call)
+        import paged_kv_cache_294_amd as pkv
+        args.partition_size = pkv.pa_decode_default_partition_size(
+            inp.num_q_heads, inp.num_kv_heads, int(inp.seq_lens.max()))
     # algorithmic bytes: every decode context token's K and V once; with shared prefix
     # blocks, every physical block's filled slots once (the logical count is reported too)
     logical_bytes = kv_read_bytes(inp, elem_bytes)

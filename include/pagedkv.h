@@ -96,8 +96,19 @@ int64_t pa_kv_elem_offset(int64_t slot, int32_t kv, int32_t head, int32_t dim,
  * at least 1. */
 int32_t pa_num_partitions(int32_t max_context_len, int32_t partition_size);
 
-/* Workspace bytes pa_decode needs: 0 when one partition covers max_context_len,
- * else num_seqs * num_q_heads * partitions * (head_size + 2) * 4, rounded up to 256. */
+/* A partition size for pa_decode / pa_decode_fp8 on this library's kernels (measured on
+ * MI355X). With one query head per KV head: the smallest multiple of 16 of at least 1024
+ * tokens that cuts max_context_len into at most 16 partitions, the range in which
+ * pa_decode schedules the longest partitions first. With grouped query heads: 256, or 512
+ * past 8192 tokens. -1 for a negative length or a head count that is not a multiple of
+ * num_kv_heads. */
+int32_t pa_decode_default_partition_size(int32_t num_q_heads, int32_t num_kv_heads,
+                                         int32_t max_context_len);
+
+/* Workspace bytes pa_decode needs: 0 when one partition covers max_context_len, else the
+ * partial results, num_seqs * num_q_heads * partitions * (head_size + 2) * 4 bytes, plus
+ * an item list of 4 * (1 + num_seqs * partitions) bytes (the order in which partitions
+ * are scheduled), each part rounded up to 256 bytes. */
 int64_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads,
                                   int32_t max_context_len, int32_t partition_size,
                                   int32_t head_size);

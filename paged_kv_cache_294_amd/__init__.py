@@ -32,6 +32,7 @@ from ._lib import (  # noqa: F401
     pa_move_blocks,
     pa_num_blocks_fit,
     pa_num_partitions,
+    pa_decode_default_partition_size,
     pa_pool_bytes,
     pa_prefill_chunk,
     pa_prefill_chunk_fp8,

@@ -36,6 +36,7 @@ SIGNATURES = {
     "pa_slot": (_i64, [ctypes.POINTER(_i32), _i64, _i32]),
     "pa_kv_elem_offset": (_i64, [_i64, _i32, _i32, _i32, _i32, _i32]),
     "pa_num_partitions": (_i32, [_i32, _i32]),
+    "pa_decode_default_partition_size": (_i32, [_i32, _i32, _i32]),
     "pa_decode_workspace_bytes": (_i64, [_i32, _i32, _i32, _i32, _i32]),
     "pa_kv_append": (ctypes.c_int, [_vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i64, _i64, _i64, _vp]),
     "pa_decode": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _i64,
@@ -185,6 +186,11 @@ def pa_kv_elem_offset(slot: int, kv: int, head: int, dim: int, num_kv_heads: int
 
 def pa_num_partitions(max_context_len: int, partition_size: int) -> int:
     return load().pa_num_partitions(max_context_len, partition_size)
+
+
+def pa_decode_default_partition_size(num_q_heads: int, num_kv_heads: int,
+                                     max_context_len: int) -> int:
+    return load().pa_decode_default_partition_size(num_q_heads, num_kv_heads, max_context_len)
 
 
 def pa_decode_workspace_bytes(num_seqs: int, num_q_heads: int, max_context_len: int,

@@ -115,6 +115,16 @@ PA_EXPORT int32_t pa_num_partitions(int32_t max_context_len, int32_t partition_s
   return p < 1 ? 1 : p;
 }
 
+PA_EXPORT int32_t pa_decode_default_partition_size(int32_t num_q_heads, int32_t num_kv_heads,
+                                                   int32_t max_context_len) {
+  if (max_context_len < 0 || num_kv_heads <= 0 || num_q_heads <= 0 || num_q_heads % num_kv_heads)
+    return -1;
+  if (num_q_heads != num_kv_heads) return max_context_len > 8192 ? 512 : 256;
+  const int64_t blocks = ((int64_t)max_context_len + kBlock - 1) / kBlock;  // = tokens / 16, rounded up
+  const int64_t ps = (blocks + 15) / 16 * 16;  // 16 partitions of ps tokens cover the context
+  return (int32_t)std::min<int64_t>(std::max<int64_t>(ps, 1024), INT32_MAX / kBlock * kBlock);
+}
+
 PA_EXPORT int64_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads,
                                             int32_t max_context_len, int32_t partition_size,
                                             int32_t head_size) {
@@ -126,6 +136,8 @@ PA_EXPORT int64_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_head
   int64_t bytes = rows * head_size * 4;  // o
   bytes = (bytes + 255) / 256 * 256;
   bytes += rows * 2 * 4;                 // (m, l)
+  bytes = (bytes + 255) / 256 * 256;
+  bytes += 4 * (1 + (int64_t)num_seqs * p);  // item list of the largest-first order
   return (bytes + 255) / 256 * 256;
 }
 
@@ -274,6 +286,10 @@ pa_status decode_impl(void* out, const void* q, const void* kv_pool, const int32
     const int64_t o_bytes = (rows * head_size * 4 + 255) / 256 * 256;
     a.ws_o = static_cast<float*>(workspace);
     a.ws_ml = reinterpret_cast<float*>(static_cast<char*>(workspace) + o_bytes);
+    if (!cascade) {  // tail of the plain layout: the item list of the largest-first order
+      const int64_t ml_bytes = (rows * 2 * 4 + 255) / 256 * 256;
+      a.ws_items = reinterpret_cast<int*>(static_cast<char*>(workspace) + o_bytes + ml_bytes);
+    }
   }
   if (cascade) return hip_status(pkv::launch_decode_shared_prefix(a, (hipStream_t)stream));
   return hip_status(pkv::launch_decode(a, (hipStream_t)stream));

@@ -20,10 +20,10 @@
 // accumulator over the tokens it sees (online softmax); the rows are merged once at the
 // end of the partition. Scores use exp2 with the scale pre-multiplied by log2(e).
 //
-// FP8 cache. With an E4M3 pool (one byte per element) each lane loads 8 codes instead of
-// 8 fp16 values and widens them exactly to fp16 (v_cvt_scalef32_pk_f16_fp8); the key
-// scale is folded into the softmax scale and the value scale into the final 1 / l, so the
-// arithmetic after the load is the fp16 cache's.
+// FP8 cache. With an E4M3 pool (one byte per element) each lane loads 16 codes (16 bytes,
+// as it loads 8 fp16 values) and widens them exactly to fp16 (v_cvt_scalef32_pk_f16_fp8);
+// the key scale is folded into the softmax scale and the value scale into the final 1 / l,
+// so the arithmetic after the load is the fp16 cache's.
 //
 // Output. A sequence with one partition writes its fp16 row directly. Otherwise every
 // partition writes (m, l, o = acc / l) to the workspace and the reduce kernel merges
@@ -119,157 +119,74 @@ __device__ __forceinline__ void write_const_rows(const DecodeArgs& a, int b, int
   }
 }
 
-template <int D, int G, bool Stream, typename KV>
-__global__ __launch_bounds__(kThreads) void decode_partition_kernel(const DecodeArgs a) {
-  constexpr int EPL = 16 / sizeof(KV);  // elements per lane and load
-  constexpr int NV = EPL / 8;           // fp16 vectors per lane
-  using Gm = Geo<D, EPL>;
-  constexpr int LPT = Gm::kLanesPerToken;
-  constexpr int TPL = Gm::kTokensPerLoad;
-  constexpr int LPB = Gm::kLoadsPerBlock;
-
-  const int lane = threadIdx.x & (kWave - 1);
-  const DecodeItem item = decode_item(a, a.num_seqs, a.num_partitions, blockIdx.x);
-  if (!item.valid) return;
-  const int kvh = item.hg * kWavesPerGroup + (threadIdx.x >> 6);
-  const int p = item.p;
-  const int b = item.b;
-  if (kvh >= a.num_kv_heads) return;
-  const int row = lane / LPT;
-  const int col = lane % LPT;
-
-  const int L = a.context_lens[b];
-  const bool bad_len = L < 0 || L > a.max_context_len || L > a.max_blocks_per_seq * kBlockSize;
-  if (bad_len || L == 0) {
-    if (p == 0 && row == 0) write_const_rows<D, G, EPL>(a, b, kvh, col, bad_len ? qnan() : 0.0f);
-    return;
-  }
-  const int part_tokens = a.partition_blocks * kBlockSize;
-  const int nparts = (L + part_tokens - 1) / part_tokens;
-  if (p >= nparts) return;
-  const int blk_begin = p * a.partition_blocks;
-  const int blk_end = min(blk_begin + a.partition_blocks, (L + kBlockSize - 1) / kBlockSize);
-
-  const half_t* qp = static_cast<const half_t*>(a.q);
-  half8_t qv[G][NV];
+// One block of the MHA kernel: scores of the LPB tokens lane row `row` sees (for each of the
+// G query heads), masked past the context length L, folded into the row's online softmax.
+template <int D, int G, int EPL, int LPT, int TPL, int LPB, int NV>
+__device__ __forceinline__ void consume_block(const half8_t (&qv)[G][NV], const half8_t (&kc)[LPB][NV],
+                                              half8_t (&vc)[LPB][NV], int tok0, int L, int row,
+                                              float scale_log2, float (&m)[G], float (&l)[G],
+                                              float (&acc)[G][EPL]) {
+  float s[G][LPB];
 #pragma unroll
-  for (int g = 0; g < G; ++g)
-#pragma unroll
-    for (int u = 0; u < NV; ++u)
-      qv[g][u] = *reinterpret_cast<const half8_t*>(
-          qp + ((int64_t)b * a.num_q_heads + (int64_t)kvh * G + g) * D + col * EPL + 8 * u);
-
-  const int kv_row = a.num_kv_heads * D;  // elements of one K (or V) row over all heads
-  const int tok_stride = 2 * kv_row;       // elements between consecutive tokens of a block
-  const int64_t block_elems = (int64_t)kBlockSize * tok_stride;
-  // element offset of this lane's piece of load i inside a block: + i * TPL * tok_stride
-  const int lane_off = row * tok_stride + kvh * D + col * EPL;
-  const KV* pool = static_cast<const KV*>(a.pool);
-  const int32_t* bt = a.block_tables + (int64_t)b * a.max_blocks_per_seq;
-
-  float m[G], l[G], acc[G][EPL];
-#pragma unroll
-  for (int g = 0; g < G; ++g) {
-    m[g] = neg_inf();
-    l[g] = 0.0f;
-#pragma unroll
-    for (int d = 0; d < EPL; ++d) acc[g][d] = 0.0f;
-  }
-
-  // Block-table entries of the partition, one per lane, fetched 64 at a time.
-  int bt_vec = (lane < blk_end - blk_begin) ? bt[blk_begin + lane] : 0;
-  bool bad_table = false;
-
-  half8_t kc[LPB][NV], vc[LPB][NV];
-  {
-    const int phys = __builtin_amdgcn_readfirstlane(bt_vec);
-    bad_table = phys < 0 || phys >= a.num_blocks;
-    const KV* base = pool + (bad_table ? 0 : (int64_t)phys * block_elems) + lane_off;
-#pragma unroll
-    for (int i = 0; i < LPB; ++i) {
-      load_row_piece<KV, Stream>(base + i * TPL * tok_stride, kc[i]);
-      load_row_piece<KV, Stream>(base + i * TPL * tok_stride + kv_row, vc[i]);
-    }
-  }
-
-  for (int j = blk_begin; j < blk_end && !bad_table; ++j) {
-    // prefetch block j+1 while block j is consumed
-    half8_t kn[LPB][NV], vn[LPB][NV];
-    const int jn = j + 1;
-    if (jn < blk_end) {
-      const int k64 = (jn - blk_begin) & 63;
-      if (k64 == 0) bt_vec = (lane < blk_end - jn) ? bt[jn + lane] : 0;
-      const int phys = __builtin_amdgcn_readlane(bt_vec, k64);
-      bad_table = phys < 0 || phys >= a.num_blocks;
-      const KV* base = pool + (bad_table ? 0 : (int64_t)phys * block_elems) + lane_off;
-#pragma unroll
-      for (int i = 0; i < LPB; ++i) {
-        load_row_piece<KV, Stream>(base + i * TPL * tok_stride, kn[i]);
-        load_row_piece<KV, Stream>(base + i * TPL * tok_stride + kv_row, vn[i]);
-      }
-    }
-
-    // scores of the LPB tokens this lane's row sees in block j, for each query head
-    float s[G][LPB];
-#pragma unroll
-    for (int i = 0; i < LPB; ++i)
-#pragma unroll
-      for (int g = 0; g < G; ++g) {
-        float dot = 0.0f;
-#pragma unroll
-        for (int u = 0; u < NV; ++u) dot = dot8(qv[g][u], kc[i][u], dot);
-        s[g][i] = group_sum<LPT>(dot) * a.scale_log2;
-      }
-
-    const int tok0 = j * kBlockSize;
-    if (tok0 + kBlockSize > L) {  // the sequence's last, partly filled block
-#pragma unroll
-      for (int i = 0; i < LPB; ++i) {
-        if (tok0 + i * TPL + row >= L) {
-#pragma unroll
-          for (int g = 0; g < G; ++g) s[g][i] = neg_inf();
-#pragma unroll
-          for (int u = 0; u < NV; ++u) vc[i][u] = half8_t{};
-        }
-      }
-    }
-
+  for (int i = 0; i < LPB; ++i)
 #pragma unroll
     for (int g = 0; g < G; ++g) {
-      float mx = m[g];
+      float dot = 0.0f;
 #pragma unroll
-      for (int i = 0; i < LPB; ++i) mx = fmaxf(mx, s[g][i]);
-      const float base = (mx == neg_inf()) ? 0.0f : mx;
-      const float alpha = fast_exp2(m[g] - base);
-      float pr[LPB], psum = 0.0f;
-#pragma unroll
-      for (int i = 0; i < LPB; ++i) {
-        pr[i] = fast_exp2(s[g][i] - base);
-        psum += pr[i];
-      }
-      l[g] = l[g] * alpha + psum;
-#pragma unroll
-      for (int d = 0; d < EPL; ++d) {
-        float x = acc[g][d] * alpha;
-#pragma unroll
-        for (int i = 0; i < LPB; ++i) x = fmaf(pr[i], (float)vc[i][d / 8][d % 8], x);
-        acc[g][d] = x;
-      }
-      m[g] = mx;
+      for (int u = 0; u < NV; ++u) dot = dot8(qv[g][u], kc[i][u], dot);
+      s[g][i] = group_sum<LPT>(dot) * scale_log2;
     }
 
+  if (tok0 + kBlockSize > L) {  // the sequence's last, partly filled block
 #pragma unroll
-    for (int i = 0; i < LPB; ++i)
+    for (int i = 0; i < LPB; ++i) {
+      if (tok0 + i * TPL + row >= L) {
 #pragma unroll
-      for (int u = 0; u < NV; ++u) {
-        kc[i][u] = kn[i][u];
-        vc[i][u] = vn[i][u];
+        for (int g = 0; g < G; ++g) s[g][i] = neg_inf();
+#pragma unroll
+        for (int u = 0; u < NV; ++u) vc[i][u] = half8_t{};
       }
+    }
   }
 
+#pragma unroll
+  for (int g = 0; g < G; ++g) {
+    float mx = m[g];
+#pragma unroll
+    for (int i = 0; i < LPB; ++i) mx = fmaxf(mx, s[g][i]);
+    const float base = (mx == neg_inf()) ? 0.0f : mx;
+    const float alpha = fast_exp2(m[g] - base);
+    float pr[LPB], psum = 0.0f;
+#pragma unroll
+    for (int i = 0; i < LPB; ++i) {
+      pr[i] = fast_exp2(s[g][i] - base);
+      psum += pr[i];
+    }
+    l[g] = l[g] * alpha + psum;
+#pragma unroll
+    for (int d = 0; d < EPL; ++d) {
+      float x = acc[g][d] * alpha;
+#pragma unroll
+      for (int i = 0; i < LPB; ++i) x = fmaf(pr[i], (float)vc[i][d / 8][d % 8], x);
+      acc[g][d] = x;
+    }
+    m[g] = mx;
+  }
+}
+
+// End of one (sequence b, KV head kvh, partition p) of the MHA kernel. A table entry outside
+// the pool (bad_table) makes the whole output row NaN: with one partition here, with
+// several through a NaN partial that the reduce kernel propagates. Otherwise the lane
+// rows' running states are merged (M = max m_r, sums and accumulators rescaled to M) and
+// written: the fp16 row when the sequence has one partition, else (m, l, o) to the
+// workspace.
+template <int D, int G, int EPL, int LPT>
+__device__ __forceinline__ void finish_partition(const DecodeArgs& a, int b, int kvh, int p,
+                                                 int nparts, int row, int col, bool bad_table,
+                                                 float (&m)[G], float (&l)[G],
+                                                 float (&acc)[G][EPL]) {
+  constexpr int NV = EPL / 8;
   if (bad_table) {
-    // A table entry outside the pool: the whole output row becomes NaN. With several
-    // partitions the reduce kernel writes the row, so poison this partition's partial.
     if (row == 0) {
       if (nparts == 1) {
         write_const_rows<D, G, EPL>(a, b, kvh, col, qnan());
@@ -285,8 +202,6 @@ __global__ __launch_bounds__(kThreads) void decode_partition_kernel(const Decode
     }
     return;
   }
-
-  // merge the rows' running states: M = max m_r, sum and accumulator rescaled to M
 #pragma unroll
   for (int g = 0; g < G; ++g) {
     float M = m[g];
@@ -331,6 +246,193 @@ __global__ __launch_bounds__(kThreads) void decode_partition_kernel(const Decode
         }
       }
     }
+  }
+}
+
+template <int D, int G, bool Stream, typename KV>
+__global__ __launch_bounds__(kThreads) void decode_partition_kernel(const DecodeArgs a,
+                                                                    const int* __restrict__ items) {
+  constexpr int EPL = 16 / sizeof(KV);  // elements per lane and load
+  constexpr int NV = EPL / 8;           // fp16 vectors per lane
+  using Gm = Geo<D, EPL>;
+  constexpr int LPT = Gm::kLanesPerToken;
+  constexpr int TPL = Gm::kTokensPerLoad;
+  constexpr int LPB = Gm::kLoadsPerBlock;
+
+  const int lane = threadIdx.x & (kWave - 1);
+  DecodeItem item;
+  if (items != nullptr) {  // largest-first list: item blockIdx / groups, KV-head group blockIdx % groups
+    const int groups = (a.num_kv_heads + kWavesPerGroup - 1) / kWavesPerGroup;
+    const int idx = blockIdx.x / groups;
+    if (idx >= items[0]) return;
+    const unsigned key = (unsigned)items[1 + idx];
+    item.hg = blockIdx.x % groups;
+    item.b = (int)(key >> 16);
+    item.p = (int)(key & 0xffffu);
+  } else {
+    item = decode_item(a, a.num_seqs, a.num_partitions, blockIdx.x);
+    if (!item.valid) return;
+  }
+  const int kvh = item.hg * kWavesPerGroup + (threadIdx.x >> 6);
+  const int p = item.p;
+  const int b = item.b;
+  if (kvh >= a.num_kv_heads) return;
+  const int row = lane / LPT;
+  const int col = lane % LPT;
+  // the partition's block-table entries, one per lane (64 at a time), are requested before
+  // the context length arrives: the table row holds max_blocks_per_seq entries either way
+  const int32_t* bt = a.block_tables + (int64_t)b * a.max_blocks_per_seq;
+  const int first = p * a.partition_blocks;
+  int bt_vec = (first + lane < a.max_blocks_per_seq) ? bt[first + lane] : 0;
+
+  const int L = a.context_lens[b];
+  const bool bad_len = L < 0 || L > a.max_context_len || L > a.max_blocks_per_seq * kBlockSize;
+  if (bad_len || L == 0) {
+    if (p == 0 && row == 0) write_const_rows<D, G, EPL>(a, b, kvh, col, bad_len ? qnan() : 0.0f);
+    return;
+  }
+  const int part_tokens = a.partition_blocks * kBlockSize;
+  const int nparts = (L + part_tokens - 1) / part_tokens;
+  if (p >= nparts) return;
+  const int blk_begin = p * a.partition_blocks;
+  const int blk_end = min(blk_begin + a.partition_blocks, (L + kBlockSize - 1) / kBlockSize);
+
+  const half_t* qp = static_cast<const half_t*>(a.q);
+  half8_t qv[G][NV];
+#pragma unroll
+  for (int g = 0; g < G; ++g)
+#pragma unroll
+    for (int u = 0; u < NV; ++u)
+      qv[g][u] = *reinterpret_cast<const half8_t*>(
+          qp + ((int64_t)b * a.num_q_heads + (int64_t)kvh * G + g) * D + col * EPL + 8 * u);
+
+  const int kv_row = a.num_kv_heads * D;  // elements of one K (or V) row over all heads
+  const int tok_stride = 2 * kv_row;       // elements between consecutive tokens of a block
+  const int64_t block_elems = (int64_t)kBlockSize * tok_stride;
+  // element offset of this lane's piece of load i inside a block: + i * TPL * tok_stride
+  const int lane_off = row * tok_stride + kvh * D + col * EPL;
+  const KV* pool = static_cast<const KV*>(a.pool);
+
+  float m[G], l[G], acc[G][EPL];
+#pragma unroll
+  for (int g = 0; g < G; ++g) {
+    m[g] = neg_inf();
+    l[g] = 0.0f;
+#pragma unroll
+    for (int d = 0; d < EPL; ++d) acc[g][d] = 0.0f;
+  }
+
+  bool bad_table = false;
+
+  half8_t kc[LPB][NV], vc[LPB][NV];
+  {
+    const int phys = __builtin_amdgcn_readfirstlane(bt_vec);
+    bad_table = phys < 0 || phys >= a.num_blocks;
+    const KV* base = pool + (bad_table ? 0 : (int64_t)phys * block_elems) + lane_off;
+#pragma unroll
+    for (int i = 0; i < LPB; ++i) {
+      load_row_piece<KV, Stream>(base + i * TPL * tok_stride, kc[i]);
+      load_row_piece<KV, Stream>(base + i * TPL * tok_stride + kv_row, vc[i]);
+    }
+  }
+
+  for (int j = blk_begin; j < blk_end && !bad_table; ++j) {
+    // prefetch block j+1 while block j is consumed
+    half8_t kn[LPB][NV], vn[LPB][NV];
+    const int jn = j + 1;
+    if (jn < blk_end) {
+      const int k64 = (jn - blk_begin) & 63;
+      if (k64 == 0) bt_vec = (lane < blk_end - jn) ? bt[jn + lane] : 0;
+      const int phys = __builtin_amdgcn_readlane(bt_vec, k64);
+      bad_table = phys < 0 || phys >= a.num_blocks;
+      const KV* base = pool + (bad_table ? 0 : (int64_t)phys * block_elems) + lane_off;
+#pragma unroll
+      for (int i = 0; i < LPB; ++i) {
+        load_row_piece<KV, Stream>(base + i * TPL * tok_stride, kn[i]);
+        load_row_piece<KV, Stream>(base + i * TPL * tok_stride + kv_row, vn[i]);
+      }
+    }
+
+    consume_block<D, G, EPL, LPT, TPL, LPB, NV>(qv, kc, vc, j * kBlockSize, L, row, a.scale_log2,
+                                                m, l, acc);
+
+#pragma unroll
+    for (int i = 0; i < LPB; ++i)
+#pragma unroll
+      for (int u = 0; u < NV; ++u) {
+        kc[i][u] = kn[i][u];
+        vc[i][u] = vn[i][u];
+      }
+  }
+
+  finish_partition<D, G, EPL, LPT>(a, b, kvh, p, nparts, row, col, bad_table, m, l, acc);
+}
+
+// ---- largest-first order ----------------------------------------------------------------
+// With several partitions per sequence the work is ragged: every sequence's last partition
+// is partly filled, and identical partitions take very different times under full load.
+// The hardware starts workgroups in launch order as slots free up, so when the partly
+// filled partitions are a sizeable share of the items (at most kOrderMaxParts partitions
+// per sequence), a one-workgroup pre-pass lists the (sequence, partition) items by
+// decreasing length and the partition kernel takes them in that order: the long items run
+// first and the short ones fill the end.
+constexpr int kOrderMaxParts = 16;
+constexpr int kOrderThreads = 1024;
+constexpr int kOrderBuckets = 1025;  // bucket 1024 - min(size in blocks, 1024)
+
+// items[0] = number of (sequence, partition) items, items[1 + i] = (b << 16) | p, longest
+// first; a sequence of length 0 or out of range has one item (p = 0) that writes its rows.
+__device__ __forceinline__ int order_bucket(const DecodeArgs& a, int b, int p) {
+  const int L = a.context_lens[b];
+  const bool bad = L < 0 || L > a.max_context_len || L > a.max_blocks_per_seq * kBlockSize;
+  if (bad || L == 0) return p == 0 ? kOrderBuckets - 1 : -1;  // one item writes the row
+  const int size = (L + kBlockSize - 1) / kBlockSize - p * a.partition_blocks;
+  if (size <= 0) return -1;
+  return 1024 - min(min(size, a.partition_blocks), 1024);
+}
+
+__global__ __launch_bounds__(kOrderThreads) void order_items_kernel(const DecodeArgs a,
+                                                                    int* __restrict__ items) {
+  __shared__ int hist[kOrderBuckets];
+  __shared__ int wsum[kOrderThreads / kWave];
+  const int tid = threadIdx.x;
+  for (int i = tid; i < kOrderBuckets; i += kOrderThreads) hist[i] = 0;
+  __syncthreads();
+  const int np = a.num_partitions;
+  const int64_t pairs = (int64_t)a.num_seqs * np;
+  for (int64_t i = tid; i < pairs; i += kOrderThreads) {
+    const int bk = order_bucket(a, (int)(i / np), (int)(i % np));
+    if (bk >= 0) atomicAdd(&hist[bk], 1);
+  }
+  __syncthreads();
+  // exclusive prefix sum of buckets 0 .. 1023 (one per thread); bucket 1024 comes last
+  const int lane = tid & (kWave - 1), w = tid / kWave;
+  const int v = hist[tid];
+  int x = v;
+#pragma unroll
+  for (int o = 1; o < kWave; o <<= 1) {
+    const int y = __shfl_up(x, o, kWave);
+    if (lane >= o) x += y;
+  }
+  if (lane == kWave - 1) wsum[w] = x;
+  __syncthreads();
+  int before = 0, all = 0;
+  for (int k = 0; k < kOrderThreads / kWave; ++k) {
+    if (k < w) before += wsum[k];
+    all += wsum[k];
+  }
+  const int last = hist[kOrderBuckets - 1];
+  __syncthreads();
+  hist[tid] = before + x - v;
+  if (tid == 0) {
+    hist[kOrderBuckets - 1] = all;
+    items[0] = all + last;
+  }
+  __syncthreads();
+  for (int64_t i = tid; i < pairs; i += kOrderThreads) {
+    const int b = (int)(i / np), p = (int)(i % np);
+    const int bk = order_bucket(a, b, p);
+    if (bk >= 0) items[1 + atomicAdd(&hist[bk], 1)] = (int)(((unsigned)b << 16) | (unsigned)p);
   }
 }
 
@@ -673,10 +775,21 @@ hipError_t launch_decode_dg(const DecodeArgs& a, hipStream_t stream) {
   if (wgs > INT32_MAX) return hipErrorInvalidValue;
   const dim3 grid((unsigned)wgs);
   if constexpr (G == 1) {  // one query head per KV head: vector ALUs
+    const int* items = nullptr;
+    dim3 pgrid = grid;
+    if (a.num_partitions > 1 && a.num_partitions <= kOrderMaxParts && a.ws_items != nullptr) {
+      const int64_t owgs = (int64_t)a.num_seqs * a.num_partitions * groups;
+      if (owgs > INT32_MAX) return hipErrorInvalidValue;
+      hipLaunchKernelGGL(order_items_kernel, dim3(1), dim3(kOrderThreads), 0, stream, a, a.ws_items);
+      const hipError_t e = hipGetLastError();
+      if (e != hipSuccess) return e;
+      items = a.ws_items;
+      pgrid = dim3((unsigned)owgs);
+    }
     if (a.stream_kv)
-      hipLaunchKernelGGL((decode_partition_kernel<D, 1, true, KV>), grid, dim3(kThreads), 0, stream, a);
+      hipLaunchKernelGGL((decode_partition_kernel<D, 1, true, KV>), pgrid, dim3(kThreads), 0, stream, a, items);
     else
-      hipLaunchKernelGGL((decode_partition_kernel<D, 1, false, KV>), grid, dim3(kThreads), 0, stream, a);
+      hipLaunchKernelGGL((decode_partition_kernel<D, 1, false, KV>), pgrid, dim3(kThreads), 0, stream, a, items);
   } else {  // a query-head group per KV head: matrix cores
     if (a.stream_kv)
       hipLaunchKernelGGL((decode_gqa_kernel<D, G, true, KV>), grid, dim3(kThreads), 0, stream, a);

@@ -23,6 +23,7 @@ struct DecodeArgs {
   const int32_t* context_lens;
   float* ws_o;   // [B][Hq][P][D] fp32, or null when P == 1
   float* ws_ml;  // [B][Hq][P][2] fp32 (max in log2 units, sum), or null when P == 1
+  int* ws_items;  // plain decode with P > 1: (sequence, partition) items, largest first
   int num_seqs, num_q_heads, num_kv_heads, head_size;
   int max_blocks_per_seq;
   int64_t num_blocks;

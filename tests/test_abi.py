@@ -100,7 +100,10 @@ def test_partitions_and_workspace(lib):
     assert pkv.pa_decode_workspace_bytes(8, 32, 512, 512, 128) == 0
     rows = 8 * 32 * 64
     o = (rows * 128 * 4 + 255) // 256 * 256
-    assert pkv.pa_decode_workspace_bytes(8, 32, 32768, 512, 128) == (o + rows * 8 + 255) // 256 * 256
+    ml = (rows * 8 + 255) // 256 * 256
+    # partials (o, then m and l), then the item list of the largest-first order (1 + 8 * 64 ints)
+    want = (o + ml + 4 * (1 + 8 * 64) + 255) // 256 * 256
+    assert pkv.pa_decode_workspace_bytes(8, 32, 32768, 512, 128) == want
 
 
 # ---------------------------------------------------------------------------------------
@@ -209,3 +212,19 @@ def test_fp8_calls_reject_bad_scales(lib):
                              1.0, 512, 0, 0, 0, None) == pkv.PA_ERR_UNSUPPORTED
     assert lib.pa_decode_fp8(FAKE, FAKE, FAKE, FAKE, FAKE, 0, 4, 4, 64, 16, 4, 16, 64, 0.125, 1.0,
                              1.0, 512, 0, 0, 0, None) == pkv.PA_OK
+
+
+def test_default_partition_size(lib):
+    f = pkv.pa_decode_default_partition_size
+    # one query head per KV head: at least 1024 tokens, at most 16 partitions
+    assert f(32, 32, 0) == 1024
+    assert f(32, 32, 2048) == 1024
+    assert f(32, 32, 16384) == 1024 and pkv.pa_num_partitions(16384, 1024) == 16
+    assert f(32, 32, 16385) == 1040
+    assert f(32, 32, 32768) == 2048
+    for L in (1, 5000, 20000, 100000, 1 << 20):
+        ps = f(32, 32, L)
+        assert ps % 16 == 0 and ps >= 1024 and pkv.pa_num_partitions(L, ps) <= 16
+    # grouped query heads
+    assert f(32, 8, 4096) == 256 and f(32, 8, 8193) == 512
+    assert f(32, 32, -1) == -1 and f(12, 8, 100) == -1
