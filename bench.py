@@ -476,7 +476,8 @@ def main():
     ap.add_argument("--workload", choices=sorted(WORKLOADS), default="c2")
     ap.add_argument("--partition-size", type=int, default=0,
                     help="decode partition in tokens; 0 (default): the library's "
-                         "pa_decode_default_partition_size for the workload")
+                         "pa_decode_default_partition_size for the workload (512 for "
+                         "shared-prefix decode)")
     ap.add_argument("--kv-stream", choices=("auto", "on", "off"), default="auto",
                     help="non-temporal K/V loads in decode; auto: on unless blocks are shared")
     ap.add_argument("--launch", choices=("graph", "eager"), default="graph",
@@ -536,10 +537,18 @@ def main():
     kv_stream = {"on": True, "off": False, "auto": not shared}[args.kv_stream]
     kv_fp8 = args.kv_dtype == "fp8"
     elem_bytes = 1 if kv_fp8 else 2
-    if args.partition_size <= 0:  # the library's choice for its kernels (a host-only call)
+    shared_prefix = {"plain": False, "shared-prefix": True,
+                     "auto": bool(inp.prefix_blocks) and not kv_fp8}[args.decode]
+    if shared_prefix and (kv_fp8 or not inp.prefix_blocks):
+        print("--decode shared-prefix needs prompt groups and an fp16 cache", file=sys.stderr)
+        sys.exit(2)
+    if args.partition_size <= 0 and shared_prefix:
+        args.partition_size = 512  # fastest of 256 .. 2048 for 64 groups of 1024-token prompts
+    elif args.partition_size <= 0:  # the library's choice for its kernels (a host-only call)
         import paged_kv_cache_294_amd as pkv
         args.partition_size = pkv.pa_decode_default_partition_size(
-            inp.num_q_heads, inp.num_kv_heads, int(inp.seq_lens.max()))
+            inp.num_seqs - inp.num_prefill, inp.num_q_heads, inp.num_kv_heads,
+            int(inp.seq_lens.max()))
     # algorithmic bytes: every decode context token's K and V once; with shared prefix
     # blocks, every physical block's filled slots once (the logical count is reported too)
     logical_bytes = kv_read_bytes(inp, elem_bytes)
@@ -576,11 +585,6 @@ def main():
         log(f"host block manager: admit {bm['admit_us']:.0f} us, step {bm['step_us']:.0f} us "
             f"({bm['new_tokens']} slots + tables)")
     log("copying the batch to the GPU")
-    shared_prefix = {"plain": False, "shared-prefix": True,
-                     "auto": bool(inp.prefix_blocks) and not kv_fp8}[args.decode]
-    if shared_prefix and (kv_fp8 or not inp.prefix_blocks):
-        print("--decode shared-prefix needs prompt groups and an fp16 cache", file=sys.stderr)
-        sys.exit(2)
     step = Step(torch, pkv, inp, args.partition_size, kv_stream, kv_fp8, shared_prefix)
     for _ in range(args.warmup):
         step.run()
@@ -680,9 +684,10 @@ def main():
         "roofline": {
             "kernel": ("pa_decode_shared_prefix (prefix, own-token and log-sum-exp reduce kernels)"
                        if shared_prefix else
-                       ("pa_decode_fp8" if kv_fp8 else "pa_decode") +
-                       (" (partition + log-sum-exp reduce kernels)" if nparts > 1
-                        else " (partition kernel)")),
+                       ("pa_decode_fp8" if kv_fp8 else "pa_decode") + " (" +
+                       ("longest-first order pre-pass + " if kv_stream and nparts <= 16 else "") +
+                       ("partition + log-sum-exp reduce kernels)" if nparts > 1
+                        else "partition kernel)")),
             "bound": "hbm",
             "achieved": achieved,
             "peak": HBM_PEAK_GBPS,

@@ -97,18 +97,23 @@ int64_t pa_kv_elem_offset(int64_t slot, int32_t kv, int32_t head, int32_t dim,
 int32_t pa_num_partitions(int32_t max_context_len, int32_t partition_size);
 
 /* A partition size for pa_decode / pa_decode_fp8 on this library's kernels (measured on
- * MI355X). With one query head per KV head: the smallest multiple of 16 of at least 1024
- * tokens that cuts max_context_len into at most 16 partitions, the range in which
- * pa_decode schedules the longest partitions first. With grouped query heads: 256, or 512
- * past 8192 tokens. -1 for a negative length or a head count that is not a multiple of
- * num_kv_heads. */
-int32_t pa_decode_default_partition_size(int32_t num_q_heads, int32_t num_kv_heads,
-                                         int32_t max_context_len);
+ * MI355X): as few partitions as keep the GPU busy. A wave serves one (sequence, KV head,
+ * partition), so P = ceil(W / (num_seqs * num_kv_heads)) partitions with W = 4096 waves
+ * (one query head per KV head) or 2048 (grouped query heads, a kernel that holds fewer
+ * waves per SIMD); the size is ceil(max_context_len / P) rounded up to a multiple of 16,
+ * and at least 512 tokens when P > 16 (up to 16 partitions pa_decode schedules the
+ * longest first). -1 for a negative length or count, or a head count that is not a
+ * multiple of num_kv_heads. */
+int32_t pa_decode_default_partition_size(int32_t num_seqs, int32_t num_q_heads,
+                                         int32_t num_kv_heads, int32_t max_context_len);
 
-/* Workspace bytes pa_decode needs: 0 when one partition covers max_context_len, else the
- * partial results, num_seqs * num_q_heads * partitions * (head_size + 2) * 4 bytes, plus
- * an item list of 4 * (1 + num_seqs * partitions) bytes (the order in which partitions
- * are scheduled), each part rounded up to 256 bytes. */
+/* Workspace bytes pa_decode uses. With several partitions: the partial results,
+ * num_seqs * num_q_heads * partitions * (head_size + 2) * 4 bytes, plus an item list of
+ * 4 * (1 + num_seqs * partitions) bytes (the order in which partitions are scheduled),
+ * each part rounded up to 256 bytes; pa_decode requires them. With one partition: the
+ * item list alone, 4 * (1 + num_seqs) bytes rounded up to 256; optional (pa_decode then
+ * accepts a NULL or smaller workspace and runs the sequences in launch order, with the
+ * same results). */
 int64_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads,
                                   int32_t max_context_len, int32_t partition_size,
                                   int32_t head_size);
@@ -154,11 +159,14 @@ pa_status pa_kv_append(void* kv_pool, const void* key, const void* value,
  *                 block_size; a context longer than one partition is computed as
  *                 partitions merged by a log-sum-exp reduction
  *   workspace     device memory of at least pa_decode_workspace_bytes(...) bytes,
- *                 256-byte aligned (may be NULL when that size is 0); scratch only
+ *                 256-byte aligned (may be NULL when one partition covers
+ *                 max_context_len); scratch only
  *   flags         0 or PA_DECODE_KV_STREAM: every block is read by one sequence only in
  *                 this call, so K/V loads carry the non-temporal cache hint (HBM
- *                 streaming rate). Leave it off when sequences share prefix blocks, so
- *                 shared blocks may be served from cache. Results are identical.
+ *                 streaming rate) and the partitions are scheduled longest first. Leave
+ *                 it off when sequences share prefix blocks, so shared blocks may be
+ *                 served from cache (neighbouring sequences then run together). Results
+ *                 are identical.
  * Query head h reads KV head h / (num_q_heads / num_kv_heads). Arithmetic: fp16
  * inputs, fp32 products, sums and softmax, fp16 output rounded to nearest even. */
 #define PA_DECODE_KV_STREAM 1u

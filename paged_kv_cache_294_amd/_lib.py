@@ -36,7 +36,7 @@ SIGNATURES = {
     "pa_slot": (_i64, [ctypes.POINTER(_i32), _i64, _i32]),
     "pa_kv_elem_offset": (_i64, [_i64, _i32, _i32, _i32, _i32, _i32]),
     "pa_num_partitions": (_i32, [_i32, _i32]),
-    "pa_decode_default_partition_size": (_i32, [_i32, _i32, _i32]),
+    "pa_decode_default_partition_size": (_i32, [_i32, _i32, _i32, _i32]),
     "pa_decode_workspace_bytes": (_i64, [_i32, _i32, _i32, _i32, _i32]),
     "pa_kv_append": (ctypes.c_int, [_vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i64, _i64, _i64, _vp]),
     "pa_decode": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _i64,
@@ -188,9 +188,10 @@ def pa_num_partitions(max_context_len: int, partition_size: int) -> int:
     return load().pa_num_partitions(max_context_len, partition_size)
 
 
-def pa_decode_default_partition_size(num_q_heads: int, num_kv_heads: int,
+def pa_decode_default_partition_size(num_seqs: int, num_q_heads: int, num_kv_heads: int,
                                      max_context_len: int) -> int:
-    return load().pa_decode_default_partition_size(num_q_heads, num_kv_heads, max_context_len)
+    return load().pa_decode_default_partition_size(num_seqs, num_q_heads, num_kv_heads,
+                                                   max_context_len)
 
 
 def pa_decode_workspace_bytes(num_seqs: int, num_q_heads: int, max_context_len: int,
@@ -244,7 +245,9 @@ def _decode_args(out, q, kv_pool, block_tables, context_lens, max_context_len, s
     need = pa_decode_workspace_bytes(B, hq, max_context_len, partition_size, d)
     if need < 0:
         raise PagedKVError("pa_decode_workspace_bytes", PA_ERR_INVALID)
-    if workspace is None and need > 0:
+    # with one partition the workspace is optional (it only orders the sequences)
+    optional = pa_num_partitions(max_context_len, partition_size) == 1
+    if workspace is None and need > 0 and not (optional and _CAPTURING):
         if _CAPTURING:
             # a buffer allocated here would be freed after the call while the graph
             # keeps writing it on every replay

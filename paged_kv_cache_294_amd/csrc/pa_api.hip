@@ -115,14 +115,18 @@ PA_EXPORT int32_t pa_num_partitions(int32_t max_context_len, int32_t partition_s
   return p < 1 ? 1 : p;
 }
 
-PA_EXPORT int32_t pa_decode_default_partition_size(int32_t num_q_heads, int32_t num_kv_heads,
-                                                   int32_t max_context_len) {
-  if (max_context_len < 0 || num_kv_heads <= 0 || num_q_heads <= 0 || num_q_heads % num_kv_heads)
+PA_EXPORT int32_t pa_decode_default_partition_size(int32_t num_seqs, int32_t num_q_heads,
+                                                   int32_t num_kv_heads, int32_t max_context_len) {
+  if (num_seqs < 0 || max_context_len < 0 || num_kv_heads <= 0 || num_q_heads <= 0 ||
+      num_q_heads % num_kv_heads)
     return -1;
-  if (num_q_heads != num_kv_heads) return max_context_len > 8192 ? 512 : 256;
-  const int64_t blocks = ((int64_t)max_context_len + kBlock - 1) / kBlock;  // = tokens / 16, rounded up
-  const int64_t ps = (blocks + 15) / 16 * 16;  // 16 partitions of ps tokens cover the context
-  return (int32_t)std::min<int64_t>(std::max<int64_t>(ps, 1024), INT32_MAX / kBlock * kBlock);
+  const int64_t target_waves = num_q_heads == num_kv_heads ? 4096 : 2048;
+  const int64_t waves_per_part = std::max<int64_t>(1, (int64_t)num_seqs * num_kv_heads);
+  const int64_t parts = (target_waves + waves_per_part - 1) / waves_per_part;
+  int64_t ps = ((int64_t)max_context_len + parts - 1) / parts;
+  ps = std::max<int64_t>(kBlock, (ps + kBlock - 1) / kBlock * kBlock);
+  if (parts > 16) ps = std::max<int64_t>(ps, 512);
+  return (int32_t)std::min<int64_t>(ps, INT32_MAX / kBlock * kBlock);
 }
 
 PA_EXPORT int64_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads,
@@ -131,7 +135,7 @@ PA_EXPORT int64_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_head
   if (num_seqs < 0 || num_q_heads <= 0 || head_size <= 0) return -1;
   const int32_t p = pa_num_partitions(max_context_len, partition_size);
   if (p < 0) return -1;
-  if (p == 1) return 0;
+  if (p == 1) return (4 * (1 + (int64_t)num_seqs) + 255) / 256 * 256;  // item list only
   const int64_t rows = (int64_t)num_seqs * num_q_heads * p;
   int64_t bytes = rows * head_size * 4;  // o
   bytes = (bytes + 255) / 256 * 256;
@@ -290,6 +294,12 @@ pa_status decode_impl(void* out, const void* q, const void* kv_pool, const int32
       const int64_t ml_bytes = (rows * 2 * 4 + 255) / 256 * 256;
       a.ws_items = reinterpret_cast<int*>(static_cast<char*>(workspace) + o_bytes + ml_bytes);
     }
+  } else if (workspace != nullptr && (reinterpret_cast<uintptr_t>(workspace) & 255u) == 0 &&
+             workspace_bytes >= pa_decode_workspace_bytes(num_seqs, num_q_heads, max_context_len,
+                                                          partition_size, head_size)) {
+    // one partition: the workspace is optional and only holds the item list; without it the
+    // sequences run in launch order
+    a.ws_items = static_cast<int*>(workspace);
   }
   if (cascade) return hip_status(pkv::launch_decode_shared_prefix(a, (hipStream_t)stream));
   return hip_status(pkv::launch_decode(a, (hipStream_t)stream));

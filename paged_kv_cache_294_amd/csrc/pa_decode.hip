@@ -373,9 +373,11 @@ __global__ __launch_bounds__(kThreads) void decode_partition_kernel(const Decode
 // is partly filled, and identical partitions take very different times under full load.
 // The hardware starts workgroups in launch order as slots free up, so when the partly
 // filled partitions are a sizeable share of the items (at most kOrderMaxParts partitions
-// per sequence), a one-workgroup pre-pass lists the (sequence, partition) items by
-// decreasing length and the partition kernel takes them in that order: the long items run
-// first and the short ones fill the end.
+// per sequence; with one partition every item is a whole, ragged context), a
+// one-workgroup pre-pass lists the (sequence, partition) items by decreasing length and
+// the partition kernel takes them in that order: the long items run first and the short
+// ones fill the end. Only when no block is shared between sequences: otherwise launch
+// order keeps the sequences of a prompt group together (see decode_item).
 constexpr int kOrderMaxParts = 16;
 constexpr int kOrderThreads = 1024;
 constexpr int kOrderBuckets = 1025;  // bucket 1024 - min(size in blocks, 1024)
@@ -475,7 +477,8 @@ __device__ __forceinline__ int group_of(const DecodeArgs& a, int b) {
 constexpr int kModePlain = 0, kModeShared = 1;
 
 template <int D, int G, bool Stream, typename KV, int Mode = kModePlain>
-__global__ __launch_bounds__(kThreads) void decode_gqa_kernel(const DecodeArgs a) {
+__global__ __launch_bounds__(kThreads) void decode_gqa_kernel(const DecodeArgs a,
+                                                              const int* __restrict__ items) {
   static_assert(G >= 1 && G <= 16, "query heads per KV head must fit 16 columns");
   constexpr int S = 16 / G;  // samples of a group per tile in the prefix pass
   using Gm = GqaGeo<D>;
@@ -489,10 +492,21 @@ __global__ __launch_bounds__(kThreads) void decode_gqa_kernel(const DecodeArgs a
   // shared-prefix decode runs both passes in one launch: the first prefix_grid workgroups
   // take the prefix items, the rest each sequence's own tokens
   const bool pre = Mode == kModeShared && (int)blockIdx.x < a.prefix_grid;
-  const DecodeItem item =
-      pre ? decode_item(a, a.num_groups * a.group_chunks, a.prefix_parts, blockIdx.x)
-          : decode_item(a, a.num_seqs, a.num_partitions, blockIdx.x - (Mode == kModeShared ? a.prefix_grid : 0));
-  if (!item.valid) return;
+  DecodeItem item;
+  if (Mode == kModePlain && items != nullptr) {  // largest-first list, as in the MHA kernel
+    const int groups = (a.num_kv_heads + kWavesPerGroup - 1) / kWavesPerGroup;
+    const int idx = blockIdx.x / groups;
+    if (idx >= items[0]) return;
+    const unsigned key = (unsigned)items[1 + idx];
+    item.hg = blockIdx.x % groups;
+    item.b = (int)(key >> 16);
+    item.p = (int)(key & 0xffffu);
+  } else {
+    item = pre ? decode_item(a, a.num_groups * a.group_chunks, a.prefix_parts, blockIdx.x)
+               : decode_item(a, a.num_seqs, a.num_partitions,
+                             blockIdx.x - (Mode == kModeShared ? a.prefix_grid : 0));
+    if (!item.valid) return;
+  }
   const int kvh = item.hg * kWavesPerGroup + w;
   const int p = item.p;
   if (kvh >= a.num_kv_heads) return;
@@ -774,27 +788,29 @@ hipError_t launch_decode_dg(const DecodeArgs& a, hipStream_t stream) {
   const int64_t wgs = (quads + kXcds - 1) / kXcds * kXcds * kSeqQuad;
   if (wgs > INT32_MAX) return hipErrorInvalidValue;
   const dim3 grid((unsigned)wgs);
+  const int* items = nullptr;
+  dim3 pgrid = grid;
+  // ordered only when no block is shared (the caller's PA_DECODE_KV_STREAM): launch order
+  // keeps sequences that share prompt blocks together, so those blocks come from L2
+  if (a.stream_kv && a.num_partitions <= kOrderMaxParts && a.ws_items != nullptr) {
+    const int64_t owgs = (int64_t)a.num_seqs * a.num_partitions * groups;
+    if (owgs > INT32_MAX) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(order_items_kernel, dim3(1), dim3(kOrderThreads), 0, stream, a, a.ws_items);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    items = a.ws_items;
+    pgrid = dim3((unsigned)owgs);
+  }
   if constexpr (G == 1) {  // one query head per KV head: vector ALUs
-    const int* items = nullptr;
-    dim3 pgrid = grid;
-    if (a.num_partitions > 1 && a.num_partitions <= kOrderMaxParts && a.ws_items != nullptr) {
-      const int64_t owgs = (int64_t)a.num_seqs * a.num_partitions * groups;
-      if (owgs > INT32_MAX) return hipErrorInvalidValue;
-      hipLaunchKernelGGL(order_items_kernel, dim3(1), dim3(kOrderThreads), 0, stream, a, a.ws_items);
-      const hipError_t e = hipGetLastError();
-      if (e != hipSuccess) return e;
-      items = a.ws_items;
-      pgrid = dim3((unsigned)owgs);
-    }
     if (a.stream_kv)
       hipLaunchKernelGGL((decode_partition_kernel<D, 1, true, KV>), pgrid, dim3(kThreads), 0, stream, a, items);
     else
       hipLaunchKernelGGL((decode_partition_kernel<D, 1, false, KV>), pgrid, dim3(kThreads), 0, stream, a, items);
   } else {  // a query-head group per KV head: matrix cores
     if (a.stream_kv)
-      hipLaunchKernelGGL((decode_gqa_kernel<D, G, true, KV>), grid, dim3(kThreads), 0, stream, a);
+      hipLaunchKernelGGL((decode_gqa_kernel<D, G, true, KV>), pgrid, dim3(kThreads), 0, stream, a, items);
     else
-      hipLaunchKernelGGL((decode_gqa_kernel<D, G, false, KV>), grid, dim3(kThreads), 0, stream, a);
+      hipLaunchKernelGGL((decode_gqa_kernel<D, G, false, KV>), pgrid, dim3(kThreads), 0, stream, a, items);
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.num_partitions == 1) return e;
@@ -833,7 +849,7 @@ hipError_t launch_shared_prefix_dg(const DecodeArgs& a, hipStream_t stream) {
   k.prefix_grid = (int)wpre;
   // one launch: prefix items, then every sequence's own tokens (independent outputs)
   hipLaunchKernelGGL((decode_gqa_kernel<D, G, false, KV, kModeShared>), dim3((unsigned)(wpre + wown)),
-                     dim3(kThreads), 0, stream, k);
+                     dim3(kThreads), 0, stream, k, nullptr);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   DecodeArgs own = k;

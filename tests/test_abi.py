@@ -97,7 +97,8 @@ def test_partitions_and_workspace(lib):
     assert pkv.pa_num_partitions(512, 512) == 1
     assert pkv.pa_num_partitions(513, 512) == 2
     assert pkv.pa_num_partitions(32768, 512) == 64
-    assert pkv.pa_decode_workspace_bytes(8, 32, 512, 512, 128) == 0
+    assert pkv.pa_decode_workspace_bytes(8, 32, 512, 512, 128) == 256  # item list only (optional)
+    assert pkv.pa_decode_workspace_bytes(100, 32, 512, 512, 128) == 512
     rows = 8 * 32 * 64
     o = (rows * 128 * 4 + 255) // 256 * 256
     ml = (rows * 8 + 255) // 256 * 256
@@ -216,15 +217,17 @@ def test_fp8_calls_reject_bad_scales(lib):
 
 def test_default_partition_size(lib):
     f = pkv.pa_decode_default_partition_size
-    # one query head per KV head: at least 1024 tokens, at most 16 partitions
-    assert f(32, 32, 0) == 1024
-    assert f(32, 32, 2048) == 1024
-    assert f(32, 32, 16384) == 1024 and pkv.pa_num_partitions(16384, 1024) == 16
-    assert f(32, 32, 16385) == 1040
-    assert f(32, 32, 32768) == 2048
-    for L in (1, 5000, 20000, 100000, 1 << 20):
-        ps = f(32, 32, L)
-        assert ps % 16 == 0 and ps >= 1024 and pkv.pa_num_partitions(L, ps) <= 16
-    # grouped query heads
-    assert f(32, 8, 4096) == 256 and f(32, 8, 8193) == 512
-    assert f(32, 32, -1) == -1 and f(12, 8, 100) == -1
+    # one query head per KV head: ceil(4096 / (seqs * kv heads)) partitions
+    assert f(256, 32, 32, 2048) == 2048               # 8192 waves per partition level: one
+    assert f(248, 32, 32, 4096) == 4096
+    assert f(8, 32, 32, 32768) == 2048                # 256 waves: 16 partitions
+    assert f(8, 32, 32, 33) == 16                     # 16 partitions of one block
+    assert f(1, 8, 8, 131072) == 512                  # > 16 partitions: at least 512 tokens
+    assert f(4, 4, 4, 0) == 512                       # 256 partitions wanted: at least 512 tokens
+    # grouped query heads: 2048 waves
+    assert f(256, 32, 8, 1280) == 1280
+    assert f(16, 32, 8, 4096) == 256                  # 16 partitions
+    for args in [(1, 32, 32, 5000), (64, 64, 8, 20000), (3, 16, 16, 1 << 20), (0, 8, 8, 100)]:
+        ps = f(*args)
+        assert ps >= 16 and ps % 16 == 0
+    assert f(4, 32, 32, -1) == -1 and f(4, 12, 8, 100) == -1 and f(-1, 8, 8, 10) == -1
