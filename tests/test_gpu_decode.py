@@ -285,6 +285,58 @@ def test_decode_zero_length_and_bad_rows():
     check_attention(got[3:4], ref[3:4], "good row next to bad ones")
 
 
+def _raw_decode_no_workspace(d, partition_size, flags):
+    """pa_decode through the C ABI with no workspace (allowed with one partition)."""
+    inp = d.inp
+    out = torch.empty_like(d.q)
+    nb, bs, _, hkv, D = d.pool.shape
+    st = pkv.load().pa_decode(out.data_ptr(), d.q.data_ptr(), d.pool.data_ptr(), d.bt.data_ptr(),
+                              d.lens.data_ptr(), d.q.shape[0], d.q.shape[1], hkv, D, bs,
+                              d.bt.shape[1], nb, int(inp.seq_lens.max()), inp.scale,
+                              partition_size, None, 0, flags, None)
+    assert st == pkv.PA_OK, st
+    torch.cuda.synchronize()
+    return host(out)
+
+
+@pytest.mark.parametrize("G", [1, 4])
+def test_decode_longest_first_order_is_bit_identical(G):
+    """PA_DECODE_KV_STREAM schedules the (sequence, partition) items longest first; results
+    are those of launch order, with several partitions, one, and one without workspace."""
+    lens = np.random.default_rng(46 + G).integers(1, 3000, 96)
+    lens[:3] = [0, 1, 16]
+    inp = workloads.decode_case(46 + G, lens, 8 * G, 8, 128)
+    ref = oracle_decode(inp)
+    d = Dev(inp)
+    for ps in (256, 1024, 1 << 16):
+        plain = d.decode(partition_size=ps)
+        ordered = d.decode(partition_size=ps, flags=pkv.PA_DECODE_KV_STREAM)
+        note(f"order G={G} ps={ps}")
+        check_attention(ordered, ref, f"ordered G{G} ps{ps}")
+        assert np.array_equal(bits(plain), bits(ordered)), ps
+    bare = _raw_decode_no_workspace(d, 1 << 16, pkv.PA_DECODE_KV_STREAM)
+    assert np.array_equal(bits(bare), bits(plain))
+
+
+@pytest.mark.parametrize("ps", [256, 1 << 16])
+def test_decode_zero_length_and_bad_rows_ordered(ps):
+    inp = workloads.decode_case(47, [0, 30, 600, 600, 20], 8, 4, 128, append=False)
+    d = Dev(inp, append=False)
+    lens = inp.seq_lens.copy()
+    lens[4] = 10_000  # beyond max_context_len and the table: NaN row
+    d.lens = dev(lens)
+    bt = inp.block_tables.copy()
+    bt[2, 20] = inp.num_blocks + 3  # outside the pool: NaN row
+    bt[1, 0] = -1                    # outside the pool, first block: NaN row
+    d.bt = dev(bt)
+    got = d.decode(partition_size=ps, max_context_len=600,
+                   flags=pkv.PA_DECODE_KV_STREAM).astype(np.float64)
+    assert np.all(got[0] == 0)
+    assert np.all(np.isnan(got[1])) and np.all(np.isnan(got[2])) and np.all(np.isnan(got[4]))
+    ref = oracle.decode(inp.q, inp.pool, inp.block_tables, inp.seq_lens, inp.scale)
+    check_attention(got[3:4], ref[3:4], "good row next to bad ones (ordered)")
+
+
 def test_stream_read_runs():
     buf = torch.ones(1 << 24, dtype=torch.uint8, device="cuda")
     sink = torch.zeros(pkv.pa_stream_read_sink_len(buf.numel()), dtype=torch.float32, device="cuda")
