@@ -693,9 +693,10 @@ def main():
             "kernel": ("pa_decode_shared_prefix (prefix, own-token and log-sum-exp reduce kernels)"
                        if shared_prefix else
                        ("pa_decode_fp8" if kv_fp8 else "pa_decode") + " (" +
-                       ("longest-first order pre-pass + " if kv_stream and nparts <= 16 else "") +
-                       ("partition + log-sum-exp reduce kernels)" if nparts > 1
-                        else "partition kernel)")),
+                       ("partition + log-sum-exp reduce kernels" if nparts > 1
+                        else "partition kernel") +
+                       ("; a longest-first order pre-pass when the items exceed what the GPU "
+                        "holds at once" if kv_stream and nparts <= 16 else "") + ")"),
             "bound": "hbm",
             "achieved": achieved,
             "peak": HBM_PEAK_GBPS,

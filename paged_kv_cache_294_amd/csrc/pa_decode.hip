@@ -28,6 +28,8 @@
 // Output. A sequence with one partition writes its fp16 row directly. Otherwise every
 // partition writes (m, l, o = acc / l) to the workspace and the reduce kernel merges
 // them: M = max m_p, w_p = l_p * 2^(m_p - M), out = sum w_p o_p / sum w_p.
+#include <atomic>
+
 #include "pa_device.h"
 #include "pa_launch.h"
 
@@ -781,6 +783,31 @@ __global__ __launch_bounds__(kThreads) void decode_reduce_kernel(const DecodeArg
   for (int k = 0; k < PER_LANE; ++k) out[k] = (half_t)(acc[k] * inv);
 }
 
+// Waves of the plain decode kernel for (D, G, Stream, KV) that the current device holds at
+// once, from the occupancy the compiled kernel allows (0 when the runtime cannot say);
+// queried once per device.
+template <int D, int G, bool Stream, typename KV>
+int64_t resident_waves() {
+  static std::atomic<int64_t> cache[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+  int64_t v = cache[dev].load(std::memory_order_relaxed);
+  if (v > 0) return v;
+  int per_cu = 0, cus = 0;
+  hipError_t e;
+  if constexpr (G == 1)
+    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, decode_partition_kernel<D, 1, Stream, KV>,
+                                                     kThreads, 0);
+  else
+    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, decode_gqa_kernel<D, G, Stream, KV>,
+                                                     kThreads, 0);
+  if (e != hipSuccess || hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+    return 0;
+  v = (int64_t)per_cu * cus * kWavesPerGroup;
+  cache[dev].store(v, std::memory_order_relaxed);
+  return v;
+}
+
 template <int D, int G, typename KV>
 hipError_t launch_decode_dg(const DecodeArgs& a, hipStream_t stream) {
   const int64_t groups = (a.num_kv_heads + kWavesPerGroup - 1) / kWavesPerGroup;
@@ -791,8 +818,11 @@ hipError_t launch_decode_dg(const DecodeArgs& a, hipStream_t stream) {
   const int* items = nullptr;
   dim3 pgrid = grid;
   // ordered only when no block is shared (the caller's PA_DECODE_KV_STREAM): launch order
-  // keeps sequences that share prompt blocks together, so those blocks come from L2
-  if (a.stream_kv && a.num_partitions <= kOrderMaxParts && a.ws_items != nullptr) {
+  // keeps sequences that share prompt blocks together, so those blocks come from L2; and
+  // only when the items do not all fit on the device at once (then order changes nothing)
+  const int64_t waves = (int64_t)a.num_seqs * a.num_partitions * groups * kWavesPerGroup;
+  if (a.stream_kv && a.num_partitions <= kOrderMaxParts && a.ws_items != nullptr &&
+      waves > resident_waves<D, G, true, KV>()) {
     const int64_t owgs = (int64_t)a.num_seqs * a.num_partitions * groups;
     if (owgs > INT32_MAX) return hipErrorInvalidValue;
     hipLaunchKernelGGL(order_items_kernel, dim3(1), dim3(kOrderThreads), 0, stream, a, a.ws_items);
