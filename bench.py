@@ -364,7 +364,12 @@ class Step:
             pkv.pa_prefill_chunk(self.pout, self.pq, self.pool, self.pbt, self.qsl, self.plens,
                                  self.max_q, self.max_s, self.inp.scale, stream=stream)
         rec(2)
-        if self.shared_prefix:
+        if self.shared_prefix and self.kv_fp8:
+            pkv.pa_decode_shared_prefix_fp8(self.dout, self.dq, self.pool, self.dbt, self.dlens,
+                                            self.mcl, self.gs, self.pl, self.max_group,
+                                            self.max_prefix, self.inp.scale, 1.0, 1.0, self.ps,
+                                            self.ws, stream=stream)
+        elif self.shared_prefix:
             pkv.pa_decode_shared_prefix(self.dout, self.dq, self.pool, self.dbt, self.dlens, self.mcl,
                                         self.gs, self.pl, self.max_group, self.max_prefix,
                                         self.inp.scale, self.ps, self.ws, stream=stream)
@@ -546,9 +551,9 @@ def main():
     kv_fp8 = args.kv_dtype == "fp8"
     elem_bytes = 1 if kv_fp8 else 2
     shared_prefix = {"plain": False, "shared-prefix": True,
-                     "auto": bool(inp.prefix_blocks) and not kv_fp8}[args.decode]
-    if shared_prefix and (kv_fp8 or not inp.prefix_blocks):
-        print("--decode shared-prefix needs prompt groups and an fp16 cache", file=sys.stderr)
+                     "auto": bool(inp.prefix_blocks)}[args.decode]
+    if shared_prefix and not inp.prefix_blocks:
+        print("--decode shared-prefix needs prompt groups (workload c4)", file=sys.stderr)
         sys.exit(2)
     if args.partition_size <= 0 and shared_prefix:
         args.partition_size = 512  # fastest of 256 .. 2048 for 64 groups of 1024-token prompts
@@ -690,7 +695,8 @@ def main():
         "pct_of_hbm_peak": 100.0 * kv_bytes / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBPS,
         "seq_steps_per_s": inp.num_seqs / (ms_step * 1e-3),
         "roofline": {
-            "kernel": ("pa_decode_shared_prefix (prefix, own-token and log-sum-exp reduce kernels)"
+            "kernel": (("pa_decode_shared_prefix_fp8" if kv_fp8 else "pa_decode_shared_prefix") +
+                       " (prefix, own-token and log-sum-exp reduce kernels)"
                        if shared_prefix else
                        ("pa_decode_fp8" if kv_fp8 else "pa_decode") + " (" +
                        ("partition + log-sum-exp reduce kernels" if nparts > 1

@@ -227,7 +227,8 @@ int64_t pa_decode_shared_prefix_workspace_bytes(int32_t num_seqs, int32_t num_q_
  * pa_decode_fp8: pa_decode over an E4M3 pool, same arguments and results plus the two
  *   scales; each code is widened exactly to fp16 and the scales applied in fp32 (the key
  *   scale with the softmax scale, the value scale with the final normalisation).
- * pa_prefill_chunk_fp8: pa_prefill_chunk over an E4M3 pool, likewise. */
+ * pa_prefill_chunk_fp8: pa_prefill_chunk over an E4M3 pool, likewise.
+ * pa_decode_shared_prefix_fp8: pa_decode_shared_prefix over an E4M3 pool, likewise. */
 pa_status pa_kv_append_fp8(void* kv_pool, const void* key, const void* value,
                            const int64_t* slot_mapping, int32_t num_tokens,
                            int32_t num_kv_heads, int32_t head_size, int32_t block_size,
@@ -248,6 +249,17 @@ pa_status pa_prefill_chunk_fp8(void* out, const void* q, const void* kv_pool,
                                int32_t num_kv_heads, int32_t head_size, int32_t block_size,
                                int32_t max_blocks_per_seq, int64_t num_blocks, float scale,
                                float k_scale, float v_scale, void* stream);
+pa_status pa_decode_shared_prefix_fp8(void* out, const void* q, const void* kv_pool,
+                                      const int32_t* block_tables, const int32_t* context_lens,
+                                      int32_t num_seqs, int32_t num_q_heads,
+                                      int32_t num_kv_heads, int32_t head_size,
+                                      int32_t block_size, int32_t max_blocks_per_seq,
+                                      int64_t num_blocks, int32_t max_context_len, float scale,
+                                      float k_scale, float v_scale, int32_t partition_size,
+                                      const int32_t* group_start, const int32_t* prefix_lens,
+                                      int32_t num_groups, int32_t max_group_size,
+                                      int32_t max_prefix_len, void* workspace,
+                                      int64_t workspace_bytes, void* stream);
 
 /* Causal attention of prefill chunks over their paged context (the scheduler on
  * page "vLLM 部署深度指南" puts prefills and decodes into one step). Request r owns

@@ -23,6 +23,7 @@ from ._lib import (  # noqa: F401
     pa_decode,
     pa_decode_fp8,
     pa_decode_shared_prefix,
+    pa_decode_shared_prefix_fp8,
     pa_decode_shared_prefix_workspace_bytes,
     pa_decode_workspace_bytes,
     pa_gather_kv,

@@ -49,6 +49,9 @@ SIGNATURES = {
     "pa_decode_shared_prefix": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32,
                                                _i32, _i64, _i32, _f32, _i32, _vp, _vp, _i32, _i32,
                                                _i32, _vp, _i64, _vp]),
+    "pa_decode_shared_prefix_fp8": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32,
+                                                   _i32, _i32, _i64, _i32, _f32, _f32, _f32, _i32,
+                                                   _vp, _vp, _i32, _i32, _i32, _vp, _i64, _vp]),
     "pa_decode_shared_prefix_workspace_bytes": (_i64, [_i32, _i32, _i32, _i32, _i32, _i32]),
     "pa_prefill_chunk": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32,
                                         _i32, _i32, _i32, _i32, _i64, _f32, _vp]),
@@ -283,12 +286,9 @@ def pa_decode_shared_prefix_workspace_bytes(num_seqs, num_q_heads, max_context_l
                                                           max_prefix_len, partition_size, head_size)
 
 
-def pa_decode_shared_prefix(out, q, kv_pool, block_tables, context_lens, max_context_len,
-                            group_start, prefix_lens, max_group_size, max_prefix_len,
-                            scale=None, partition_size=256, workspace=None, stream=None):
-    """pa_decode for groups of sequences sharing prefix blocks: group g is sequences
-    group_start[g] .. group_start[g+1]-1 (device int32), sharing prefix_lens[g] tokens
-    (device int32, multiples of the block size). Same result as pa_decode."""
+def _shared_prefix_args(out, q, kv_pool, block_tables, context_lens, max_context_len,
+                        group_start, prefix_lens, max_group_size, max_prefix_len, scale,
+                        partition_size, workspace, pool_dtype):
     nb, bs, hkv, d = _pool_geometry(kv_pool)
     B, hq, dq = q.shape
     if dq != d or tuple(out.shape) != (B, hq, d):
@@ -308,15 +308,43 @@ def pa_decode_shared_prefix(out, q, kv_pool, block_tables, context_lens, max_con
         if _CAPTURING:
             raise ValueError("pa_decode_shared_prefix under capture needs a caller-owned workspace")
         workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
-    st = load().pa_decode_shared_prefix(
-        _dense(out, "out", torch.float16), _dense(q, "q", torch.float16),
-        _dense(kv_pool, "kv_pool", torch.float16), _dense(block_tables, "block_tables", torch.int32),
-        _dense(context_lens, "context_lens", torch.int32), B, hq, hkv, d, bs,
-        int(block_tables.shape[1]), nb, int(max_context_len), float(scale), int(partition_size),
-        _dense(group_start, "group_start", torch.int32), _dense(prefix_lens, "prefix_lens", torch.int32),
-        G, int(max_group_size), int(max_prefix_len), _dense(workspace, "workspace", torch.uint8),
-        workspace.numel(), _stream(stream))
+    head = (_dense(out, "out", torch.float16), _dense(q, "q", torch.float16),
+            _dense(kv_pool, "kv_pool", pool_dtype), _dense(block_tables, "block_tables", torch.int32),
+            _dense(context_lens, "context_lens", torch.int32), B, hq, hkv, d, bs,
+            int(block_tables.shape[1]), nb, int(max_context_len), float(scale))
+    tail = (int(partition_size), _dense(group_start, "group_start", torch.int32),
+            _dense(prefix_lens, "prefix_lens", torch.int32), G, int(max_group_size),
+            int(max_prefix_len), _dense(workspace, "workspace", torch.uint8), workspace.numel())
+    return head, tail, workspace
+
+
+def pa_decode_shared_prefix(out, q, kv_pool, block_tables, context_lens, max_context_len,
+                            group_start, prefix_lens, max_group_size, max_prefix_len,
+                            scale=None, partition_size=256, workspace=None, stream=None):
+    """pa_decode for groups of sequences sharing prefix blocks: group g is sequences
+    group_start[g] .. group_start[g+1]-1 (device int32), sharing prefix_lens[g] tokens
+    (device int32, multiples of the block size). Same result as pa_decode."""
+    head, tail, ws = _shared_prefix_args(out, q, kv_pool, block_tables, context_lens,
+                                         max_context_len, group_start, prefix_lens,
+                                         max_group_size, max_prefix_len, scale, partition_size,
+                                         workspace, torch.float16)
+    st = load().pa_decode_shared_prefix(*head, *tail, _stream(stream))
     _check("pa_decode_shared_prefix", st)
+
+
+def pa_decode_shared_prefix_fp8(out, q, kv_pool, block_tables, context_lens, max_context_len,
+                                group_start, prefix_lens, max_group_size, max_prefix_len,
+                                scale=None, k_scale=1.0, v_scale=1.0, partition_size=256,
+                                workspace=None, stream=None):
+    """pa_decode_shared_prefix over an FP8 (E4M3) pool held as a uint8 tensor, with its
+    per-tensor scales."""
+    head, tail, ws = _shared_prefix_args(out, q, kv_pool, block_tables, context_lens,
+                                         max_context_len, group_start, prefix_lens,
+                                         max_group_size, max_prefix_len, scale, partition_size,
+                                         workspace, torch.uint8)
+    st = load().pa_decode_shared_prefix_fp8(*head, float(k_scale), float(v_scale), *tail,
+                                            _stream(stream))
+    _check("pa_decode_shared_prefix_fp8", st)
 
 
 def pa_decode_fp8(out, q, kv_pool, block_tables, context_lens, max_context_len, scale=None,

@@ -335,6 +335,22 @@ PA_EXPORT pa_status pa_decode_shared_prefix(
                      max_group_size, max_prefix_len);
 }
 
+PA_EXPORT pa_status pa_decode_shared_prefix_fp8(
+    void* out, const void* q, const void* kv_pool, const int32_t* block_tables,
+    const int32_t* context_lens, int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+    int32_t head_size, int32_t block_size, int32_t max_blocks_per_seq, int64_t num_blocks,
+    int32_t max_context_len, float scale, float k_scale, float v_scale, int32_t partition_size,
+    const int32_t* group_start, const int32_t* prefix_lens, int32_t num_groups,
+    int32_t max_group_size, int32_t max_prefix_len, void* workspace, int64_t workspace_bytes,
+    void* stream) {
+  if (group_start == nullptr && num_seqs > 0) return PA_ERR_INVALID;
+  return decode_impl(out, q, kv_pool, block_tables, context_lens, num_seqs, num_q_heads,
+                     num_kv_heads, head_size, block_size, max_blocks_per_seq, num_blocks,
+                     max_context_len, scale, partition_size, workspace, workspace_bytes, 0u,
+                     true, k_scale, v_scale, stream, group_start, prefix_lens, num_groups,
+                     max_group_size, max_prefix_len);
+}
+
 PA_EXPORT pa_status pa_decode_fp8(void* out, const void* q, const void* kv_pool,
                                   const int32_t* block_tables, const int32_t* context_lens,
                                   int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,

@@ -174,3 +174,44 @@ def test_prefill_fp8_long_prior_sampled_rows():
     want = oracle.prefill_chunk(q, fp8.dequantize_pool(pool, 0.05, 0.04), bt, qsl, lens,
                                 inp.scale, rows=set(rows.tolist()))
     check_attention(host(out)[rows], want[rows], "prefill fp8 long prior")
+
+
+def run_shared_fp8(inp, pool_u8, ks, vs, group_start, prefix_lens, ps):
+    q, bt, L = inp.decode_part()
+    out = torch.full(q.shape, float("nan"), dtype=torch.float16, device="cuda")
+    gs = np.asarray(group_start, np.int32)
+    pl = np.asarray(prefix_lens, np.int32)
+    pkv.pa_decode_shared_prefix_fp8(out, dev(q), dev(pool_u8), dev(bt), dev(L), int(L.max()),
+                                    dev(gs), dev(pl), int(np.diff(gs).max()), int(pl.max()),
+                                    inp.scale, ks, vs, ps)
+    return host(out)
+
+
+@pytest.mark.parametrize("G", [1, 4])
+def test_shared_prefix_fp8_matches_oracle(G):
+    rng = np.random.default_rng(130 + G)
+    priv = rng.integers(0, 70, 24)
+    priv[2] = 0
+    inp = workloads.prefix_shared_case(130 + G, 3, 8, 4, priv, 4 * G, 4, 128)
+    ks, vs = 0.02, 0.03
+    pool = np.concatenate([fp8.quantize(inp.pool[:, :, 0:1], ks),
+                           fp8.quantize(inp.pool[:, :, 1:2], vs)], axis=2)
+    q, bt, L = inp.decode_part()
+    want = oracle.decode(q, fp8.dequantize_pool(pool, ks, vs), bt, L, inp.scale)
+    for ps in (16, 256):
+        note(f"shared prefix fp8 G={G} ps={ps}")
+        got = run_shared_fp8(inp, pool, ks, vs, [0, 8, 16, 24], [64, 64, 64], ps)
+        check_attention(got, want, f"shared fp8 G{G} ps{ps}")
+
+
+def test_shared_prefix_fp8_config4():
+    inp = workloads.config4()
+    pool = np.concatenate([fp8.quantize(inp.pool[:, :, 0:1], 1.0),
+                           fp8.quantize(inp.pool[:, :, 1:2], 1.0)], axis=2)
+    note("shared prefix fp8 config 4")
+    got = run_shared_fp8(inp, pool, 1.0, 1.0, np.arange(0, 257, 4), np.full(64, 1024), 512)
+    q, bt, L = inp.decode_part()
+    rng = np.random.default_rng(0)
+    pairs = [(int(b), int(h)) for b, h in zip(rng.integers(0, 256, 200), rng.integers(0, 32, 200))]
+    want = oracle.decode_rows(q, fp8.dequantize_pool(pool, 1.0, 1.0), bt, L, inp.scale, pairs)
+    check_attention(np.stack([got[b, h] for b, h in pairs]), want, "shared fp8 config4")
