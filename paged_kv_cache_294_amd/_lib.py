@@ -245,6 +245,8 @@ def _decode_args(out, q, kv_pool, block_tables, context_lens, max_context_len, s
         raise ValueError("block_tables must be [num_seqs, max_blocks], context_lens [num_seqs]")
     if scale is None:
         scale = 1.0 / math.sqrt(d)
+    if partition_size is None:
+        partition_size = pa_decode_default_partition_size(B, hq, hkv, int(max_context_len))
     need = pa_decode_workspace_bytes(B, hq, max_context_len, partition_size, d)
     if need < 0:
         raise PagedKVError("pa_decode_workspace_bytes", PA_ERR_INVALID)
@@ -266,13 +268,15 @@ def _decode_args(out, q, kv_pool, block_tables, context_lens, max_context_len, s
 
 
 def pa_decode(out, q, kv_pool, block_tables, context_lens, max_context_len, scale=None,
-              partition_size=512, workspace=None, flags=0, stream=None):
+              partition_size=None, workspace=None, flags=0, stream=None):
     """Paged decode: out[b] = attention of q[b] ([B, Hq, D]) over its first context_lens[b] tokens.
 
-    ``max_context_len`` is a host upper bound of context_lens. ``workspace`` is a device
-    uint8 tensor of at least :func:`pa_decode_workspace_bytes` bytes; one is allocated
-    here when it is None. ``flags``: 0 or ``PA_DECODE_KV_STREAM`` (no block is shared
-    between the sequences of the call; K/V loads bypass cache retention).
+    ``max_context_len`` is a host upper bound of context_lens. ``partition_size`` None:
+    :func:`pa_decode_default_partition_size`. ``workspace`` is a device uint8 tensor of at
+    least :func:`pa_decode_workspace_bytes` bytes; one is allocated here when it is None
+    (with one partition it is optional and only orders the work). ``flags``: 0 or
+    ``PA_DECODE_KV_STREAM`` (no block is shared between the sequences of the call: K/V
+    loads bypass cache retention and the longest partitions are scheduled first).
     """
     head, tail, ws = _decode_args(out, q, kv_pool, block_tables, context_lens, max_context_len,
                                   scale, partition_size, workspace, torch.float16)
@@ -320,7 +324,7 @@ def _shared_prefix_args(out, q, kv_pool, block_tables, context_lens, max_context
 
 def pa_decode_shared_prefix(out, q, kv_pool, block_tables, context_lens, max_context_len,
                             group_start, prefix_lens, max_group_size, max_prefix_len,
-                            scale=None, partition_size=256, workspace=None, stream=None):
+                            scale=None, partition_size=512, workspace=None, stream=None):
     """pa_decode for groups of sequences sharing prefix blocks: group g is sequences
     group_start[g] .. group_start[g+1]-1 (device int32), sharing prefix_lens[g] tokens
     (device int32, multiples of the block size). Same result as pa_decode."""
@@ -334,7 +338,7 @@ def pa_decode_shared_prefix(out, q, kv_pool, block_tables, context_lens, max_con
 
 def pa_decode_shared_prefix_fp8(out, q, kv_pool, block_tables, context_lens, max_context_len,
                                 group_start, prefix_lens, max_group_size, max_prefix_len,
-                                scale=None, k_scale=1.0, v_scale=1.0, partition_size=256,
+                                scale=None, k_scale=1.0, v_scale=1.0, partition_size=512,
                                 workspace=None, stream=None):
     """pa_decode_shared_prefix over an FP8 (E4M3) pool held as a uint8 tensor, with its
     per-tensor scales."""
@@ -348,7 +352,7 @@ def pa_decode_shared_prefix_fp8(out, q, kv_pool, block_tables, context_lens, max
 
 
 def pa_decode_fp8(out, q, kv_pool, block_tables, context_lens, max_context_len, scale=None,
-                  k_scale=1.0, v_scale=1.0, partition_size=512, workspace=None, flags=0,
+                  k_scale=1.0, v_scale=1.0, partition_size=None, workspace=None, flags=0,
                   stream=None):
     """pa_decode over an FP8 (E4M3) pool held as a uint8 tensor, with its per-tensor scales."""
     head, tail, ws = _decode_args(out, q, kv_pool, block_tables, context_lens, max_context_len,
