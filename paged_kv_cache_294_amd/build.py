@@ -32,6 +32,10 @@ HIPCC_FLAGS = [
     "-Wno-unused-result",
     # no packed-fp32 instructions in generated code
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # matrix-core results in ordinary VGPRs rather than accumulation registers: the
+    # grouped-query decode kernel then needs 155 registers instead of 155 + 32 (three
+    # waves per SIMD instead of two)
+    "-mllvm", "-amdgpu-mfma-vgpr-form",
 ]
 
 
