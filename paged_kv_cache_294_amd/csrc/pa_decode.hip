@@ -7,7 +7,10 @@
 // Work split. A context is cut into partitions of `partition_blocks` blocks. One wave
 // handles one (sequence, KV head, partition) and all Hq/Hkv query heads reading that KV
 // head; a workgroup holds four consecutive KV heads of the same (sequence, partition),
-// so its loads touch neighbouring 256-byte rows of the same tokens.
+// so its loads touch neighbouring 256-byte rows of the same tokens. When no block is
+// shared and the items do not all fit on the GPU at once, a pre-pass lists them longest
+// first and the workgroups take them in that order (order_items_kernel); otherwise they
+// follow launch order (decode_item).
 //
 // Lane layout. A key (or value) row of one head is head_size fp16 = head_size/8
 // 16-byte pieces. Lane (r, c) = (lane / (D/8), lane % (D/8)) holds piece c of token r of
