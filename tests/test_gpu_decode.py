@@ -190,14 +190,25 @@ def test_decode_length_one_rows_are_exact():
             assert np.array_equal(bits(got[b, h]), bits(inp.value_new[b, h // 4]))
 
 
+def bench_partition_size(inp):
+    """The partition size bench.py runs a workload's decode with."""
+    return pkv.pa_decode_default_partition_size(inp.num_seqs - inp.num_prefill, inp.num_q_heads,
+                                                inp.num_kv_heads, int(inp.seq_lens.max()))
+
+
 def test_decode_config2_full():
     inp = cfg(2)
     d = Dev(inp)
     got = d.decode(partition_size=256)
     streamed = d.decode(partition_size=256, flags=pkv.PA_DECODE_KV_STREAM)
+    # bench.py's launch: its default partition size, no block shared (longest first)
+    ps = bench_partition_size(inp)
+    as_bench = d.decode(partition_size=ps, flags=pkv.PA_DECODE_KV_STREAM)
     del d
     free()
-    check_attention(got, oracle_decode(inp), "config2")
+    ref = oracle_decode(inp)
+    check_attention(got, ref, "config2")
+    check_attention(as_bench, ref, f"config2 as bench.py runs it (ps {ps})")
     # the cache hint changes no result bit
     assert np.array_equal(bits(got), bits(streamed))
 
@@ -223,18 +234,27 @@ def test_decode_config4_full_and_shared_equals_private():
     free()
     check_attention(got, oracle_decode(inp), "config4")
     priv = workloads.unshare_prefix(inp)
-    got2 = Dev(priv).decode()
+    dp = Dev(priv)
+    got2 = dp.decode()
+    # the private-copy workload (c4p) as bench.py runs it: no block shared
+    as_bench = dp.decode(partition_size=bench_partition_size(priv), flags=pkv.PA_DECODE_KV_STREAM)
+    del dp
     free()
     assert np.array_equal(bits(got), bits(got2)), "shared prefix blocks change the output"
+    check_attention(as_bench, oracle_decode(inp), "config4 private copies as bench.py runs it")
 
 
 def test_decode_config5_decode_part():
     inp = cfg(5)
     d = Dev(inp)
-    got = d.decode()
+    got = d.decode(partition_size=512)
+    ps = bench_partition_size(inp)
+    as_bench = d.decode(partition_size=ps, flags=pkv.PA_DECODE_KV_STREAM)
     del d
     free()
-    check_attention(got, oracle_decode(inp), "config5 decode")
+    ref = oracle_decode(inp)
+    check_attention(got, ref, "config5 decode")
+    check_attention(as_bench, ref, f"config5 decode as bench.py runs it (ps {ps})")
 
 
 # ---------------------------------------------------------------------------------------

@@ -78,6 +78,7 @@ def test_config4_full():
     inp = workloads.config4()
     gs = np.arange(0, 257, 4)
     pl = np.full(64, 1024)
-    note("shared prefix config 4")
-    got = run(inp, gs, pl, 256)
-    check_attention(got, oracle_out(inp), "config4 shared prefix")
+    ref = oracle_out(inp)
+    for ps in (256, 512):  # 512: the partition size bench.py runs it with
+        note(f"shared prefix config 4 ps={ps}")
+        check_attention(run(inp, gs, pl, ps), ref, f"config4 shared prefix ps{ps}")
