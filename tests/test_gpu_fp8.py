@@ -115,13 +115,16 @@ def test_decode_fp8_config2_sampled():
     ks, vs = 0.04, 0.03
     pool = quantized_pool(inp, ks, vs, seqs=rows)
     q, bt, lens = inp.decode_part()
-    out = torch.empty(q.shape, dtype=torch.float16, device="cuda")
-    ws = torch.empty(pkv.pa_decode_workspace_bytes(len(lens), 32, int(lens.max()), 256, 128),
-                     dtype=torch.uint8, device="cuda")
-    note("decode fp8 config 2, 4 sampled sequences, partitions of 256, streaming loads")
-    pkv.pa_decode_fp8(out, dev(q), dev(pool), dev(bt), dev(lens), int(lens.max()), inp.scale,
-                      ks, vs, 256, ws, pkv.PA_DECODE_KV_STREAM)
-    check_attention(host(out)[rows], oracle_decode_fp8(inp, pool, ks, vs, rows), "fp8 config 2")
+    want = oracle_decode_fp8(inp, pool, ks, vs, rows)
+    # partitions of 256, and bench.py's default size (one partition, longest first)
+    for ps in (256, pkv.pa_decode_default_partition_size(len(lens), 32, 32, int(lens.max()))):
+        out = torch.empty(q.shape, dtype=torch.float16, device="cuda")
+        ws = torch.empty(pkv.pa_decode_workspace_bytes(len(lens), 32, int(lens.max()), ps, 128),
+                         dtype=torch.uint8, device="cuda")
+        note(f"decode fp8 config 2, 4 sampled sequences, partitions of {ps}, streaming loads")
+        pkv.pa_decode_fp8(out, dev(q), dev(pool), dev(bt), dev(lens), int(lens.max()), inp.scale,
+                          ks, vs, ps, ws, pkv.PA_DECODE_KV_STREAM)
+        check_attention(host(out)[rows], want, f"fp8 config 2 ps{ps}")
 
 
 def test_decode_fp8_bad_rows_are_nan():
