@@ -5,13 +5,14 @@ A step is the whole hot path over one batch: ``pa_kv_append`` of this step's new
 into their pool slots, ``pa_prefill_chunk`` for prefill chunks (mixed workload only) and
 ``pa_decode`` (split-context partitions and their log-sum-exp merge). Workloads:
 
-  c1            4 tiny decode sequences (1, 15, 16, 33 tokens), 4 heads x 64: launch-bound
-  c2 (default)  256 decode sequences, context U{128..2048}, 32 heads x 128, + append
-  c3            8 sequences x 32768 tokens, 32 x 128 (64 partitions of 512)
-  c4            64 prompt groups x 4 samples sharing 64 blocks, 32q / 8kv heads x 128
-  c4p           c4 with private copies of the shared blocks (grouped-query decode from HBM)
-  c5            8 prefill chunks of 512 over priors U{0..3584} + 248 decodes U{256..4096},
-                append of all 4344 new tokens
+  tiny                 4 decode sequences (1, 15, 16, 33 tokens), 4 heads x 64: launch-bound
+  decode256 (default)  256 decode sequences, context U{128..2048}, 32 heads x 128, + append
+  long32k              8 sequences x 32768 tokens, 32 x 128 (split-context partitions)
+  prefix-groups        64 prompt groups x 4 samples sharing 64 blocks, 32q / 8kv heads x 128
+  prefix-private       prefix-groups with private copies of the shared blocks
+                       (grouped-query decode from HBM)
+  mixed                8 prefill chunks of 512 over priors U{0..3584} + 248 decodes
+                       U{256..4096}, append of all 4344 new tokens
 
 The timed steps replay the step captured once into a HIP graph (``--launch graph``, the
 default, as a serving engine runs it) or launch it call by call (``--launch eager``).
@@ -44,18 +45,18 @@ MFMA_F16_PEAK_TFLOPS = 2500.0   # MI355X dense fp16 matrix peak, vendor figure
 PROFILES = os.path.join(ROOT, "profiles")
 DECODE_SRC = os.path.join(ROOT, "paged_kv_cache_294_amd", "csrc", "pa_decode.hip")
 
-WORKLOADS = {
-    "c1": (1, "tiny decode: 4 sequences of 1, 15, 16, 33 tokens over a 16-block pool, "
+WORKLOADS = {  # name: (generator in workloads.WORKLOADS, description)
+    "tiny": ("tiny", "tiny decode: 4 sequences of 1, 15, 16, 33 tokens over a 16-block pool, "
               "4 heads x 64, block 16, fp16 (launch-bound)"),
-    "c2": (2, "decode step: kv_append of 256 tokens + paged decode of 256 sequences, "
+    "decode256": ("decode256", "decode step: kv_append of 256 tokens + paged decode of 256 sequences, "
               "context U{128..2048}, 32 heads x 128, block 16, fp16, shuffled blocks"),
-    "c3": (3, "long-context decode: 8 sequences x 32768 tokens, 32 heads x 128, block 16, "
+    "long32k": ("long32k", "long-context decode: 8 sequences x 32768 tokens, 32 heads x 128, block 16, "
               "fp16, split-context partitions"),
-    "c4": (4, "prefix-shared GQA decode: 64 groups x 4 samples, 1024-token shared prompt "
+    "prefix-groups": ("prefix-groups", "prefix-shared GQA decode: 64 groups x 4 samples, 1024-token shared prompt "
               "(64 blocks) + 64..256 private tokens, 32 q / 8 kv heads x 128, fp16"),
-    "c4p": (4, "config 4 with private copies of every shared prefix block (no sharing): "
-               "256 GQA sequences of 1088..1280 tokens, 32 q / 8 kv heads x 128, fp16"),
-    "c5": (5, "mixed step: kv_append of 4344 tokens + 8 prefill chunks of 512 over priors "
+    "prefix-private": ("prefix-groups", "the prefix-groups batch with private copies of "
+                       "every shared prefix block (no sharing): 256 GQA sequences of 1088..1280 tokens, 32 q / 8 kv heads x 128, fp16"),
+    "mixed": ("mixed", "mixed step: kv_append of 4344 tokens + 8 prefill chunks of 512 over priors "
               "U{0..3584} + 248 decodes U{256..4096}, 32 heads x 128, fp16"),
 }
 
@@ -486,7 +487,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", choices=sorted(WORKLOADS), default="c2")
+    ap.add_argument("--workload", choices=sorted(WORKLOADS), default="decode256")
     ap.add_argument("--partition-size", type=int, default=0,
                     help="decode partition in tokens; 0 (default): the library's "
                          "pa_decode_default_partition_size for the workload (512 for "
@@ -538,11 +539,12 @@ def main():
               file=sys.stderr)
         sys.exit(2)
 
-    seed, desc = WORKLOADS[args.workload]
-    log(f"generating workload {args.workload} (seed {seed})")
+    gen, desc = WORKLOADS[args.workload]
+    log(f"generating workload {args.workload}")
     t0 = time.perf_counter()
-    inp = workloads.CONFIGS[seed]()
-    if args.workload == "c4p":
+    inp = workloads.WORKLOADS[gen]()
+    seed = inp.seed
+    if args.workload == "prefix-private":
         inp = workloads.unshare_prefix(inp)
     log(f"generated in {time.perf_counter() - t0:.1f}s: {inp.num_blocks} blocks, "
         f"{inp.num_seqs} sequences, sum L = {int(inp.seq_lens.sum())}")
@@ -553,7 +555,7 @@ def main():
     shared_prefix = {"plain": False, "shared-prefix": True,
                      "auto": bool(inp.prefix_blocks)}[args.decode]
     if shared_prefix and not inp.prefix_blocks:
-        print("--decode shared-prefix needs prompt groups (workload c4)", file=sys.stderr)
+        print("--decode shared-prefix needs prompt groups (workload prefix-groups)", file=sys.stderr)
         sys.exit(2)
     if args.partition_size <= 0 and shared_prefix:
         args.partition_size = 512  # fastest of 256 .. 2048 for 64 groups of 1024-token prompts
@@ -576,7 +578,7 @@ def main():
         log("CPU baseline skipped for the FP8 cache (the oracle's fp16 run is the reference)")
     elif not args.no_cpu_baseline:
         log("CPU baseline: oracle on the host cores")
-        cpu = cpu_baseline(inp, args.cpu_cores, decode_seqs=4 if args.workload == "c3" else None)
+        cpu = cpu_baseline(inp, args.cpu_cores, decode_seqs=4 if args.workload == "long32k" else None)
         log(f"CPU baseline done in {cpu['seconds']:.1f}s on {cpu['cores']} cores")
 
     import torch

@@ -54,9 +54,9 @@ def oracle_decode(inp, pool=None):
 
 
 @functools.lru_cache(maxsize=2)
-def cfg(i):
-    note(f"generating config {i}")
-    return workloads.CONFIGS[i]()
+def cfg(name):
+    note(f"generating workload {name}")
+    return workloads.WORKLOADS[name]()
 
 
 def free():
@@ -78,11 +78,11 @@ def check_append(inp):
 
 
 def test_append_tiny_full_into_nan_pool():
-    inp = workloads.config1_full_append()
+    inp = workloads.tiny_decode_full_append()
     check_append(inp)
     # the appended pool is the tiny decode batch's pool
     d = Dev(inp, append=True)
-    assert np.array_equal(bits(host(d.pool)), bits(workloads.config1().pool))
+    assert np.array_equal(bits(host(d.pool)), bits(workloads.tiny_decode().pool))
 
 
 def test_append_small_mixed_and_ragged():
@@ -116,12 +116,12 @@ def test_append_strided_rows():
     assert np.array_equal(bits(host(pool)), bits(oracle_pool(inp)))
 
 
-def test_append_config2_full():
-    check_append(cfg(2))
+def test_append_decode256_full():
+    check_append(cfg("decode256"))
 
 
-def test_append_config5_full():
-    check_append(cfg(5))
+def test_append_mixed_full():
+    check_append(cfg("mixed"))
 
 
 # ---------------------------------------------------------------------------------------
@@ -142,7 +142,7 @@ def check_gather(inp, seqs=None):
 
 
 def test_gather_tiny():
-    check_gather(workloads.config1())
+    check_gather(workloads.tiny_decode())
 
 
 def test_gather_shared_and_mixed():
@@ -150,8 +150,8 @@ def test_gather_shared_and_mixed():
     check_gather(workloads.mixed_case(36, [0, 33], [17, 40], [2, 100], 4, 4, 128))
 
 
-def test_gather_config2_sampled():
-    check_gather(cfg(2), seqs=[0, 1, 77, 255])
+def test_gather_decode256_sampled():
+    check_gather(cfg("decode256"), seqs=[0, 1, 77, 255])
     free()
 
 
@@ -160,7 +160,7 @@ def test_gather_config2_sampled():
 # ---------------------------------------------------------------------------------------
 
 def test_decode_tiny():
-    inp = workloads.config1()
+    inp = workloads.tiny_decode()
     got = Dev(inp).decode()
     ref = oracle_decode(inp)
     check_attention(got, ref, "tiny")
@@ -196,8 +196,8 @@ def bench_partition_size(inp):
                                                 inp.num_kv_heads, int(inp.seq_lens.max()))
 
 
-def test_decode_config2_full():
-    inp = cfg(2)
+def test_decode_decode256_full():
+    inp = cfg("decode256")
     d = Dev(inp)
     got = d.decode(partition_size=256)
     streamed = d.decode(partition_size=256, flags=pkv.PA_DECODE_KV_STREAM)
@@ -207,14 +207,14 @@ def test_decode_config2_full():
     del d
     free()
     ref = oracle_decode(inp)
-    check_attention(got, ref, "config2")
-    check_attention(as_bench, ref, f"config2 as bench.py runs it (ps {ps})")
+    check_attention(got, ref, "decode256")
+    check_attention(as_bench, ref, f"decode256 as bench.py runs it (ps {ps})")
     # the cache hint changes no result bit
     assert np.array_equal(bits(got), bits(streamed))
 
 
-def test_decode_config3_sampled():
-    inp = cfg(3)
+def test_decode_long32k_sampled():
+    inp = cfg("long32k")
     d = Dev(inp)
     outs = {ps: d.decode(partition_size=ps, flags=pkv.PA_DECODE_KV_STREAM) for ps in (512, 2048)}
     del d
@@ -224,15 +224,15 @@ def test_decode_config3_sampled():
     ref = oracle.decode_rows(inp.q, inp.pool, inp.block_tables, inp.seq_lens, inp.scale, pairs)
     for ps, got in outs.items():
         rows = np.stack([got[b, h] for b, h in pairs])
-        check_attention(rows, ref, f"config3 ps{ps}")
+        check_attention(rows, ref, f"long32k ps{ps}")
     assert np.abs(outs[512].astype(np.float64) - outs[2048].astype(np.float64)).max() <= 1e-4
 
 
-def test_decode_config4_full_and_shared_equals_private():
-    inp = cfg(4)
+def test_decode_prefix_groups_full_and_shared_equals_private():
+    inp = cfg("prefix-groups")
     got = Dev(inp).decode()
     free()
-    check_attention(got, oracle_decode(inp), "config4")
+    check_attention(got, oracle_decode(inp), "prefix-groups")
     priv = workloads.unshare_prefix(inp)
     dp = Dev(priv)
     got2 = dp.decode()
@@ -241,11 +241,11 @@ def test_decode_config4_full_and_shared_equals_private():
     del dp
     free()
     assert np.array_equal(bits(got), bits(got2)), "shared prefix blocks change the output"
-    check_attention(as_bench, oracle_decode(inp), "config4 private copies as bench.py runs it")
+    check_attention(as_bench, oracle_decode(inp), "prefix-groups private copies as bench.py runs it")
 
 
-def test_decode_config5_decode_part():
-    inp = cfg(5)
+def test_decode_mixed_decode_part():
+    inp = cfg("mixed")
     d = Dev(inp)
     got = d.decode(partition_size=512)
     ps = bench_partition_size(inp)
@@ -253,8 +253,8 @@ def test_decode_config5_decode_part():
     del d
     free()
     ref = oracle_decode(inp)
-    check_attention(got, ref, "config5 decode")
-    check_attention(as_bench, ref, f"config5 decode as bench.py runs it (ps {ps})")
+    check_attention(got, ref, "mixed decode")
+    check_attention(as_bench, ref, f"mixed decode as bench.py runs it (ps {ps})")
 
 
 # ---------------------------------------------------------------------------------------

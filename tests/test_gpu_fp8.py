@@ -63,11 +63,11 @@ def test_append_fp8_bit_exact(k_scale, v_scale):
     assert np.array_equal(host(pd), want)
 
 
-def test_append_fp8_config2_bit_exact():
-    inp = workloads.config2()
+def test_append_fp8_decode256_bit_exact():
+    inp = workloads.decode_256seq()
     pool = np.zeros((inp.num_blocks, 16, 2, 32, 128), np.uint8)
     pool[:] = 0x7F
-    note("append fp8 config 2 (256 tokens)")
+    note("append fp8 decode256 (256 tokens)")
     pd = dev(pool)
     pkv.pa_kv_append_fp8(pd, dev(inp.key_new), dev(inp.value_new), dev(inp.slot_mapping), 0.05, 0.07)
     got = host(pd)
@@ -109,8 +109,8 @@ def test_decode_fp8_length_one_is_the_value_row():
         assert np.array_equal(got[b], want)
 
 
-def test_decode_fp8_config2_sampled():
-    inp = workloads.config2()
+def test_decode_fp8_decode256_sampled():
+    inp = workloads.decode_256seq()
     rows = np.array([0, 37, 101, 255])
     ks, vs = 0.04, 0.03
     pool = quantized_pool(inp, ks, vs, seqs=rows)
@@ -121,10 +121,10 @@ def test_decode_fp8_config2_sampled():
         out = torch.empty(q.shape, dtype=torch.float16, device="cuda")
         ws = torch.empty(pkv.pa_decode_workspace_bytes(len(lens), 32, int(lens.max()), ps, 128),
                          dtype=torch.uint8, device="cuda")
-        note(f"decode fp8 config 2, 4 sampled sequences, partitions of {ps}, streaming loads")
+        note(f"decode fp8 decode256, 4 sampled sequences, partitions of {ps}, streaming loads")
         pkv.pa_decode_fp8(out, dev(q), dev(pool), dev(bt), dev(lens), int(lens.max()), inp.scale,
                           ks, vs, ps, ws, pkv.PA_DECODE_KV_STREAM)
-        check_attention(host(out)[rows], want, f"fp8 config 2 ps{ps}")
+        check_attention(host(out)[rows], want, f"fp8 decode256 ps{ps}")
 
 
 def test_decode_fp8_bad_rows_are_nan():
@@ -207,14 +207,14 @@ def test_shared_prefix_fp8_matches_oracle(G):
         check_attention(got, want, f"shared fp8 G{G} ps{ps}")
 
 
-def test_shared_prefix_fp8_config4():
-    inp = workloads.config4()
+def test_shared_prefix_fp8_prefix_groups():
+    inp = workloads.shared_prompt_groups()
     pool = np.concatenate([fp8.quantize(inp.pool[:, :, 0:1], 1.0),
                            fp8.quantize(inp.pool[:, :, 1:2], 1.0)], axis=2)
-    note("shared prefix fp8 config 4")
+    note("shared prefix fp8 prefix-groups")
     got = run_shared_fp8(inp, pool, 1.0, 1.0, np.arange(0, 257, 4), np.full(64, 1024), 512)
     q, bt, L = inp.decode_part()
     rng = np.random.default_rng(0)
     pairs = [(int(b), int(h)) for b, h in zip(rng.integers(0, 256, 200), rng.integers(0, 32, 200))]
     want = oracle.decode_rows(q, fp8.dequantize_pool(pool, 1.0, 1.0), bt, L, inp.scale, pairs)
-    check_attention(np.stack([got[b, h] for b, h in pairs]), want, "shared fp8 config4")
+    check_attention(np.stack([got[b, h] for b, h in pairs]), want, "shared fp8 prefix-groups")

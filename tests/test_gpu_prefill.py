@@ -60,18 +60,18 @@ def test_prefill_long_prior():
 
 
 @functools.lru_cache(maxsize=1)
-def config5():
-    note("generating config 5")
-    return workloads.config5()
+def mixed_workload():
+    note("generating mixed")
+    return workloads.mixed_prefill_decode()
 
 
-def test_prefill_config5_full():
-    inp = config5()
+def test_prefill_mixed_full():
+    inp = mixed_workload()
     got, pool = gpu_prefill(inp)
     del pool
     torch.cuda.empty_cache()
-    note("oracle prefill of config 5 (4096 rows x 32 heads)")
-    check_attention(got, oracle_prefill(inp), "config5 prefill")
+    note("oracle prefill of mixed (4096 rows x 32 heads)")
+    check_attention(got, oracle_prefill(inp), "mixed prefill")
 
 
 def test_prefill_row_matches_decode_kernel():

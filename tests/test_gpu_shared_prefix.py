@@ -2,7 +2,7 @@
 grouping only changes how the work is split, never the result. Groups of several sizes
 (more samples than one tile holds, singletons), prefixes shorter than what is actually
 shared, members with no tokens of their own, every group size of query heads, one and
-several partitions, bad groups and prefixes (NaN rows), and the whole of config 4."""
+several partitions, bad groups and prefixes (NaN rows), and the whole of prefix-groups."""
 
 import numpy as np
 import pytest
@@ -74,11 +74,11 @@ def test_bad_groups_and_prefixes_are_nan():
     check_attention(got2[:8], oracle_out(one)[:8], "covered samples")
 
 
-def test_config4_full():
-    inp = workloads.config4()
+def test_prefix_groups_full():
+    inp = workloads.shared_prompt_groups()
     gs = np.arange(0, 257, 4)
     pl = np.full(64, 1024)
     ref = oracle_out(inp)
     for ps in (256, 512):  # 512: the partition size bench.py runs it with
-        note(f"shared prefix config 4 ps={ps}")
-        check_attention(run(inp, gs, pl, ps), ref, f"config4 shared prefix ps{ps}")
+        note(f"shared prefix prefix-groups ps={ps}")
+        check_attention(run(inp, gs, pl, ps), ref, f"prefix-groups shared prefix ps{ps}")

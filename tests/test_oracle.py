@@ -65,8 +65,8 @@ def test_gather_matches_logical(make):
     pins.check_gather_matches_logical(make())
 
 
-def test_gather_config1():
-    pins.check_gather_matches_logical(workloads.config1())
+def test_gather_tiny():
+    pins.check_gather_matches_logical(workloads.tiny_decode())
 
 
 @pytest.mark.parametrize("make", [mha_case, gqa_case, mixed_case])
@@ -74,8 +74,8 @@ def test_decode_vs_sdpa(make):
     pins.check_decode_vs_sdpa(make())
 
 
-def test_decode_vs_sdpa_config1():
-    pins.check_decode_vs_sdpa(workloads.config1())
+def test_decode_vs_sdpa_tiny():
+    pins.check_decode_vs_sdpa(workloads.tiny_decode())
 
 
 def test_decode_vs_brute_force():
@@ -127,10 +127,10 @@ def test_kv_append(make):
     pins.check_kv_append(make())
 
 
-def test_kv_append_full_config1():
+def test_kv_append_full_tiny():
     """All 65 tokens of the tiny batch appended into an all-NaN pool rebuild its pool bit for bit."""
-    base = workloads.config1()
-    full = workloads.config1_full_append()
+    base = workloads.tiny_decode()
+    full = workloads.tiny_decode_full_append()
     pins.check_kv_append(full)
     out = opa.kv_append(full.pool, full.key_new, full.value_new, full.slot_mapping)
     assert np.array_equal(out.view(np.uint16), base.pool.view(np.uint16))

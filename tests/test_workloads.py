@@ -21,7 +21,7 @@ def _same(a, b):
 
 
 def test_deterministic_per_seed():
-    _same(workloads.config1(), workloads.config1())
+    _same(workloads.tiny_decode(), workloads.tiny_decode())
     a = workloads.mixed_case(3, [0, 40], [16, 20], [5, 70], 4, 2, 32)
     b = workloads.mixed_case(3, [0, 40], [16, 20], [5, 70], 4, 2, 32)
     _same(a, b)
@@ -35,8 +35,8 @@ def test_keep_logical_does_not_change_values():
     _same(a, b)
 
 
-def test_config1_recipe():
-    inp = workloads.config1()
+def test_tiny_recipe():
+    inp = workloads.tiny_decode()
     assert inp.pool.shape == (16, 16, 2, 4, 64)
     assert list(inp.seq_lens) == [1, 15, 16, 33]
     assert inp.scale == 1.0 / 8.0
@@ -76,8 +76,8 @@ def test_repermute_and_unshare_keep_values():
                                       inp.logical_kv[b][pos].view(np.uint16))
 
 
-def test_config4_sharing_structure():
-    inp = workloads.config4()
+def test_prefix_groups_sharing_structure():
+    inp = workloads.shared_prompt_groups()
     assert inp.num_q_heads == 32 and inp.num_kv_heads == 8 and inp.head_size == 128
     assert inp.num_seqs == 256
     for g in range(64):
@@ -88,10 +88,10 @@ def test_config4_sharing_structure():
     assert priv.min() >= 64 and priv.max() <= 256
 
 
-def test_config5_fits_the_scheduler_limits():
+def test_mixed_fits_the_scheduler_limits():
     """The mixed step obeys the scheduler sketch's budget: 8192 tokens, 256 sequences
     (page "vLLM 部署深度指南", continuous-batching scheduler listing)."""
-    inp = workloads.config5()
+    inp = workloads.mixed_prefill_decode()
     assert inp.num_seqs <= 256
     tokens = int(inp.q_lens.sum())
     assert tokens == 8 * 512 + 248 <= 8192

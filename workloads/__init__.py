@@ -9,16 +9,16 @@ from .synth import (  # noqa: F401
     POISON_F16,
     PagedInputs,
     build,
-    config1,
-    config1_full_append,
-    config2,
-    config3,
-    config4,
-    config5,
+    tiny_decode,
+    tiny_decode_full_append,
+    decode_256seq,
+    long_context_32k,
+    shared_prompt_groups,
+    mixed_prefill_decode,
     decode_case,
     mixed_case,
     prefix_shared_case,
     repermute,
     unshare_prefix,
-    CONFIGS,
+    WORKLOADS,
 )

@@ -368,7 +368,7 @@ def prefix_shared_case(seed, num_groups, samples, prefix_blocks, private_lens, n
 # the five frozen workloads
 # ---------------------------------------------------------------------------------------
 
-def config1(keep_logical=True) -> PagedInputs:
+def tiny_decode(keep_logical=True) -> PagedInputs:
     """Tiny paged decode: lengths {1, 15, 16, 33}, 4 heads x 64, 16 physical blocks."""
     rng = np.random.default_rng(1)
     lens = np.array([1, 15, 16, 33])
@@ -376,9 +376,9 @@ def config1(keep_logical=True) -> PagedInputs:
                  keep_logical=keep_logical, scale=1.0 / 8.0, name="tiny-decode-4x{1,15,16,33}")
 
 
-def config1_full_append() -> PagedInputs:
+def tiny_decode_full_append() -> PagedInputs:
     """The tiny decode batch with every one of its 65 tokens appended into an all-NaN pool."""
-    base = config1(keep_logical=True)
+    base = tiny_decode(keep_logical=True)
     inp = dataclasses.replace(base)
     pool = np.empty_like(base.pool)
     pool.view(np.uint16).fill(POISON_F16)
@@ -396,7 +396,7 @@ def config1_full_append() -> PagedInputs:
     return inp
 
 
-def config2(keep_logical=False) -> PagedInputs:
+def decode_256seq(keep_logical=False) -> PagedInputs:
     """Llama-7B-layer-shaped decode: 256 sequences, lengths U{128..2048}, 32 x 128, append."""
     rng = np.random.default_rng(2)
     lens = rng.integers(128, 2048, size=256, endpoint=True)
@@ -404,7 +404,7 @@ def config2(keep_logical=False) -> PagedInputs:
                  keep_logical=keep_logical, name="decode-256seq-U[128,2048]-32x128")
 
 
-def config3(keep_logical=False) -> PagedInputs:
+def long_context_32k(keep_logical=False) -> PagedInputs:
     """Long-context decode: 8 sequences of 32768 tokens, 32 x 128."""
     rng = np.random.default_rng(3)
     lens = np.full(8, 32768)
@@ -413,7 +413,7 @@ def config3(keep_logical=False) -> PagedInputs:
                  name="decode-8seq-32768-32x128")
 
 
-def config4(keep_logical=False) -> PagedInputs:
+def shared_prompt_groups(keep_logical=False) -> PagedInputs:
     """Prefix-shared GQA decode: 64 groups x 4 samples, 64 shared blocks, 32q/8kv x 128."""
     rng = np.random.default_rng(4)
     priv = rng.integers(64, 256, size=256, endpoint=True)
@@ -424,7 +424,7 @@ def config4(keep_logical=False) -> PagedInputs:
                  name="gqa-prefix-shared-64x4-32q8kv")
 
 
-def config5(keep_logical=False) -> PagedInputs:
+def mixed_prefill_decode(keep_logical=False) -> PagedInputs:
     """Mixed step: 8 prefill chunks of 512 over priors U{0..3584}, 248 decodes U{256..4096}."""
     rng = np.random.default_rng(5)
     pri = np.empty(8, np.int64)
@@ -438,7 +438,8 @@ def config5(keep_logical=False) -> PagedInputs:
                  keep_logical=keep_logical, name="mixed-8x512prefill+248decode-32x128")
 
 
-CONFIGS = {1: config1, 2: config2, 3: config3, 4: config4, 5: config5}
+WORKLOADS = {"tiny": tiny_decode, "decode256": decode_256seq, "long32k": long_context_32k,
+             "prefix-groups": shared_prompt_groups, "mixed": mixed_prefill_decode}
 
 
 # ---------------------------------------------------------------------------------------
