@@ -13,6 +13,9 @@ into their pool slots, ``pa_prefill_chunk`` for prefill chunks (mixed workload o
                        (grouped-query decode from HBM)
   mixed                8 prefill chunks of 512 over priors U{0..3584} + 248 decodes
                        U{256..4096}, append of all 4344 new tokens
+  long-prefill         the last 512-row chunk of a 32768-token prompt + 8 decodes
+                       U{256..4096} (few row tiles over a long context: the prefill's
+                       context split)
 
 The timed steps replay the step captured once into a HIP graph (``--launch graph``, the
 default, as a serving engine runs it) or launch it call by call (``--launch eager``).
@@ -58,6 +61,8 @@ WORKLOADS = {  # name: (generator in workloads.WORKLOADS, description)
                        "every shared prefix block (no sharing): 256 GQA sequences of 1088..1280 tokens, 32 q / 8 kv heads x 128, fp16"),
     "mixed": ("mixed", "mixed step: kv_append of 4344 tokens + 8 prefill chunks of 512 over priors "
               "U{0..3584} + 248 decodes U{256..4096}, 32 heads x 128, fp16"),
+    "long-prefill": ("long-prefill", "long-prompt step: kv_append of 520 tokens + the last 512-row "
+                     "chunk of a 32768-token prompt + 8 decodes U{256..4096}, 32 heads x 128, fp16"),
 }
 
 
@@ -109,7 +114,13 @@ def shares_blocks(inp) -> bool:
 
 
 def source_digest(path) -> str:
-    return hashlib.sha256(open(path, "rb").read()).hexdigest()[:16]
+    """Digest of a kernel source together with the shared device header and the build
+    script (its compiler flags change the code as much as the source does)."""
+    h = hashlib.sha256()
+    for f in (path, os.path.join(os.path.dirname(path), "pa_device.h"),
+              os.path.join(ROOT, "paged_kv_cache_294_amd", "build.py")):
+        h.update(open(f, "rb").read())
+    return h.hexdigest()[:16]
 
 
 def read_traffic(name, digest):
@@ -303,7 +314,7 @@ class Step:
     """Device copies of a batch and one step of the hot path over them."""
 
     def __init__(self, torch, pkv, inp, partition_size, kv_stream, kv_fp8=False,
-                 shared_prefix=False):
+                 shared_prefix=False, prefill_split=True):
         self.torch, self.pkv, self.inp = torch, pkv, inp
 
         def c(a):
@@ -343,6 +354,12 @@ class Step:
             self.pout = torch.empty_like(self.pq)
             self.max_q = int(np.diff(qsl).max())
             self.max_s = int(lensp.max())
+            # split-context workspace (caller-owned, so the captured graph uses it too)
+            self.pws_bytes = (pkv.pa_prefill_workspace_bytes(len(lensp), inp.num_q_heads, self.max_q,
+                                                             self.max_s, inp.head_size)
+                              if prefill_split else 0)
+            self.pws = (torch.empty(self.pws_bytes, dtype=torch.uint8, device="cuda")
+                        if self.pws_bytes > 0 else None)
 
     def run(self, ev=None, stream=None):
         pkv = self.pkv
@@ -360,10 +377,12 @@ class Step:
         rec(1)
         if self.has_prefill and self.kv_fp8:
             pkv.pa_prefill_chunk_fp8(self.pout, self.pq, self.pool, self.pbt, self.qsl, self.plens,
-                                     self.max_q, self.max_s, self.inp.scale, 1.0, 1.0, stream=stream)
+                                     self.max_q, self.max_s, self.inp.scale, 1.0, 1.0,
+                                     workspace=self.pws, split=self.pws is not None, stream=stream)
         elif self.has_prefill:
             pkv.pa_prefill_chunk(self.pout, self.pq, self.pool, self.pbt, self.qsl, self.plens,
-                                 self.max_q, self.max_s, self.inp.scale, stream=stream)
+                                 self.max_q, self.max_s, self.inp.scale, workspace=self.pws,
+                                 split=self.pws is not None, stream=stream)
         rec(2)
         if self.shared_prefix and self.kv_fp8:
             pkv.pa_decode_shared_prefix_fp8(self.dout, self.dq, self.pool, self.dbt, self.dlens,
@@ -508,6 +527,9 @@ def main():
     ap.add_argument("--kv-dtype", choices=("fp16", "fp8"), default="fp16",
                     help="cache element: fp16, or FP8 E4M3 codes (decode-only workloads; the "
                          "prefill kernel reads fp16 caches only)")
+    ap.add_argument("--prefill-split", choices=("on", "off"), default="on",
+                    help="on: pa_prefill_chunk gets its split-context workspace (long contexts "
+                         "cut into pieces merged by log-sum-exp); off: one workgroup per row tile")
     ap.add_argument("--cpu-cores", type=int, default=16)
     ap.add_argument("--mode", choices=("bench", "counters"), default="bench",
                     help="counters: a short fixed dispatch sequence for rocprofv3 --pmc passes "
@@ -600,7 +622,8 @@ def main():
         log(f"host block manager: admit {bm['admit_us']:.0f} us, step {bm['step_us']:.0f} us "
             f"({bm['new_tokens']} slots + tables)")
     log("copying the batch to the GPU")
-    step = Step(torch, pkv, inp, args.partition_size, kv_stream, kv_fp8, shared_prefix)
+    step = Step(torch, pkv, inp, args.partition_size, kv_stream, kv_fp8, shared_prefix,
+                args.prefill_split == "on")
     for _ in range(args.warmup):
         step.run()
     torch.cuda.synchronize()
@@ -666,7 +689,8 @@ def main():
         fl = prefill_flops(inp)
         tf = fl / (prefill_ms * 1e-3) / 1e12
         kernels["prefill"] = {"us": prefill_ms * 1e3, "gflop": fl / 1e9, "TFLOPs": tf,
-                              "frac_mfma_peak": tf / MFMA_F16_PEAK_TFLOPS}
+                              "frac_mfma_peak": tf / MFMA_F16_PEAK_TFLOPS,
+                              "split_workspace_bytes": step.pws_bytes}
     if shared:
         kernels["decode"]["logical_kv_bytes"] = logical_bytes
         kernels["decode"]["logical_kv_GBps"] = logical_bytes / (decode_ms * 1e-3) / 1e9

@@ -248,7 +248,8 @@ pa_status pa_prefill_chunk_fp8(void* out, const void* q, const void* kv_pool,
                                int32_t max_q_len, int32_t max_seq_len, int32_t num_q_heads,
                                int32_t num_kv_heads, int32_t head_size, int32_t block_size,
                                int32_t max_blocks_per_seq, int64_t num_blocks, float scale,
-                               float k_scale, float v_scale, void* stream);
+                               float k_scale, float v_scale, void* workspace,
+                               int64_t workspace_bytes, void* stream);
 pa_status pa_decode_shared_prefix_fp8(void* out, const void* q, const void* kv_pool,
                                       const int32_t* block_tables, const int32_t* context_lens,
                                       int32_t num_seqs, int32_t num_q_heads,
@@ -277,6 +278,15 @@ pa_status pa_decode_shared_prefix_fp8(void* out, const void* q, const void* kv_p
  *                    and <= max_blocks_per_seq * block_size; rows of a request that breaks
  *                    these bounds, or whose table holds an entry outside [0, num_blocks),
  *                    are set to NaN
+ *   workspace        optional device memory of pa_prefill_workspace_bytes(...) bytes,
+ *                    16-byte aligned, owned by the caller, contents not kept between
+ *                    calls (calls sharing one workspace must not overlap). NULL: every
+ *                    128-row tile of a chunk runs over its whole context in one workgroup.
+ *                    Given: the library may cut long contexts into pieces run by separate
+ *                    workgroups, their fp32 partial results merged by log-sum-exp in a
+ *                    second kernel (the same split-context merge as decode), so that few
+ *                    or uneven requests still fill the GPU. Fewer bytes than needed:
+ *                    PA_ERR_WORKSPACE.
  * Arithmetic: fp16 inputs on the matrix cores with fp32 accumulation, fp32 softmax,
  * fp16 output rounded to nearest even. */
 pa_status pa_prefill_chunk(void* out, const void* q, const void* kv_pool,
@@ -285,7 +295,15 @@ pa_status pa_prefill_chunk(void* out, const void* q, const void* kv_pool,
                            int32_t max_q_len, int32_t max_seq_len, int32_t num_q_heads,
                            int32_t num_kv_heads, int32_t head_size, int32_t block_size,
                            int32_t max_blocks_per_seq, int64_t num_blocks, float scale,
-                           void* stream);
+                           void* workspace, int64_t workspace_bytes, void* stream);
+
+/* Workspace bytes that pa_prefill_chunk and pa_prefill_chunk_fp8 take for these sizes
+ * on the current device (the split depends on how many workgroups it holds at once):
+ * 0 when no split would help (the call then uses no workspace), -1 for bad sizes
+ * (num_reqs < 0, num_q_heads <= 0, max_q_len < 0, max_seq_len < max_q_len, head_size
+ * not 64 or 128). */
+int64_t pa_prefill_workspace_bytes(int32_t num_reqs, int32_t num_q_heads, int32_t max_q_len,
+                                   int32_t max_seq_len, int32_t head_size);
 
 /* Copy one sequence's keys and values, in logical order, out of the pool: the
  * block-table indexing of the attention kernels, made visible bit for bit.

@@ -37,6 +37,7 @@ from ._lib import (  # noqa: F401
     pa_pool_bytes,
     pa_prefill_chunk,
     pa_prefill_chunk_fp8,
+    pa_prefill_workspace_bytes,
     pa_slot,
     pa_stream_read,
     pa_stream_read_sink_len,

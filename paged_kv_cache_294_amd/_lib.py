@@ -54,10 +54,11 @@ SIGNATURES = {
                                                    _vp, _vp, _i32, _i32, _i32, _vp, _i64, _vp]),
     "pa_decode_shared_prefix_workspace_bytes": (_i64, [_i32, _i32, _i32, _i32, _i32, _i32]),
     "pa_prefill_chunk": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32,
-                                        _i32, _i32, _i32, _i32, _i64, _f32, _vp]),
+                                        _i32, _i32, _i32, _i32, _i64, _f32, _vp, _i64, _vp]),
     "pa_prefill_chunk_fp8": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32,
                                             _i32, _i32, _i32, _i32, _i32, _i64, _f32, _f32, _f32,
-                                            _vp]),
+                                            _vp, _i64, _vp]),
+    "pa_prefill_workspace_bytes": (_i64, [_i32, _i32, _i32, _i32, _i32]),
     "pa_gather_kv": (ctypes.c_int, [_vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i64, _vp]),
     "pa_stream_read": (ctypes.c_int, [_vp, _i64, _vp, _vp]),
     "pa_stream_read_sink_len": (_i64, [_i64]),
@@ -380,22 +381,51 @@ def _prefill_args(out, q, kv_pool, block_tables, query_start_loc, seq_lens, max_
             hq, hkv, d, bs, int(block_tables.shape[1]), nb, float(scale))
 
 
+def pa_prefill_workspace_bytes(num_reqs, num_q_heads, max_q_len, max_seq_len, head_size) -> int:
+    """Bytes of the optional split-context workspace of pa_prefill_chunk (0: no split helps)."""
+    return load().pa_prefill_workspace_bytes(int(num_reqs), int(num_q_heads), int(max_q_len),
+                                             int(max_seq_len), int(head_size))
+
+
+def _prefill_workspace(args, workspace, split, device):
+    """(pointer, bytes) of the workspace for a prefill call: none when split is off or no
+    split helps; one the caller gave; else a new one (not under graph capture, where the
+    call then runs unsplit)."""
+    if not split:
+        return 0, 0
+    R, hq, mq, ms, d = args[6], args[10], args[8], args[9], args[12]
+    need = pa_prefill_workspace_bytes(R, hq, mq, ms, d)
+    if need < 0:
+        raise PagedKVError("pa_prefill_workspace_bytes", PA_ERR_INVALID)
+    if need == 0:
+        return 0, 0
+    if workspace is None:
+        if _CAPTURING:
+            return 0, 0
+        workspace = torch.empty(need, dtype=torch.uint8, device=device)
+    return _dense(workspace, "workspace", torch.uint8), workspace.numel()
+
+
 def pa_prefill_chunk(out, q, kv_pool, block_tables, query_start_loc, seq_lens, max_q_len,
-                     max_seq_len, scale=None, stream=None):
-    """Causal attention of prefill chunks (rows of q [total_q, Hq, D]) over their paged context."""
-    st = load().pa_prefill_chunk(*_prefill_args(out, q, kv_pool, block_tables, query_start_loc,
-                                                seq_lens, max_q_len, max_seq_len, scale,
-                                                torch.float16), _stream(stream))
+                     max_seq_len, scale=None, workspace=None, split=True, stream=None):
+    """Causal attention of prefill chunks (rows of q [total_q, Hq, D]) over their paged context.
+    split: let the library cut long contexts into pieces merged by log-sum-exp (in
+    `workspace`, a uint8 tensor of pa_prefill_workspace_bytes bytes, allocated if None)."""
+    args = _prefill_args(out, q, kv_pool, block_tables, query_start_loc, seq_lens, max_q_len,
+                         max_seq_len, scale, torch.float16)
+    ws = _prefill_workspace(args, workspace, split, q.device)
+    st = load().pa_prefill_chunk(*args, *ws, _stream(stream))
     _check("pa_prefill_chunk", st)
 
 
 def pa_prefill_chunk_fp8(out, q, kv_pool, block_tables, query_start_loc, seq_lens, max_q_len,
-                         max_seq_len, scale=None, k_scale=1.0, v_scale=1.0, stream=None):
+                         max_seq_len, scale=None, k_scale=1.0, v_scale=1.0, workspace=None,
+                         split=True, stream=None):
     """pa_prefill_chunk over an FP8 (E4M3) pool held as a uint8 tensor, with its scales."""
-    st = load().pa_prefill_chunk_fp8(*_prefill_args(out, q, kv_pool, block_tables, query_start_loc,
-                                                    seq_lens, max_q_len, max_seq_len, scale,
-                                                    torch.uint8), float(k_scale), float(v_scale),
-                                     _stream(stream))
+    args = _prefill_args(out, q, kv_pool, block_tables, query_start_loc, seq_lens, max_q_len,
+                         max_seq_len, scale, torch.uint8)
+    ws = _prefill_workspace(args, workspace, split, q.device)
+    st = load().pa_prefill_chunk_fp8(*args, float(k_scale), float(v_scale), *ws, _stream(stream))
     _check("pa_prefill_chunk_fp8", st)
 
 

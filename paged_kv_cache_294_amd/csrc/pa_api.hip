@@ -160,6 +160,16 @@ PA_EXPORT int64_t pa_decode_shared_prefix_workspace_bytes(int32_t num_seqs, int3
   return (o_bytes + rows * 8 + 255) / 256 * 256;
 }
 
+PA_EXPORT int64_t pa_prefill_workspace_bytes(int32_t num_reqs, int32_t num_q_heads,
+                                             int32_t max_q_len, int32_t max_seq_len,
+                                             int32_t head_size) {
+  if (num_reqs < 0 || num_q_heads <= 0 || max_q_len < 0 || max_seq_len < max_q_len ||
+      (head_size != 64 && head_size != 128))
+    return -1;
+  const int pieces = pkv::prefill_max_pieces(num_reqs, num_q_heads, max_q_len, max_seq_len, head_size);
+  return pkv::prefill_workspace_bytes(num_reqs, num_q_heads, max_q_len, head_size, pieces);
+}
+
 // ---------------------------------------------------------------------------------------
 // device operations
 // ---------------------------------------------------------------------------------------
@@ -372,7 +382,8 @@ pa_status prefill_impl(void* out, const void* q, const void* kv_pool, const int3
                        int32_t total_q, int32_t max_q_len, int32_t max_seq_len,
                        int32_t num_q_heads, int32_t num_kv_heads, int32_t head_size,
                        int32_t block_size, int32_t max_blocks_per_seq, int64_t num_blocks,
-                       float scale, bool fp8, float k_scale, float v_scale, void* stream) {
+                       float scale, bool fp8, float k_scale, float v_scale, void* workspace,
+                       int64_t workspace_bytes, void* stream) {
   if (fp8 && !(std::isfinite(k_scale) && k_scale > 0.0f && std::isfinite(v_scale) && v_scale > 0.0f))
     return PA_ERR_INVALID;
   if (num_reqs < 0 || total_q < 0 || max_q_len < 0 || max_seq_len < 0 ||
@@ -388,7 +399,19 @@ pa_status prefill_impl(void* out, const void* q, const void* kv_pool, const int3
   if (!out || !q || !kv_pool || !block_tables || !query_start_loc || !seq_lens)
     return PA_ERR_INVALID;
   if (!aligned16(out) || !aligned16(q) || !aligned16(kv_pool)) return PA_ERR_INVALID;
+  if (workspace_bytes < 0 || (workspace && !aligned16(workspace))) return PA_ERR_INVALID;
   pkv::PrefillArgs a{};
+  a.max_pieces = 1;
+  if (workspace) {
+    const int pieces = pkv::prefill_max_pieces(num_reqs, num_q_heads, max_q_len, max_seq_len, head_size);
+    const int64_t need = pkv::prefill_workspace_bytes(num_reqs, num_q_heads, max_q_len, head_size, pieces);
+    if (workspace_bytes < need) return PA_ERR_WORKSPACE;
+    if (pieces > 1) {
+      a.max_pieces = pieces;
+      a.slots = pkv::prefill_slots(head_size);
+      a.ws_o = static_cast<float*>(workspace);  // (m, l) after o: placed by the launcher
+    }
+  }
   a.out = out;
   a.q = q;
   a.pool = kv_pool;
@@ -420,10 +443,11 @@ PA_EXPORT pa_status pa_prefill_chunk(void* out, const void* q, const void* kv_po
                                      int32_t max_q_len, int32_t max_seq_len, int32_t num_q_heads,
                                      int32_t num_kv_heads, int32_t head_size, int32_t block_size,
                                      int32_t max_blocks_per_seq, int64_t num_blocks, float scale,
-                                     void* stream) {
+                                     void* workspace, int64_t workspace_bytes, void* stream) {
   return prefill_impl(out, q, kv_pool, block_tables, query_start_loc, seq_lens, num_reqs, total_q,
                       max_q_len, max_seq_len, num_q_heads, num_kv_heads, head_size, block_size,
-                      max_blocks_per_seq, num_blocks, scale, false, 1.0f, 1.0f, stream);
+                      max_blocks_per_seq, num_blocks, scale, false, 1.0f, 1.0f, workspace,
+                      workspace_bytes, stream);
 }
 
 PA_EXPORT pa_status pa_prefill_chunk_fp8(void* out, const void* q, const void* kv_pool,
@@ -434,10 +458,12 @@ PA_EXPORT pa_status pa_prefill_chunk_fp8(void* out, const void* q, const void* k
                                          int32_t num_kv_heads, int32_t head_size,
                                          int32_t block_size, int32_t max_blocks_per_seq,
                                          int64_t num_blocks, float scale, float k_scale,
-                                         float v_scale, void* stream) {
+                                         float v_scale, void* workspace, int64_t workspace_bytes,
+                                         void* stream) {
   return prefill_impl(out, q, kv_pool, block_tables, query_start_loc, seq_lens, num_reqs, total_q,
                       max_q_len, max_seq_len, num_q_heads, num_kv_heads, head_size, block_size,
-                      max_blocks_per_seq, num_blocks, scale, true, k_scale, v_scale, stream);
+                      max_blocks_per_seq, num_blocks, scale, true, k_scale, v_scale, workspace,
+                      workspace_bytes, stream);
 }
 
 PA_EXPORT pa_status pa_gather_kv(void* k_out, void* v_out, const void* kv_pool,

@@ -62,8 +62,24 @@ struct PrefillArgs {
   float scale_log2;  // softmax scale * log2(e), times the key scale of an FP8 cache
   float v_scale;     // value scale of an FP8 cache (1 for fp16)
   bool kv_fp8;       // the pool holds E4M3 codes (1 byte per element)
+  // Context split: a request's context may be cut into up to max_pieces pieces of whole
+  // stages, each piece of a row tile run by its own workgroup; split tiles leave fp32
+  // partials (o, then (m, l)) in the workspace for the merge kernel. max_pieces == 1: no
+  // split, no workspace.
+  int max_pieces;
+  int slots;         // prefill workgroups the device holds at once
+  float* ws_o;       // [num_reqs][Hq][tiles][max_pieces][128 * D]
+  float* ws_ml;      // [num_reqs][Hq][tiles][max_pieces][256][2]
 };
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream);
+// Pieces per request a launch may use (1: no split), the workspace it then needs, and the
+// prefill workgroups the current device holds at once (fp16 and FP8 caches alike use the
+// fp16 kernel's occupancy, so both take the same workspace).
+int prefill_max_pieces(int num_reqs, int num_q_heads, int max_q_len, int max_seq_len,
+                       int head_size);
+int64_t prefill_workspace_bytes(int num_reqs, int num_q_heads, int max_q_len, int head_size,
+                                int max_pieces);
+int prefill_slots(int head_size);
 
 hipError_t launch_gather_kv(void* k_out, void* v_out, const void* pool, const int32_t* table_row,
                             int len, int kv_row_elems, int64_t num_blocks, hipStream_t stream);

@@ -32,6 +32,8 @@
 // the accumulator rescale is rare and fp16 P stays <= 256. Causal mask: chunk row i
 // (position P + i) sees tokens 0 .. P + i; only stages crossing that diagonal or the end
 // of the context are masked, and stages past every row of a wave are skipped by it.
+#include <algorithm>
+#include <atomic>
 #include <type_traits>
 
 #include "pa_device.h"
@@ -39,6 +41,8 @@
 
 namespace pkv {
 namespace {
+
+typedef float float2_t __attribute__((ext_vector_type(2)));
 
 constexpr int kBM = 128;     // query rows per workgroup
 constexpr int kWRows = 32;   // query rows per wave
@@ -119,23 +123,120 @@ __device__ __forceinline__ void write_rows(const PrefillArgs& a, int q0, int row
   for (int d = 0; d < D; ++d) out[d] = (half_t)value;
 }
 
-// The request with rank `rank` in decreasing seq_len order (ties by index). Every thread
-// returns the same value.
-__device__ int request_of_rank(const PrefillArgs& a, int rank, int* slot) {
-  if (a.num_reqs > kMaxRanked) return rank;
-  if (threadIdx.x == 0) *slot = rank;
+// Lengths of request r and whether they are within the call's bounds.
+struct Request {
+  int q0, C, S, P;
+  bool rows_ok;  // its query rows lie inside [0, total_q)
+  bool bad;      // rows or lengths break the bounds: its rows become NaN
+};
+
+__device__ __forceinline__ Request load_request(const PrefillArgs& a, int r) {
+  Request q;
+  q.q0 = a.query_start_loc[r];
+  const int q1 = a.query_start_loc[r + 1];
+  q.C = q1 - q.q0;
+  q.S = a.seq_lens[r];
+  q.P = q.S - q.C;
+  q.rows_ok = q.q0 >= 0 && q1 >= q.q0 && q1 <= a.total_q;
+  q.bad = !q.rows_ok || q.C > a.max_q_len || q.S < q.C || q.S > a.max_seq_len ||
+          q.S > a.max_blocks_per_seq * kBlockSize;
+  return q;
+}
+
+// Stages of the context that the row tile starting at chunk row i0 sees: every token up
+// to the tile's last row.
+__device__ __forceinline__ int tile_stages(const Request& q, int i0) {
+  return (min(q.S, q.P + min(i0 + kBM, q.C)) + kBN - 1) / kBN;
+}
+
+// Context split. A request whose context is long next to the launch's average load per
+// resident workgroup has it cut into n equal pieces of L whole stages (the last piece
+// shorter), the same cut for all its row tiles and heads; a tile that sees more than L
+// stages is run piece by piece by separate workgroups and merged afterwards by
+// log-sum-exp. Work is then issued by piece weight (the stages its heaviest tile runs),
+// heaviest first, so that the last workgroups to start are light ones.
+constexpr int kMaxPieces = 16;       // pieces per request at most
+constexpr int kMinPieceStages = 16;  // a piece covers at least 512 tokens
+constexpr int kCapNum = 4, kCapDen = 5;  // piece cap: 4/5 of the load per resident workgroup
+
+struct PlanSmem {
+  int nst[kMaxRanked];  // stages of the request's context (0 when it breaks the bounds)
+  int n[kMaxRanked];    // pieces
+  int L[kMaxRanked];    // stages per piece
+  unsigned long long total;  // stages over all requests and row tiles (one head)
+  int sel;              // picked (request, piece) as request * kMaxPieces + piece, or -1
+};
+
+// Fills the plan of every request (num_reqs <= kMaxRanked). Every thread of the workgroup
+// takes part; the same plan comes out in every workgroup of a launch.
+__device__ void make_plan(const PrefillArgs& a, PlanSmem& sp) {
+  const int tid = threadIdx.x;
+  if (tid == 0) sp.total = 0;
   __syncthreads();
-  for (int r = threadIdx.x; r < a.num_reqs; r += kThreads) {
-    const int sr = a.seq_lens[r];
-    int k = 0;
-    for (int u = 0; u < a.num_reqs; ++u) {
-      const int su = a.seq_lens[u];
-      k += (su > sr) || (su == sr && u < r);
+  unsigned long long work = 0;
+  for (int r = tid; r < a.num_reqs; r += kThreads) {
+    const Request q = load_request(a, r);
+    int nst = 0;
+    if (!q.bad) {
+      nst = (q.S + kBN - 1) / kBN;
+      if (a.max_pieces > 1)
+        for (int i0 = 0; i0 < q.C; i0 += kBM) work += (unsigned long long)tile_stages(q, i0);
     }
-    if (k == rank) *slot = r;
+    sp.nst[r] = nst;
+  }
+  if (a.max_pieces > 1 && work) atomicAdd(&sp.total, work);
+  __syncthreads();
+  int cap = INT32_MAX;  // no split with one piece per request
+  if (a.max_pieces > 1) {  // then slots >= 1
+    const unsigned long long den = (unsigned long long)max(a.slots, 1) * kCapDen;
+    const unsigned long long c = (sp.total * (unsigned long long)a.num_q_heads * kCapNum + den - 1) / den;
+    cap = (int)max((unsigned long long)kMinPieceStages, min(c, (unsigned long long)INT32_MAX));
+  }
+  for (int r = tid; r < a.num_reqs; r += kThreads) {
+    const int nst = sp.nst[r];
+    const int n = nst == 0 ? 1 : min(a.max_pieces, (nst - 1) / cap + 1);
+    sp.n[r] = n;
+    sp.L[r] = (nst + n - 1) / n;
   }
   __syncthreads();
-  return *slot;
+}
+
+// Weight of piece p of a request cut into n pieces of L stages out of nst
+__device__ __forceinline__ int piece_weight(int nst, int n, int L, int p) {
+  return p < n - 1 ? L : nst - (n - 1) * L;
+}
+
+// The (request, piece) of rank k in decreasing piece weight (ties by request, then piece),
+// as request * kMaxPieces + piece, or -1 past the last piece. Every thread returns it.
+__device__ int piece_of_rank(const PrefillArgs& a, PlanSmem& sp, int k) {
+  const int tid = threadIdx.x;
+  if (tid == 0) sp.sel = -1;
+  __syncthreads();
+  const int R = a.num_reqs;
+  for (int r = tid; r < R; r += kThreads) {
+    const int n = sp.n[r], L = sp.L[r], nst = sp.nst[r];
+    for (int p = 0; p < n; ++p) {
+      const int wt = piece_weight(nst, n, L, p);
+      int rank = 0;
+      for (int u = 0; u < R; ++u) {
+        const int nu = sp.n[u], Lu = sp.L[u];
+        const int wl = piece_weight(sp.nst[u], nu, Lu, nu - 1);
+        if (u < r) {
+          rank += (Lu >= wt) * (nu - 1) + (wl >= wt);
+        } else if (u > r) {
+          rank += (Lu > wt) * (nu - 1) + (wl > wt);
+        } else {
+          for (int q = 0; q < nu; ++q) {
+            const int wq = piece_weight(nst, nu, Lu, q);
+            rank += q < p ? (wq >= wt) : q > p ? (wq > wt) : 0;
+          }
+        }
+      }
+      if (rank == k) sp.sel = r * kMaxPieces + p;
+    }
+  }
+  __syncthreads();
+  return sp.sel;
 }
 
 template <int D, typename KV>
@@ -152,35 +253,41 @@ __global__ __launch_bounds__(kThreads, 3) void prefill_kernel(const PrefillArgs 
   constexpr int ROW = Smem::ROW;
   extern __shared__ __align__(16) unsigned char smem_raw[];
   Smem& sm = *reinterpret_cast<Smem*>(smem_raw);
-  __shared__ int s_req;
+  __shared__ PlanSmem sp;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, uniform per wave
   const int g = lane >> 5;
 
-  // Work item of this workgroup (see the header comment on XCDs and order)
+  // Work item of this workgroup (see the header comment on XCDs and order): group k * Hq +
+  // h is piece rank k of query head h
   const int tiles = (a.max_q_len + kBM - 1) / kBM;
   const int xcd = blockIdx.x % kXcds, slot = blockIdx.x / kXcds;
   const int group = (slot / tiles) * kXcds + xcd;
-  if (group >= a.num_reqs * a.num_q_heads) return;  // padding of the grid (uniform per WG)
+  if (group >= a.num_reqs * a.max_pieces * a.num_q_heads) return;  // grid padding (uniform)
   const int h = group % a.num_q_heads;
+  const int k = group / a.num_q_heads;
   // uniform, so the request's lengths and table entries are read with scalar loads (a vector
   // load there would have to wait for every staging load in flight)
-  const int r = __builtin_amdgcn_readfirstlane(request_of_rank(a, group / a.num_q_heads, &s_req));
+  int r, p = 0, L = INT32_MAX;
+  if (a.num_reqs <= kMaxRanked) {
+    make_plan(a, sp);
+    const int sel = __builtin_amdgcn_readfirstlane(piece_of_rank(a, sp, k));
+    if (sel < 0) return;  // past the last piece
+    r = sel / kMaxPieces;
+    p = sel % kMaxPieces;
+    L = __builtin_amdgcn_readfirstlane(sp.L[r]);
+  } else {  // launch order (one piece per request: the host splits only ranked batches)
+    r = k;
+  }
   const int i0 = (tiles - 1 - slot % tiles) * kBM;
   const int kvh = h / (a.num_q_heads / a.num_kv_heads);
 
-  const int q0 = a.query_start_loc[r];
-  const int q1 = a.query_start_loc[r + 1];
-  const int C = q1 - q0;
-  const int S = a.seq_lens[r];
-  const int P = S - C;
-  const bool rows_ok = q0 >= 0 && q1 >= q0 && q1 <= a.total_q;
-  const bool bad = !rows_ok || C > a.max_q_len || S < C || S > a.max_seq_len ||
-                   S > a.max_blocks_per_seq * kBlockSize;
-  if (bad) {
-    if (rows_ok)
+  const Request rq = load_request(a, r);
+  const int q0 = rq.q0, C = rq.C, S = rq.S, P = rq.P;
+  if (rq.bad) {
+    if (rq.rows_ok && p == 0)
       for (int i = i0 + tid; i < min(i0 + kBM, C); i += kThreads) write_rows<D>(a, q0, i, h, qnan());
     return;
   }
@@ -192,9 +299,21 @@ __global__ __launch_bounds__(kThreads, 3) void prefill_kernel(const PrefillArgs 
   const half_t* qp = static_cast<const half_t*>(a.q);
   half8_t qb[KS];
 
-  const int kv_end = min(S, P + min(i0 + kBM, C));               // tokens the workgroup sees
   const int wave_end = row_w < C ? P + min(row_w + kWRows, C) : 0;  // tokens this wave sees
-  const int nst = (kv_end + kBN - 1) / kBN;                       // stages
+  const int nst = tile_stages(rq, i0);                            // stages the tile sees
+  // this workgroup's piece: stages s0 .. s1 - 1; a tile seeing more than L stages is split
+  const int s0 = p * L;
+  if (s0 >= nst) return;  // the tile ends before this piece
+  const int s1 = min(nst, s0 + L);
+  const bool split = nst > L;
+  // Where this wave's results go, fixed before the stage loop so that one pointer stays live
+  // across it: the fp16 output rows of the wave, or (split tile) the wave's part of the
+  // piece's partial slot, (m, l) at the same slot index of the second region.
+  const int64_t pslot = (((int64_t)r * a.num_q_heads + h) * tiles + i0 / kBM) * a.max_pieces + p;
+  char* const dst = split ? reinterpret_cast<char*>(a.ws_o + pslot * (kBM * D) + w * (kWRows * D))
+                          : reinterpret_cast<char*>(static_cast<half_t*>(a.out) +
+                                                    ((int64_t)(q0 + row_w) * a.num_q_heads + h) * D);
+  const int rows_left = C - row_w;  // rows of the wave inside the chunk (may be <= 0)
 
   const int kv_row = a.num_kv_heads * D;
   const int tok_stride = 2 * kv_row;
@@ -245,7 +364,7 @@ __global__ __launch_bounds__(kThreads, 3) void prefill_kernel(const PrefillArgs 
     }
   };
   auto issue_stage = [&](int st, int ring) {
-    if (st > 0 && st % (64 * kTabRegs) == 0) load_table(st / (64 * kTabRegs));  // uniform
+    if (st > s0 && st % (64 * kTabRegs) == 0) load_table(st / (64 * kTabRegs));  // uniform
     const int v = (st >> 6) % kTabRegs;
     int cand = tab[0];
 #pragma unroll
@@ -272,8 +391,8 @@ __global__ __launch_bounds__(kThreads, 3) void prefill_kernel(const PrefillArgs 
   const int dh = (lane >> 4) & 1;   // which 16 dims of the 32-dim tile
   const int vtok = 4 * g + li / 4;  // token (within a 16-token k-step half) of this source lane
 
-  load_table(0);
-  for (int st = 0; st < kStages - 1 && st < nst; ++st) issue_stage(st, st);
+  load_table(s0 / (64 * kTabRegs));
+  for (int st = s0; st < s0 + kStages - 1 && st < s1; ++st) issue_stage(st, st - s0);
   // the query rows come in behind the first stages, and one wait covers both: the compiler
   // then knows of no load in flight inside the loop and leaves the waiting to the loop's
   // own counted waits
@@ -296,7 +415,7 @@ __global__ __launch_bounds__(kThreads, 3) void prefill_kernel(const PrefillArgs 
     // this wave's loads of stage `it` have landed once at most the loads of the stages
     // issued after it are outstanding; the barrier makes every wave's loads visible and
     // frees ring slot (it - 1) % kStages for stage it + kStages - 1
-    if (it + 1 < nst) wait_vm<2 * INST>();
+    if (it + 1 < s1) wait_vm<2 * INST>();
     else wait_vm<0>();
     lds_barrier();
     const int t0 = it * kBN;
@@ -326,7 +445,7 @@ __global__ __launch_bounds__(kThreads, 3) void prefill_kernel(const PrefillArgs 
       }
       lds_barrier();
     }
-    if (it + kStages - 1 < nst) issue_stage(it + kStages - 1, (kRing + kStages - 1) % kStages);
+    if (it + kStages - 1 < s1) issue_stage(it + kStages - 1, (kRing + kStages - 1) % kStages);
 
     if (t0 < wave_end) {
       // S^T for the stage's 32 tokens
@@ -417,19 +536,34 @@ __global__ __launch_bounds__(kThreads, 3) void prefill_kernel(const PrefillArgs 
   using R1 = std::integral_constant<int, 1>;
   using R2 = std::integral_constant<int, 2>;
   static_assert(kStages == 3, "the stage loop is unrolled by a ring of three");
-  int it = 0;
-  for (; it + 3 <= nst; it += 3) {
+  int it = s0;  // ring slot (it - s0) % kStages
+  for (; it + 3 <= s1; it += 3) {
     stage(R0{}, it);
     stage(R1{}, it + 1);
     stage(R2{}, it + 2);
   }
-  if (it < nst) stage(R0{}, it++);
-  if (it < nst) stage(R1{}, it++);
+  if (it < s1) stage(R0{}, it++);
+  if (it < s1) stage(R1{}, it++);
 
   l += __shfl_xor(l, 32, kWave);
   const bool bad_table = __builtin_amdgcn_ballot_w64(bad_lanes) != 0;
-  if (qrow >= C) return;
-  half_t* out = static_cast<half_t*>(a.out) + ((int64_t)(q0 + qrow) * a.num_q_heads + h) * D;
+  if (split) {
+    // fp32 partials of this piece for the merge kernel, in lane order: o (not normalised),
+    // then (m, l) per lane; a bad table entry makes l NaN, which the merge carries on
+    float4_t* po = reinterpret_cast<float4_t*>(dst) + lane;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+      for (int v4 = 0; v4 < 4; ++v4)
+        po[(dt * 4 + v4) * kWave] =
+            float4_t{o[dt][4 * v4], o[dt][4 * v4 + 1], o[dt][4 * v4 + 2], o[dt][4 * v4 + 3]};
+    const int64_t ps = (reinterpret_cast<float*>(dst) - a.ws_o) / (kBM * D);
+    float2_t* pml = reinterpret_cast<float2_t*>(a.ws_ml + ps * (kThreads * 2));
+    pml[tid] = float2_t{m, bad_table ? qnan() : l};
+    return;
+  }
+  if ((lane & 31) >= rows_left) return;
+  half_t* out = reinterpret_cast<half_t*>(dst) + (int64_t)(lane & 31) * a.num_q_heads * D;
   const float inv = bad_table ? qnan() : a.v_scale / l;
 #pragma unroll
   for (int dt = 0; dt < DT; ++dt)
@@ -442,8 +576,64 @@ __global__ __launch_bounds__(kThreads, 3) void prefill_kernel(const PrefillArgs 
     }
 }
 
+// Merge of a split row tile: one workgroup per (request, query head, row tile), lanes laid
+// out as in the prefill kernel's epilogue. With M the largest of the pieces' reference maxima
+// (log2 units), out = sum_p 2^(m_p - M) o_p / sum_p 2^(m_p - M) l_p, times the value scale of
+// an FP8 cache. Tiles that were not split are left alone.
+template <int D>
+__global__ __launch_bounds__(kThreads) void prefill_merge_kernel(const PrefillArgs a) {
+  constexpr int DT = D / 32;
+  __shared__ PlanSmem sp;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int w = tid >> 6;
+  const int g = lane >> 5;
+  const int tiles = (a.max_q_len + kBM - 1) / kBM;
+  const int ti = blockIdx.x % tiles;
+  const int h = (blockIdx.x / tiles) % a.num_q_heads;
+  const int r = blockIdx.x / tiles / a.num_q_heads;
+  make_plan(a, sp);
+  const Request rq = load_request(a, r);
+  const int i0 = ti * kBM;
+  if (rq.bad || i0 >= rq.C) return;
+  const int L = sp.L[r];
+  const int nst = tile_stages(rq, i0);
+  if (nst <= L) return;  // one piece: written by the prefill kernel itself
+  const int np = (nst + L - 1) / L;
+  const int64_t ps0 = (((int64_t)r * a.num_q_heads + h) * tiles + ti) * a.max_pieces;
+  const float2_t* pml = reinterpret_cast<const float2_t*>(a.ws_ml + ps0 * (kThreads * 2)) + tid;
+  float mmax = neg_inf();
+  for (int p = 0; p < np; ++p) mmax = fmaxf(mmax, pml[p * kThreads][0]);
+  float lsum = 0.0f;
+  float4_t acc[DT * 4];
+#pragma unroll
+  for (int j = 0; j < DT * 4; ++j) acc[j] = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
+  for (int p = 0; p < np; ++p) {
+    const float2_t ml = pml[p * kThreads];
+    const float wgt = fast_exp2(ml[0] - mmax);  // 0 for a piece the row saw nothing of
+    lsum = fmaf(wgt, ml[1], lsum);
+    const float4_t* po =
+        reinterpret_cast<const float4_t*>(a.ws_o + (ps0 + p) * (kBM * D)) + w * (DT * 4 * kWave) + lane;
+#pragma unroll
+    for (int j = 0; j < DT * 4; ++j) acc[j] += wgt * po[j * kWave];
+  }
+  const int row = i0 + kWRows * w + (lane & 31);
+  if (row >= rq.C) return;
+  half_t* out = static_cast<half_t*>(a.out) + ((int64_t)(rq.q0 + row) * a.num_q_heads + h) * D;
+  const float inv = a.v_scale / lsum;
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+    for (int v4 = 0; v4 < 4; ++v4) {
+      half4_t x;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) x[e] = (half_t)(acc[dt * 4 + v4][e] * inv);
+      *reinterpret_cast<half4_t*>(out + 32 * dt + 8 * v4 + 4 * g) = x;
+    }
+}
+
 template <int D, typename KV>
-hipError_t launch_prefill_d(const PrefillArgs& a, hipStream_t stream) {
+hipError_t launch_prefill_d(PrefillArgs a, hipStream_t stream) {
   const size_t smem = sizeof(PrefillSmem<D, KV>);
   static bool attr_set = false;  // the attribute is per function, set once per process
   if (!attr_set) {
@@ -452,15 +642,79 @@ hipError_t launch_prefill_d(const PrefillArgs& a, hipStream_t stream) {
     if (e != hipSuccess) return e;
     attr_set = true;
   }
-  const int64_t groups = (int64_t)a.num_reqs * a.num_q_heads;
+  const int64_t groups = (int64_t)a.num_reqs * a.max_pieces * a.num_q_heads;
   const int64_t tiles = (a.max_q_len + kBM - 1) / kBM;
+  if (a.max_pieces > 1)  // the workspace: o of every piece slot, then their (m, l)
+    a.ws_ml = a.ws_o + (int64_t)a.num_reqs * a.num_q_heads * tiles * a.max_pieces * kBM * D;
   const int64_t wgs = (groups + kXcds - 1) / kXcds * kXcds * tiles;
   if (wgs > INT32_MAX) return hipErrorInvalidValue;
   hipLaunchKernelGGL((prefill_kernel<D, KV>), dim3((unsigned)wgs), dim3(kThreads), smem, stream, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || a.max_pieces == 1) return e;
+  const int64_t mwgs = (int64_t)a.num_reqs * a.num_q_heads * tiles;
+  if (mwgs > INT32_MAX) return hipErrorInvalidValue;
+  hipLaunchKernelGGL((prefill_merge_kernel<D>), dim3((unsigned)mwgs), dim3(kThreads), 0, stream, a);
   return hipGetLastError();
 }
 
+// Prefill workgroups the current device holds at once (0 when the runtime cannot say);
+// queried once per device.
+template <int D, typename KV>
+int64_t resident_prefill_groups() {
+  static std::atomic<int64_t> cache[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+  int64_t v = cache[dev].load(std::memory_order_relaxed);
+  if (v > 0) return v;
+  int per_cu = 0, cus = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, prefill_kernel<D, KV>, kThreads,
+                                                   sizeof(PrefillSmem<D, KV>)) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+    return 0;
+  v = (int64_t)per_cu * cus;
+  cache[dev].store(v, std::memory_order_relaxed);
+  return v;
+}
+
+int64_t resident_prefill(int head_size) {
+  return head_size == 128 ? resident_prefill_groups<128, half_t>() : resident_prefill_groups<64, half_t>();
+}
+
 }  // namespace
+
+// Pieces per request: only a launch whose row tiles fill at most half of the device's
+// workgroup slots is split, into as many pieces as those slots take (row tiles x heads x
+// pieces <= resident workgroups), each piece at least kMinPieceStages stages; no split for
+// batches above kMaxRanked requests. (With more tiles than that the split measured no
+// faster: at the mixed step's 1024 tiles for 768 slots it took 198 + 22 us for the merge
+// against 189 us unsplit.)
+int prefill_max_pieces(int num_reqs, int num_q_heads, int max_q_len, int max_seq_len,
+                       int head_size) {
+  if (num_reqs <= 0 || num_reqs > kMaxRanked || num_q_heads <= 0 || max_q_len <= 0) return 1;
+  if (head_size != 64 && head_size != 128) return 1;
+  const int64_t slots = resident_prefill(head_size);
+  if (slots <= 0) return 1;
+  const int64_t tiles = (int64_t)num_reqs * num_q_heads * ((max_q_len + kBM - 1) / kBM);
+  int64_t n = slots / tiles;
+  const int64_t max_stages = ((int64_t)max_seq_len + kBN - 1) / kBN;
+  n = std::min<int64_t>(n, max_stages / kMinPieceStages);
+  n = std::min<int64_t>(n, kMaxPieces);
+  return n < 2 ? 1 : (int)n;
+}
+
+int64_t prefill_workspace_bytes(int num_reqs, int num_q_heads, int max_q_len, int head_size,
+                                int max_pieces) {
+  if (max_pieces <= 1) return 0;
+  const int64_t slots_total = (int64_t)num_reqs * num_q_heads * ((max_q_len + kBM - 1) / kBM) * max_pieces;
+  const int64_t o_bytes = slots_total * kBM * head_size * 4;
+  const int64_t ml_bytes = slots_total * kThreads * 2 * 4;
+  return o_bytes + ml_bytes;
+}
+
+int prefill_slots(int head_size) {
+  const int64_t v = resident_prefill(head_size);
+  return v > INT32_MAX ? INT32_MAX : (int)v;
+}
 
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream) {
   if (a.kv_fp8) {

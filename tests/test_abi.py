@@ -158,7 +158,7 @@ def test_append_rejects(lib):
 
 def test_prefill_rejects(lib):
     f = lib.pa_prefill_chunk
-    base = [FAKE] * 6 + [2, 64, 32, 64, 4, 4, 64, 16, 8, 16, 0.125, None]
+    base = [FAKE] * 6 + [2, 64, 32, 64, 4, 4, 64, 16, 8, 16, 0.125, None, 0, None]
     def call(**idx):
         a = list(base)
         for i, v in idx.items():
@@ -169,6 +169,18 @@ def test_prefill_rejects(lib):
     assert call(a0=0) == pkv.PA_ERR_INVALID              # null out
     assert call(a8=65) == pkv.PA_ERR_INVALID             # max_q_len > max_seq_len
     assert call(a6=0) == pkv.PA_OK                       # no requests
+    assert call(a17=FAKE, a18=-1) == pkv.PA_ERR_INVALID  # negative workspace size
+    assert call(a17=FAKE + 8, a18=1 << 20) == pkv.PA_ERR_INVALID  # workspace not 16-byte aligned
+
+
+def test_prefill_workspace_bytes(lib):
+    f = lib.pa_prefill_workspace_bytes
+    assert f(-1, 32, 512, 4096, 128) == -1
+    assert f(8, 0, 512, 4096, 128) == -1
+    assert f(8, 32, 512, 256, 128) == -1     # max_seq_len < max_q_len
+    assert f(8, 32, 512, 4096, 80) == -1     # head size
+    assert f(0, 32, 0, 0, 128) == 0          # nothing to split
+    assert f(300, 32, 512, 4096, 128) == 0   # above 256 requests: no split
 
 
 def test_gather_and_stream_read_reject(lib):

@@ -1,7 +1,8 @@
 """A step captured into a HIP graph (StepGraph) replays to exactly the eager step's bits.
 
-The step is kv_append -> chunked prefill -> decode (grouped-query tile, several
-partitions, so the log-sum-exp reduce runs too). Replays are separated by eager work
+The step is kv_append -> chunked prefill (its context split, so the merge kernel runs
+too) -> decode (grouped-query tile, several partitions, so the log-sum-exp reduce runs
+too). Replays are separated by eager work
 and host synchronisations, and the queries are changed in place between them."""
 
 import numpy as np
@@ -32,19 +33,24 @@ class Batch:
         qp, btp, qsl, lensp = inp.prefill_part()
         self.pq, self.pbt, self.qsl, self.plens = dev(qp), dev(btp), dev(qsl), dev(lensp)
         self.max_q, self.max_s = int(np.diff(qsl).max()), int(lensp.max())
+        pws = pkv.pa_prefill_workspace_bytes(len(lensp), inp.num_q_heads, self.max_q, self.max_s,
+                                             inp.head_size)
+        assert pws > 0  # the prefill's context split and merge kernel are part of the step
+        self.pws = torch.empty(pws, dtype=torch.uint8, device="cuda")
         self.dout = torch.full_like(self.dq, float("nan"))
         self.pout = torch.full_like(self.pq, float("nan"))
 
     def step(self, stream):
         pkv.pa_kv_append(self.pool, self.key, self.value, self.slots, stream=stream)
         pkv.pa_prefill_chunk(self.pout, self.pq, self.pool, self.pbt, self.qsl, self.plens,
-                             self.max_q, self.max_s, self.inp.scale, stream=stream)
+                             self.max_q, self.max_s, self.inp.scale, workspace=self.pws,
+                             stream=stream)
         pkv.pa_decode(self.dout, self.dq, self.pool, self.dbt, self.dlens, self.mcl,
                       self.inp.scale, self.ps, self.ws, stream=stream)
 
 
 def test_captured_step_replays_bit_exact():
-    inp = workloads.mixed_case(71, [0, 300, 40], [64, 100, 33], [1, 50, 700, 2000, 1100], 8, 4, 128)
+    inp = workloads.mixed_case(71, [0, 1500, 40], [64, 100, 33], [1, 50, 700, 2000, 1100], 8, 4, 128)
     side = torch.cuda.Stream()
     b = Batch(inp)
     note("graph: eager reference step")

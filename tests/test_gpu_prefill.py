@@ -125,3 +125,104 @@ def test_prefill_bad_rows_are_nan():
     check_attention(got[:r0], ref[:r0], "good request")
     assert np.all(np.isnan(got[r0:r1].astype(np.float64)))
     assert np.all(np.isnan(got[r1:r2].astype(np.float64)))
+
+
+# ---- split context: long contexts cut into pieces merged by log-sum-exp ----------------
+
+def run_prefill(inp, pool, split, rows_hint=None, workspace=None):
+    q, bt, qsl, lens = inp.prefill_part()
+    qd = dev(q)
+    out = torch.full_like(qd, float("nan"))
+    pkv.pa_prefill_chunk(out, qd, pool, dev(bt), dev(qsl), dev(lens), int(np.diff(qsl).max()),
+                         int(lens.max()), inp.scale, workspace=workspace, split=split)
+    return host(out)
+
+
+def appended_pool(inp):
+    pool = dev(inp.pool)
+    pkv.pa_kv_append(pool, dev(inp.key_new), dev(inp.value_new), dev(inp.slot_mapping))
+    return pool
+
+
+def workspace_bytes(inp):
+    q, bt, qsl, lens = inp.prefill_part()
+    return pkv.pa_prefill_workspace_bytes(len(lens), inp.num_q_heads, int(np.diff(qsl).max()),
+                                          int(lens.max()), inp.head_size)
+
+
+@pytest.mark.parametrize("D", [64, 128])
+def test_prefill_split_matches_unsplit_and_oracle(D):
+    """Requests with long priors next to short ones: the split launch agrees with the
+    oracle and with the unsplit launch (fp32 sums in another order: within 2e-3)."""
+    inp = workloads.mixed_case(56 + D, [6000, 2100, 0, 700], [256, 300, 100, 17], [], 16, 4, D)
+    assert workspace_bytes(inp) > 0  # the split is taken at these sizes
+    pool = appended_pool(inp)
+    note(f"prefill split D={D}")
+    split = run_prefill(inp, pool, True)
+    whole = run_prefill(inp, pool, False)
+    rows = np.arange(0, split.shape[0], 3)
+    check_attention(split[rows], oracle_prefill(inp, rows=set(rows.tolist()))[rows], f"split D{D}")
+    assert np.abs(split.astype(np.float64) - whole.astype(np.float64)).max() <= 2e-3
+
+
+def test_prefill_split_single_long_request():
+    """One 512-row chunk after 15872 cached tokens: 32 row tiles for the whole GPU, so the
+    context is cut into the most pieces; sampled rows against the oracle."""
+    inp = workloads.mixed_case(57, [15872], [512], [], 8, 8, 128)
+    assert workspace_bytes(inp) > 0
+    pool = appended_pool(inp)
+    note("prefill split, one 16k request")
+    got = run_prefill(inp, pool, True)
+    rows = np.concatenate([np.arange(0, 512, 37), [127, 128, 255, 256, 511]])
+    check_attention(got[rows], oracle_prefill(inp, rows=set(rows.tolist()))[rows], "16k request")
+    whole = run_prefill(inp, pool, False)
+    assert np.abs(got.astype(np.float64) - whole.astype(np.float64)).max() <= 2e-3
+
+
+def test_prefill_split_bad_entry_in_late_piece_is_nan():
+    inp = workloads.mixed_case(58, [9000, 3000], [200, 64], [], 8, 8, 128)
+    assert workspace_bytes(inp) > 0
+    pool = appended_pool(inp)
+    q, bt, qsl, lens = inp.prefill_part()
+    bt = bt.copy()
+    bt[0, 500] = inp.num_blocks + 3  # token 8000 of request 0: in its last pieces
+    out = torch.full_like(dev(q), 0.0)
+    pkv.pa_prefill_chunk(out, dev(q), pool, dev(bt), dev(qsl), dev(lens),
+                         int(np.diff(qsl).max()), int(lens.max()), inp.scale)
+    got = host(out).astype(np.float64)
+    r0 = int(qsl[1])
+    assert np.all(np.isnan(got[:r0]))
+    rows = np.arange(r0, got.shape[0], 5)
+    check_attention(got[rows], oracle_prefill(inp, rows=set(rows.tolist()))[rows], "good request")
+
+
+def test_prefill_split_workspace_too_small():
+    inp = workloads.mixed_case(59, [4000], [128], [], 8, 8, 128)
+    need = workspace_bytes(inp)
+    assert need > 0
+    pool = appended_pool(inp)
+    small = torch.empty(need - 16, dtype=torch.uint8, device="cuda")
+    with pytest.raises(pkv.PagedKVError):
+        run_prefill(inp, pool, True, workspace=small)
+    ok = torch.empty(need, dtype=torch.uint8, device="cuda")
+    got = run_prefill(inp, pool, True, workspace=ok)
+    # a second call into the same workspace with a shorter chunk
+    inp2 = workloads.mixed_case(60, [2500], [40], [], 8, 8, 128)
+    assert workspace_bytes(inp2) <= need
+    got2 = run_prefill(inp2, appended_pool(inp2), True, workspace=ok)
+    rows = np.arange(0, 128, 9)
+    check_attention(got[rows], oracle_prefill(inp, rows=set(rows.tolist()))[rows], "first call")
+    check_attention(got2, oracle_prefill(inp2), "second call")
+
+
+def test_prefill_long_prompt_workload_sampled():
+    """The long-prompt workload at full size, in the bench's configuration (the step's
+    append, then the split prefill): sampled rows of every row tile against the oracle."""
+    inp = workloads.long_prompt_prefill()
+    assert workspace_bytes(inp) > 0
+    note("long-prompt workload: append + split prefill")
+    got, pool = gpu_prefill(inp)
+    del pool
+    torch.cuda.empty_cache()
+    rows = np.concatenate([np.arange(0, 512, 23), [127, 128, 383, 384, 511]])
+    check_attention(got[rows], oracle_prefill(inp, rows=set(rows.tolist()))[rows], "long prompt")

@@ -15,6 +15,7 @@ from .synth import (  # noqa: F401
     long_context_32k,
     shared_prompt_groups,
     mixed_prefill_decode,
+    long_prompt_prefill,
     decode_case,
     mixed_case,
     prefix_shared_case,

@@ -438,8 +438,18 @@ def mixed_prefill_decode(keep_logical=False) -> PagedInputs:
                  keep_logical=keep_logical, name="mixed-8x512prefill+248decode-32x128")
 
 
+def long_prompt_prefill(keep_logical=False) -> PagedInputs:
+    """The last 512-row chunk of a 32768-token prompt (32256 tokens cached before it) in a
+    step with 8 decodes U{256..4096}: few row tiles next to a long context."""
+    rng = np.random.default_rng(6)
+    dl = rng.integers(256, 4096, size=8, endpoint=True)
+    return mixed_case(6, [32256], [512], dl.tolist(), 32, 32, 128, keep_logical=keep_logical,
+                      name="long-prompt-chunk-512of32768+8decode-32x128")
+
+
 WORKLOADS = {"tiny": tiny_decode, "decode256": decode_256seq, "long32k": long_context_32k,
-             "prefix-groups": shared_prompt_groups, "mixed": mixed_prefill_decode}
+             "prefix-groups": shared_prompt_groups, "mixed": mixed_prefill_decode,
+             "long-prefill": long_prompt_prefill}
 
 
 # ---------------------------------------------------------------------------------------
