@@ -159,6 +159,24 @@ constexpr int kMaxPieces = 16;       // pieces per request at most
 constexpr int kMinPieceStages = 16;  // a piece covers at least 512 tokens
 constexpr int kCapNum = 4, kCapDen = 5;  // piece cap: 4/5 of the load per resident workgroup
 
+// The request with rank `rank` in decreasing seq_len order (ties by index), for launches
+// without a split. Every thread returns the same value.
+__device__ int request_of_rank(const PrefillArgs& a, int rank, int* slot) {
+  if (threadIdx.x == 0) *slot = rank;
+  __syncthreads();
+  for (int r = threadIdx.x; r < a.num_reqs; r += kThreads) {
+    const int sr = a.seq_lens[r];
+    int k = 0;
+    for (int u = 0; u < a.num_reqs; ++u) {
+      const int su = a.seq_lens[u];
+      k += (su > sr) || (su == sr && u < r);
+    }
+    if (k == rank) *slot = r;
+  }
+  __syncthreads();
+  return *slot;
+}
+
 struct PlanSmem {
   int nst[kMaxRanked];  // stages of the request's context (0 when it breaks the bounds)
   int n[kMaxRanked];    // pieces
@@ -271,15 +289,15 @@ __global__ __launch_bounds__(kThreads, 3) void prefill_kernel(const PrefillArgs 
   // uniform, so the request's lengths and table entries are read with scalar loads (a vector
   // load there would have to wait for every staging load in flight)
   int r, p = 0, L = INT32_MAX;
-  if (a.num_reqs <= kMaxRanked) {
+  if (a.max_pieces == 1) {  // no split: requests by length (launch order above kMaxRanked)
+    r = a.num_reqs <= kMaxRanked ? __builtin_amdgcn_readfirstlane(request_of_rank(a, k, &sp.sel)) : k;
+  } else {  // the host splits only batches of at most kMaxRanked requests
     make_plan(a, sp);
     const int sel = __builtin_amdgcn_readfirstlane(piece_of_rank(a, sp, k));
     if (sel < 0) return;  // past the last piece
     r = sel / kMaxPieces;
     p = sel % kMaxPieces;
     L = __builtin_amdgcn_readfirstlane(sp.L[r]);
-  } else {  // launch order (one piece per request: the host splits only ranked batches)
-    r = k;
   }
   const int i0 = (tiles - 1 - slot % tiles) * kBM;
   const int kvh = h / (a.num_q_heads / a.num_kv_heads);
@@ -576,22 +594,25 @@ __global__ __launch_bounds__(kThreads, 3) void prefill_kernel(const PrefillArgs 
     }
 }
 
-// Merge of a split row tile: one workgroup per (request, query head, row tile), lanes laid
-// out as in the prefill kernel's epilogue. With M the largest of the pieces' reference maxima
-// (log2 units), out = sum_p 2^(m_p - M) o_p / sum_p 2^(m_p - M) l_p, times the value scale of
-// an FP8 cache. Tiles that were not split are left alone.
+// Merge of a split row tile: one workgroup per (request, query head, row tile, wave of
+// the tile), its 256 threads taking a quarter of a wave lane's partial each (lane layout of
+// the prefill kernel's epilogue). With M the largest of the pieces' reference maxima (log2
+// units), out = sum_p 2^(m_p - M) o_p / sum_p 2^(m_p - M) l_p, times the value scale of an
+// FP8 cache. Tiles that were not split are left alone.
 template <int D>
 __global__ __launch_bounds__(kThreads) void prefill_merge_kernel(const PrefillArgs a) {
   constexpr int DT = D / 32;
+  constexpr int J = DT;  // float4 of a lane's partial per thread (a quarter of DT * 4)
   __shared__ PlanSmem sp;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int w = tid >> 6;
+  const int part = tid >> 6;  // which quarter of the lane's DT * 4 float4
   const int g = lane >> 5;
   const int tiles = (a.max_q_len + kBM - 1) / kBM;
-  const int ti = blockIdx.x % tiles;
-  const int h = (blockIdx.x / tiles) % a.num_q_heads;
-  const int r = blockIdx.x / tiles / a.num_q_heads;
+  const int w = blockIdx.x & 3;
+  const int ti = (blockIdx.x >> 2) % tiles;
+  const int h = (blockIdx.x >> 2) / tiles % a.num_q_heads;
+  const int r = (blockIdx.x >> 2) / tiles / a.num_q_heads;
   make_plan(a, sp);
   const Request rq = load_request(a, r);
   const int i0 = ti * kBM;
@@ -601,35 +622,36 @@ __global__ __launch_bounds__(kThreads) void prefill_merge_kernel(const PrefillAr
   if (nst <= L) return;  // one piece: written by the prefill kernel itself
   const int np = (nst + L - 1) / L;
   const int64_t ps0 = (((int64_t)r * a.num_q_heads + h) * tiles + ti) * a.max_pieces;
-  const float2_t* pml = reinterpret_cast<const float2_t*>(a.ws_ml + ps0 * (kThreads * 2)) + tid;
+  const float2_t* pml = reinterpret_cast<const float2_t*>(a.ws_ml + ps0 * (kThreads * 2)) + w * kWave + lane;
   float mmax = neg_inf();
   for (int p = 0; p < np; ++p) mmax = fmaxf(mmax, pml[p * kThreads][0]);
   float lsum = 0.0f;
-  float4_t acc[DT * 4];
+  float4_t acc[J];
 #pragma unroll
-  for (int j = 0; j < DT * 4; ++j) acc[j] = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
+  for (int j = 0; j < J; ++j) acc[j] = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll 4
   for (int p = 0; p < np; ++p) {
     const float2_t ml = pml[p * kThreads];
     const float wgt = fast_exp2(ml[0] - mmax);  // 0 for a piece the row saw nothing of
     lsum = fmaf(wgt, ml[1], lsum);
-    const float4_t* po =
-        reinterpret_cast<const float4_t*>(a.ws_o + (ps0 + p) * (kBM * D)) + w * (DT * 4 * kWave) + lane;
+    const float4_t* po = reinterpret_cast<const float4_t*>(a.ws_o + (ps0 + p) * (kBM * D)) +
+                         w * (DT * 4 * kWave) + part * (J * kWave) + lane;
 #pragma unroll
-    for (int j = 0; j < DT * 4; ++j) acc[j] += wgt * po[j * kWave];
+    for (int j = 0; j < J; ++j) acc[j] += wgt * po[j * kWave];
   }
   const int row = i0 + kWRows * w + (lane & 31);
   if (row >= rq.C) return;
   half_t* out = static_cast<half_t*>(a.out) + ((int64_t)(rq.q0 + row) * a.num_q_heads + h) * D;
   const float inv = a.v_scale / lsum;
 #pragma unroll
-  for (int dt = 0; dt < DT; ++dt)
+  for (int j = 0; j < J; ++j) {  // float4 index jj = dt * 4 + v4 of the epilogue's layout
+    const int jj = part * J + j;
+    const int dt = jj / 4, v4 = jj % 4;
+    half4_t x;
 #pragma unroll
-    for (int v4 = 0; v4 < 4; ++v4) {
-      half4_t x;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) x[e] = (half_t)(acc[dt * 4 + v4][e] * inv);
-      *reinterpret_cast<half4_t*>(out + 32 * dt + 8 * v4 + 4 * g) = x;
-    }
+    for (int e = 0; e < 4; ++e) x[e] = (half_t)(acc[j][e] * inv);
+    *reinterpret_cast<half4_t*>(out + 32 * dt + 8 * v4 + 4 * g) = x;
+  }
 }
 
 template <int D, typename KV>
@@ -651,7 +673,7 @@ hipError_t launch_prefill_d(PrefillArgs a, hipStream_t stream) {
   hipLaunchKernelGGL((prefill_kernel<D, KV>), dim3((unsigned)wgs), dim3(kThreads), smem, stream, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.max_pieces == 1) return e;
-  const int64_t mwgs = (int64_t)a.num_reqs * a.num_q_heads * tiles;
+  const int64_t mwgs = (int64_t)a.num_reqs * a.num_q_heads * tiles * (kBM / kWRows);
   if (mwgs > INT32_MAX) return hipErrorInvalidValue;
   hipLaunchKernelGGL((prefill_merge_kernel<D>), dim3((unsigned)mwgs), dim3(kThreads), 0, stream, a);
   return hipGetLastError();
