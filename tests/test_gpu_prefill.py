@@ -226,3 +226,15 @@ def test_prefill_long_prompt_workload_sampled():
     torch.cuda.empty_cache()
     rows = np.concatenate([np.arange(0, 512, 23), [127, 128, 383, 384, 511]])
     check_attention(got[rows], oracle_prefill(inp, rows=set(rows.tolist()))[rows], "long prompt")
+
+
+def test_prefill_many_requests_launch_order():
+    """300 short requests (above the 256 that are ranked by length): launch order, no
+    split; every row against the oracle."""
+    rng = np.random.default_rng(61)
+    priors = rng.integers(0, 200, size=300).tolist()
+    chunks = rng.integers(1, 6, size=300).tolist()
+    inp = workloads.mixed_case(61, priors, chunks, [], 4, 4, 64)
+    assert workspace_bytes(inp) == 0
+    got, _ = gpu_prefill(inp)
+    check_attention(got, oracle_prefill(inp), "300 requests")
