@@ -218,3 +218,29 @@ def test_shared_prefix_fp8_prefix_groups():
     pairs = [(int(b), int(h)) for b, h in zip(rng.integers(0, 256, 200), rng.integers(0, 32, 200))]
     want = oracle.decode_rows(q, fp8.dequantize_pool(pool, 1.0, 1.0), bt, L, inp.scale, pairs)
     check_attention(np.stack([got[b, h] for b, h in pairs]), want, "shared fp8 prefix-groups")
+
+
+@pytest.mark.parametrize("D", [64, 128])
+def test_prefill_fp8_split_matches_unsplit_and_oracle(D):
+    """FP8 prefill with long priors: the context split (pieces merged by log-sum-exp, the
+    value scale applied after the merge) agrees with the oracle on the dequantized pool
+    and with the unsplit launch."""
+    inp = workloads.mixed_case(126 + D, [5000, 1900, 30], [200, 256, 64], [], 16, 4, D)
+    q, bt, qsl, lens = inp.prefill_part()
+    mq, ms = int(np.diff(qsl).max()), int(lens.max())
+    assert pkv.pa_prefill_workspace_bytes(len(lens), 16, mq, ms, D) > 0
+    ks, vs = 0.04, 0.03
+    pool_h = quantized_step_pool(inp, ks, vs)
+    pool = dev(pool_h)
+    outs = []
+    for split in (True, False):
+        out = torch.full(q.shape, float("nan"), dtype=torch.float16, device="cuda")
+        note(f"prefill fp8 D={D} split={split}")
+        pkv.pa_prefill_chunk_fp8(out, dev(q), pool, dev(bt), dev(qsl), dev(lens), mq, ms,
+                                 inp.scale, ks, vs, split=split)
+        outs.append(host(out).astype(np.float64))
+    rows = np.arange(0, q.shape[0], 4)
+    want = oracle.prefill_chunk(q, fp8.dequantize_pool(pool_h, ks, vs), bt, qsl, lens, inp.scale,
+                                rows=set(rows.tolist()))
+    check_attention(outs[0][rows], want[rows], f"fp8 split D{D}")
+    assert np.abs(outs[0] - outs[1]).max() <= 2e-3
