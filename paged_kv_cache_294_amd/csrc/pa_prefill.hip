@@ -7,6 +7,9 @@
 // chunk); each wave owns 32 query rows. Workgroups are issued heaviest first (requests in
 // decreasing order of context length, ranked inside the kernel; later row tiles first),
 // and all row tiles of one (request, head) go to the same XCD so they share its L2.
+// A launch whose tiles cannot fill the GPU may also cut each request's context into
+// pieces (the context split below), one workgroup per (piece, head, tile), merged by a
+// second kernel.
 //
 // Staging. The KV context is streamed in stages of 32 tokens (two 16-token blocks found
 // through the table). Each stage's K and V rows go from HBM straight into LDS with
