@@ -238,3 +238,38 @@ def test_prefill_many_requests_launch_order():
     assert workspace_bytes(inp) == 0
     got, _ = gpu_prefill(inp)
     check_attention(got, oracle_prefill(inp), "300 requests")
+
+
+@pytest.mark.parametrize("split", [True, False])
+def test_prefill_zero_length_chunk_among_others(split):
+    """A request with no query rows this step (an empty chunk between two others, its
+    context still cached): its neighbours are unaffected and nothing is written for it,
+    with and without the context split."""
+    inp = workloads.mixed_case(62, [3000, 1200, 2500], [100, 1, 70], [], 8, 8, 128)
+    q, bt, qsl, lens = inp.prefill_part()
+    pool = appended_pool(inp)
+    # request 1 keeps its 1201 cached tokens but asks for no rows
+    qsl0 = qsl.copy()
+    qsl0[2:] -= 1
+    lens0 = lens.copy()
+    lens0[1] -= 1
+    keep = np.r_[0:int(qsl[1]), int(qsl[2]):int(qsl[3])]
+    qd = dev(np.ascontiguousarray(q[keep]))
+    out = torch.full_like(qd, float("nan"))
+    pkv.pa_prefill_chunk(out, qd, pool, dev(bt), dev(qsl0), dev(lens0),
+                         int(np.diff(qsl0).max()), int(lens0.max()), inp.scale, split=split)
+    got = host(out)
+    ref = oracle.prefill_chunk(q[keep], oracle.kv_append(inp.pool, inp.key_new, inp.value_new,
+                                                         inp.slot_mapping),
+                               bt, qsl0, lens0, inp.scale)
+    check_attention(got, ref, f"empty chunk split={split}")
+
+
+def test_prefill_2048_row_chunk():
+    """One 2048-row chunk (16 row tiles) after 2000 cached tokens next to a short request;
+    sampled rows of every tile against the oracle."""
+    inp = workloads.mixed_case(63, [2000, 10], [2048, 40], [], 8, 4, 128)
+    note("prefill 2048-row chunk")
+    got, _ = gpu_prefill(inp)
+    rows = np.concatenate([np.arange(0, 2088, 29), [127, 128, 1023, 1024, 2047, 2048, 2087]])
+    check_attention(got[rows], oracle_prefill(inp, rows=set(rows.tolist()))[rows], "2048 rows")
