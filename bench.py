@@ -22,7 +22,9 @@ default, as a serving engine runs it) or launch it call by call (``--launch eage
 
 Printed: one JSON line. ``value`` is the KV-read rate of the step (algorithmic bytes:
 every decode context token's K and V row once) over the whole step time; ``roofline``
-is the decode kernel call against the 8 TB/s HBM peak; ``cpu_baseline`` is the oracle on
+is the step's dominant call: the decode against the 8 TB/s HBM peak, or, when the
+prefill takes longer (long-prefill), the prefill against the fp16 matrix-core peak;
+``cpu_baseline`` is the oracle on
 the host cores, run before the GPU is touched.
 """
 
@@ -749,6 +751,22 @@ def main():
             "gpu_cache_usage": used_blocks / inp.num_blocks,
         },
     }
+    if inp.num_prefill and prefill_ms > decode_ms:
+        # the prefill call dominates the step: its roofline is the matrix-core peak
+        pf = kernels["prefill"]
+        result["decode_roofline"] = result["roofline"]
+        result["roofline"] = {
+            "kernel": ("pa_prefill_chunk_fp8" if kv_fp8 else "pa_prefill_chunk") +
+                      (" (prefill and context-split merge kernels)" if step.pws_bytes
+                       else " (prefill kernel)"),
+            "bound": "mfma",
+            "achieved": pf["TFLOPs"],
+            "peak": MFMA_F16_PEAK_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": pf["frac_mfma_peak"],
+            "traffic": None,
+            "algorithmic_flops_per_launch": prefill_flops(inp),
+        }
     print(json.dumps(result), flush=True)
 
 
