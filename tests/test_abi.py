@@ -243,3 +243,34 @@ def test_default_partition_size(lib):
         ps = f(*args)
         assert ps >= 16 and ps % 16 == 0
     assert f(4, 32, 32, -1) == -1 and f(4, 12, 8, 100) == -1 and f(-1, 8, 8, 10) == -1
+
+
+def test_prefill_workspace_choice(monkeypatch):
+    """The binding's workspace decision for pa_prefill_chunk, with the size query stubbed:
+    no split asked or none useful -> no workspace; a bad size -> error; under graph capture
+    without a caller workspace -> unsplit; host memory is refused, never used."""
+    import torch
+
+    args = (0,) * 6 + (3, 100, 64, 4096, 8, 8, 128)  # R, total_q, max_q, max_seq, Hq, Hkv, D
+    seen = []
+
+    def fake_bytes(R, hq, mq, ms, d):
+        seen.append((R, hq, mq, ms, d))
+        return fake_bytes.value
+
+    monkeypatch.setattr(_lib, "pa_prefill_workspace_bytes", fake_bytes)
+    fake_bytes.value = 4096
+    assert _lib._prefill_workspace(args, None, False, "cpu") == (0, 0)
+    assert seen == []  # split off: not even asked
+    fake_bytes.value = 0
+    assert _lib._prefill_workspace(args, None, True, "cpu") == (0, 0)
+    assert seen == [(3, 8, 64, 4096, 128)]
+    fake_bytes.value = -1
+    with pytest.raises(pkv.PagedKVError):
+        _lib._prefill_workspace(args, None, True, "cpu")
+    fake_bytes.value = 4096
+    monkeypatch.setattr(_lib, "_CAPTURING", 1)
+    assert _lib._prefill_workspace(args, None, True, "cpu") == (0, 0)
+    monkeypatch.setattr(_lib, "_CAPTURING", 0)
+    with pytest.raises(TypeError):
+        _lib._prefill_workspace(args, torch.empty(4096, dtype=torch.uint8), True, "cpu")
