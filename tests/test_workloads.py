@@ -102,6 +102,19 @@ def test_mixed_fits_the_scheduler_limits():
     assert d.min() >= 256 and d.max() <= 4096
 
 
+def test_long_prompt_workload_shape():
+    """The long-prompt step: one 512-row chunk ending a 32768-token prompt (32256 tokens
+    cached), 8 decodes U{256..4096}, 32 heads x 128; its 520 new tokens are appended."""
+    inp = workloads.long_prompt_prefill()
+    assert inp.num_prefill == 1 and inp.num_seqs == 9
+    assert int(inp.seq_lens[0]) == 32768 and int(inp.q_lens[0]) == 512
+    assert inp.num_q_heads == 32 and inp.num_kv_heads == 32 and inp.head_size == 128
+    d = inp.seq_lens[1:]
+    assert d.min() >= 256 and d.max() <= 4096 and np.all(inp.q_lens[1:] == 1)
+    assert len(inp.slot_mapping) == 512 + 8
+    assert inp.block_tables.shape[1] >= 32768 // 16
+
+
 # ---------------------------------------------------------------------------------------
 # independence of the oracle from the product path
 # ---------------------------------------------------------------------------------------
