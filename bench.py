@@ -404,10 +404,11 @@ class Step:
         rec(3)
 
 
-def run_counter_sequence(inp, partition_size, kv_stream, kv_fp8=False):
+def run_counter_sequence(inp, partition_size, kv_stream, kv_fp8=False, shared_prefix=False,
+                         prefill_split=True):
     """Dispatches for counter passes, in a fixed order: a torch copy of 1 GiB (reads and
     writes exactly 1 GiB: the calibration of FETCH_SIZE / WRITE_SIZE), pa_stream_read of
-    1 GiB (reads 1 GiB), then three steps of the workload."""
+    1 GiB (reads 1 GiB), then three steps of the workload, run as the bench runs them."""
     import torch
     import paged_kv_cache_294_amd as pkv
 
@@ -415,7 +416,7 @@ def run_counter_sequence(inp, partition_size, kv_stream, kv_fp8=False):
     src = torch.ones(nbytes, dtype=torch.uint8, device="cuda")
     dst = torch.empty_like(src)
     sink = torch.zeros(pkv.pa_stream_read_sink_len(nbytes), dtype=torch.float32, device="cuda")
-    step = Step(torch, pkv, inp, partition_size, kv_stream, kv_fp8)
+    step = Step(torch, pkv, inp, partition_size, kv_stream, kv_fp8, shared_prefix, prefill_split)
     torch.cuda.synchronize()
     dst.copy_(src)
     torch.cuda.synchronize()
@@ -525,7 +526,7 @@ def main():
     ap.add_argument("--decode", choices=("auto", "plain", "shared-prefix"), default="auto",
                     help="shared-prefix: pa_decode_shared_prefix over the workload's prompt "
                          "groups (reads each shared prefix once); auto: that when the workload "
-                         "has prompt groups and an fp16 cache, else plain")
+                         "has prompt groups, else plain")
     ap.add_argument("--kv-dtype", choices=("fp16", "fp8"), default="fp16",
                     help="cache element: fp16, or FP8 E4M3 codes (decode-only workloads; the "
                          "prefill kernel reads fp16 caches only)")
@@ -594,7 +595,8 @@ def main():
     kv_bytes = kv_unique_bytes(inp, elem_bytes) if shared else logical_bytes
 
     if args.mode == "counters":
-        run_counter_sequence(inp, args.partition_size, kv_stream, kv_fp8)
+        run_counter_sequence(inp, args.partition_size, kv_stream, kv_fp8, shared_prefix,
+                             args.prefill_split == "on")
         return
 
     cpu = None
