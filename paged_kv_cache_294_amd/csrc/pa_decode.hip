@@ -33,6 +33,8 @@
 // them: M = max m_p, w_p = l_p * 2^(m_p - M), out = sum w_p o_p / sum w_p.
 #include <atomic>
 
+#include <type_traits>
+
 #include "pa_device.h"
 #include "pa_launch.h"
 
@@ -464,6 +466,23 @@ struct GqaGeo {
   static constexpr int VPITCH = D + 16;      // LDS row pitch (halves): 8 rows fill 64 banks
 };
 
+// An FP8 cache's grouped-query loads bring 16 codes per lane (one 16-byte load); they are
+// widened to fp16 where they are used.
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(1))) const u32x4_t gconst_u32x4_t;
+
+template <bool Stream>
+__device__ __forceinline__ u32x4_t load_codes16(const fp8_t* p) {
+  gconst_u32x4_t* gp = (gconst_u32x4_t*)(p);
+  if constexpr (Stream)
+    return __builtin_nontemporal_load(gp);
+  else
+    return *gp;
+}
+
+__device__ __forceinline__ half8_t widen_lo(u32x4_t w) { return widen_fp8x8(u32x2_t{w[0], w[1]}); }
+__device__ __forceinline__ half8_t widen_hi(u32x4_t w) { return widen_fp8x8(u32x2_t{w[2], w[3]}); }
+
 // The group of sequence b: g with group_start[g] <= b < group_start[g + 1], or -1.
 __device__ __forceinline__ int group_of(const DecodeArgs& a, int b) {
   int lo = 0, hi = a.num_groups;
@@ -488,6 +507,16 @@ __global__ __launch_bounds__(kThreads) void decode_gqa_kernel(const DecodeArgs a
   constexpr int S = 16 / G;  // samples of a group per tile in the prefix pass
   using Gm = GqaGeo<D>;
   constexpr int KS = Gm::KS, DT = Gm::DT, PIECES = Gm::PIECES, VLOADS = Gm::VLOADS;
+  // FP8 cache: one 16-byte load per lane covers two k-steps of K (dims 64j + 16q4 .. +16,
+  // the first 8 for k-step 2j, the next 8 for 2j + 1; the query's dims follow the same
+  // order, so the products and their sum over dims are unchanged) and two 8-element pieces
+  // of V; the codes stay packed until they are used
+  constexpr bool kFp8 = sizeof(KV) == 1;
+  constexpr int KL = kFp8 ? KS / 2 : KS;          // K loads per lane and block
+  constexpr int VL = kFp8 ? VLOADS / 2 : VLOADS;  // V loads per lane and block
+  constexpr int VPL = kFp8 ? 2 : 1;               // 8-element V pieces per load
+  using Raw = std::conditional_t<kFp8, u32x4_t, half8_t>;  // what one load brings
+  static_assert(!kFp8 || (KS % 2 == 0 && VLOADS % 2 == 0), "FP8 loads pair k-steps and pieces");
   constexpr int VPITCH = Gm::VPITCH;
   constexpr float kSlack = 8.0f;
   __shared__ __align__(16) half_t vstage[kWavesPerGroup][kBlockSize * VPITCH];
@@ -573,7 +602,8 @@ __global__ __launch_bounds__(kThreads) void decode_gqa_kernel(const DecodeArgs a
   half8_t qb[KS];
 #pragma unroll
   for (int ks = 0; ks < KS; ++ks)
-    qb[ks] = col_ok ? load16(qp + ((int64_t)col_seq * a.num_q_heads + col_head) * D + 32 * ks + 8 * q4)
+    qb[ks] = col_ok ? load16(qp + ((int64_t)col_seq * a.num_q_heads + col_head) * D +
+                             (kFp8 ? 64 * (ks >> 1) + 16 * q4 + 8 * (ks & 1) : 32 * ks + 8 * q4))
                     : half8_t{};
 
   const int kv_row = a.num_kv_heads * D;
@@ -582,15 +612,22 @@ __global__ __launch_bounds__(kThreads) void decode_gqa_kernel(const DecodeArgs a
   const KV* pool = static_cast<const KV*>(a.pool);
   const int32_t* bt = a.block_tables + (int64_t)b * a.max_blocks_per_seq;
   // per-lane element offsets inside a block
-  const int koff = n * tok_stride + kvh * D + 8 * q4;  // + 32 ks
-  int voff[VLOADS], vlds[VLOADS];
+  constexpr int KSTEP = kFp8 ? 64 : 32;  // elements between a lane's K loads
+  const int koff = n * tok_stride + kvh * D + (kFp8 ? 16 : 8) * q4;  // + KSTEP j
+  int voff[VL], vlds[VL];
 #pragma unroll
-  for (int j = 0; j < VLOADS; ++j) {
+  for (int j = 0; j < VL; ++j) {
     const int idx = lane + kWave * j;
-    const int t = idx / PIECES, c = idx % PIECES;
-    voff[j] = t * tok_stride + kv_row + kvh * D + 8 * c;
-    vlds[j] = t * VPITCH + 8 * c;
+    const int t = idx / (PIECES / VPL), c = idx % (PIECES / VPL);
+    voff[j] = t * tok_stride + kv_row + kvh * D + 8 * VPL * c;
+    vlds[j] = t * VPITCH + 8 * VPL * c;
   }
+  auto load_raw = [&](const KV* p) -> Raw {
+    if constexpr (kFp8)
+      return load_codes16<Stream>(p);
+    else
+      return load_kv8<KV, Stream>(p);
+  };
   // transposing read of V tile dt: token 4q4 + n/4, dims 16dt + 4(n%4)
   const int vtr = (4 * q4 + n / 4) * VPITCH + 4 * (n % 4);
 
@@ -601,19 +638,19 @@ __global__ __launch_bounds__(kThreads) void decode_gqa_kernel(const DecodeArgs a
 
   int bt_vec = (lane < blk_end - blk_begin) ? bt[blk_begin + lane] : 0;
   bool bad_table = false;
-  half8_t kc[KS], vc[VLOADS];
+  Raw kc[KL], vc[VL];
   {
     const int phys = __builtin_amdgcn_readfirstlane(bt_vec);
     bad_table = phys < 0 || phys >= a.num_blocks;
     const KV* base = pool + (bad_table ? 0 : (int64_t)phys * block_elems);
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) kc[ks] = load_kv8<KV, Stream>(base + koff + 32 * ks);
+    for (int j = 0; j < KL; ++j) kc[j] = load_raw(base + koff + KSTEP * j);
 #pragma unroll
-    for (int j = 0; j < VLOADS; ++j) vc[j] = load_kv8<KV, Stream>(base + voff[j]);
+    for (int j = 0; j < VL; ++j) vc[j] = load_raw(base + voff[j]);
   }
 
   for (int jb = blk_begin; jb < blk_end && !bad_table; ++jb) {
-    half8_t kn[KS], vn[VLOADS];
+    Raw kn[KL], vn[VL];
     const int jn = jb + 1;
     if (jn < blk_end) {
       const int k64 = (jn - blk_begin) & 63;
@@ -622,23 +659,35 @@ __global__ __launch_bounds__(kThreads) void decode_gqa_kernel(const DecodeArgs a
       bad_table = phys < 0 || phys >= a.num_blocks;
       const KV* base = pool + (bad_table ? 0 : (int64_t)phys * block_elems);
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) kn[ks] = load_kv8<KV, Stream>(base + koff + 32 * ks);
+      for (int j = 0; j < KL; ++j) kn[j] = load_raw(base + koff + KSTEP * j);
 #pragma unroll
-      for (int j = 0; j < VLOADS; ++j) vn[j] = load_kv8<KV, Stream>(base + voff[j]);
+      for (int j = 0; j < VL; ++j) vn[j] = load_raw(base + voff[j]);
     }
     const int tok0 = jb * kBlockSize;
     const bool tail = tok0 + kBlockSize > L;
     // stage V (tokens past the context end as zeros: their slots may hold anything)
 #pragma unroll
-    for (int j = 0; j < VLOADS; ++j) {
-      const int t = (lane + kWave * j) / PIECES;
-      *reinterpret_cast<half8_t*>(vs + vlds[j]) = (tail && tok0 + t >= L) ? half8_t{} : vc[j];
+    for (int j = 0; j < VL; ++j) {
+      const int t = (lane + kWave * j) / (PIECES / VPL);
+      const bool zero = tail && tok0 + t >= L;
+      if constexpr (kFp8) {
+        *reinterpret_cast<half8_t*>(vs + vlds[j]) = zero ? half8_t{} : widen_lo(vc[j]);
+        *reinterpret_cast<half8_t*>(vs + vlds[j] + 8) = zero ? half8_t{} : widen_hi(vc[j]);
+      } else {
+        *reinterpret_cast<half8_t*>(vs + vlds[j]) = zero ? half8_t{} : vc[j];
+      }
     }
     // S^T of the block
     float4_t sacc = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks)
-      sacc = __builtin_amdgcn_mfma_f32_16x16x32_f16(kc[ks], qb[ks], sacc, 0, 0, 0);
+    for (int ks = 0; ks < KS; ++ks) {
+      half8_t ka;
+      if constexpr (kFp8)
+        ka = (ks & 1) ? widen_hi(kc[ks >> 1]) : widen_lo(kc[ks >> 1]);
+      else
+        ka = kc[ks];
+      sacc = __builtin_amdgcn_mfma_f32_16x16x32_f16(ka, qb[ks], sacc, 0, 0, 0);
+    }
     // mask, column max over the block's 16 tokens, lazy rescale
     float mloc = neg_inf();
 #pragma unroll
@@ -679,9 +728,9 @@ __global__ __launch_bounds__(kThreads) void decode_gqa_kernel(const DecodeArgs a
     // the next block's V overwrites the stage only after these reads have returned
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) kc[ks] = kn[ks];
+    for (int j = 0; j < KL; ++j) kc[j] = kn[j];
 #pragma unroll
-    for (int j = 0; j < VLOADS; ++j) vc[j] = vn[j];
+    for (int j = 0; j < VL; ++j) vc[j] = vn[j];
   }
 
   // column sums over the four 16-lane groups
