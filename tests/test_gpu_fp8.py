@@ -80,7 +80,7 @@ def test_append_fp8_decode256_bit_exact():
 
 
 @pytest.mark.parametrize("D", [64, 128])
-@pytest.mark.parametrize("G", [1, 4])
+@pytest.mark.parametrize("G", [1, 2, 4, 8])
 @pytest.mark.parametrize("ps", [16, 512])
 def test_decode_fp8_small(D, G, ps):
     inp = workloads.decode_case(90 + D + G, [1, 2, 15, 16, 17, 100, 700, 1500], 4 * G, 4, D,
@@ -190,21 +190,22 @@ def run_shared_fp8(inp, pool_u8, ks, vs, group_start, prefix_lens, ps):
     return host(out)
 
 
-@pytest.mark.parametrize("G", [1, 4])
-def test_shared_prefix_fp8_matches_oracle(G):
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("G", [1, 4, 8])
+def test_shared_prefix_fp8_matches_oracle(G, D):
     rng = np.random.default_rng(130 + G)
     priv = rng.integers(0, 70, 24)
     priv[2] = 0
-    inp = workloads.prefix_shared_case(130 + G, 3, 8, 4, priv, 4 * G, 4, 128)
+    inp = workloads.prefix_shared_case(130 + G, 3, 8, 4, priv, 4 * G, 4, D)
     ks, vs = 0.02, 0.03
     pool = np.concatenate([fp8.quantize(inp.pool[:, :, 0:1], ks),
                            fp8.quantize(inp.pool[:, :, 1:2], vs)], axis=2)
     q, bt, L = inp.decode_part()
     want = oracle.decode(q, fp8.dequantize_pool(pool, ks, vs), bt, L, inp.scale)
     for ps in (16, 256):
-        note(f"shared prefix fp8 G={G} ps={ps}")
+        note(f"shared prefix fp8 G={G} D={D} ps={ps}")
         got = run_shared_fp8(inp, pool, ks, vs, [0, 8, 16, 24], [64, 64, 64], ps)
-        check_attention(got, want, f"shared fp8 G{G} ps{ps}")
+        check_attention(got, want, f"shared fp8 G{G} D{D} ps{ps}")
 
 
 def test_shared_prefix_fp8_prefix_groups():
