@@ -20,8 +20,13 @@ into their pool slots, ``pa_prefill_chunk`` for prefill chunks (mixed workload o
 The timed steps replay the step captured once into a HIP graph (``--launch graph``, the
 default, as a serving engine runs it) or launch it call by call (``--launch eager``).
 
+Timing: by default each timed step is bracketed by its own HIP events and followed by an
+untimed 1 GiB read that flushes the L2 caches and the Infinity Cache (``--flush on``), so
+no step starts with the previous one's blocks cached; the mean, median and min of those
+per-step times are reported, and back-to-back steps without the flush beside them.
+
 Printed: one JSON line. ``value`` is the KV-read rate of the step (algorithmic bytes:
-every decode context token's K and V row once) over the whole step time; ``roofline``
+every decode context token's K and V row once) over the mean step time; ``roofline``
 is the step's dominant call: the decode against the 8 TB/s HBM peak, or, when the
 prefill takes longer (long-prefill), the prefill against the fp16 matrix-core peak;
 ``cpu_baseline`` is the oracle on
@@ -244,6 +249,23 @@ def stream_read_gbps(torch, pkv, nbytes=4 << 30, reps=10):
     del buf, sink
     torch.cuda.empty_cache()
     return nbytes / (ms * 1e-3) / 1e9
+
+
+def make_flush(torch, nbytes=1 << 30):
+    """An untimed cache flush between timed steps: one read of a 1 GiB buffer with ordinary
+    (cached) loads, which evicts what the last step left in the XCDs' L2 and in the
+    256 MB Infinity Cache. Reads only, so no dirty lines are written back during the next
+    step."""
+    buf = torch.ones(nbytes // 4, dtype=torch.float32, device="cuda")
+
+    def flush():
+        buf.sum()
+    return flush
+
+
+def stats_ms(xs):
+    xs = np.asarray(xs, dtype=np.float64)
+    return {"mean": float(xs.mean()), "median": float(np.median(xs)), "min": float(xs.min())}
 
 
 def block_manager_leg(pkv, inp):
@@ -533,6 +555,11 @@ def main():
     ap.add_argument("--prefill-split", choices=("on", "off"), default="on",
                     help="on: pa_prefill_chunk gets its split-context workspace (long contexts "
                          "cut into pieces merged by log-sum-exp); off: one workgroup per row tile")
+    ap.add_argument("--flush", choices=("on", "off"), default="on",
+                    help="on: an untimed 1 GiB cache-flushing read between timed steps, each "
+                         "step timed on its own (mean, median, min reported; back-to-back "
+                         "steps are timed too and reported as *_no_flush); off: back-to-back "
+                         "steps only")
     ap.add_argument("--cpu-cores", type=int, default=16)
     ap.add_argument("--mode", choices=("bench", "counters"), default="bench",
                     help="counters: a short fixed dispatch sequence for rocprofv3 --pmc passes "
@@ -584,6 +611,8 @@ def main():
         sys.exit(2)
     if args.partition_size <= 0 and shared_prefix:
         args.partition_size = 512  # fastest of 256 .. 2048 for 64 groups of 1024-token prompts
+    elif args.partition_size <= 0 and args.workload == "long32k":
+        args.partition_size = 512  # the long-context workload is specified with 512-token partitions
     elif args.partition_size <= 0:  # the library's choice for its kernels (a host-only call)
         import paged_kv_cache_294_amd as pkv
         args.partition_size = pkv.pa_decode_default_partition_size(
@@ -633,22 +662,38 @@ def main():
     torch.cuda.synchronize()
     log(f"warmup done; timing {args.steps} steps")
 
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
-    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
+    flush = make_flush(torch) if args.flush == "on" else None
+
+    def eager_loop(with_flush):
+        """Per-step event times (ms) of append, prefill, decode and the whole step."""
+        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+        torch.cuda.synchronize()
+        for i in range(args.steps):
+            step.run(evs[i])
+            if with_flush:
+                flush()
+        torch.cuda.synchronize()
+        return {"append": [e[0].elapsed_time(e[1]) for e in evs],
+                "prefill": [e[1].elapsed_time(e[2]) for e in evs],
+                "decode": [e[2].elapsed_time(e[3]) for e in evs],
+                "step": [e[0].elapsed_time(e[3]) for e in evs]}
+
     w0 = time.perf_counter()
-    start.record()
-    for i in range(args.steps):
-        step.run(evs[i])
-    end.record()
-    torch.cuda.synchronize()
+    eag = eager_loop(flush is not None)
     wall = time.perf_counter() - w0
-    ms_step = start.elapsed_time(end) / args.steps
-    append_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
-    prefill_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in evs]))
-    decode_ms = float(np.mean([e[2].elapsed_time(e[3]) for e in evs]))
+    eag_nf = eager_loop(False) if flush is not None else eag
+    append_ms = float(np.mean(eag["append"]))
+    prefill_ms = float(np.mean(eag["prefill"]))
+    decode_ms = float(np.mean(eag["decode"]))
+    decode_stats = stats_ms(eag["decode"])
+    decode_nf_ms = float(np.mean(eag_nf["decode"]))
+    ms_step = float(np.mean(eag["step"]))
+    step_stats = stats_ms(eag["step"])
+    ms_step_nf = float(np.mean(eag_nf["step"]))
     log(f"step {ms_step:.3f} ms (wall {wall / args.steps * 1e3:.3f} ms): append "
-        f"{append_ms * 1e3:.1f} us, prefill {prefill_ms * 1e3:.1f} us, decode {decode_ms * 1e3:.1f} us")
+        f"{append_ms * 1e3:.1f} us, prefill {prefill_ms * 1e3:.1f} us, decode {decode_ms * 1e3:.1f} us"
+        f" (median {decode_stats['median'] * 1e3:.1f}, min {decode_stats['min'] * 1e3:.1f};"
+        f" back to back without flush {decode_nf_ms * 1e3:.1f} us)")
 
     eager_ms_step = ms_step
     if args.launch == "graph":
@@ -661,15 +706,31 @@ def main():
         for _ in range(args.warmup):
             graph.launch()
         torch.cuda.synchronize()
+        if flush is not None:  # each replay timed on its own, the flush between them untimed
+            gev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                   for _ in range(args.steps)]
+            with torch.cuda.stream(side):
+                for gs_, ge_ in gev:
+                    gs_.record(side)
+                    graph.launch()
+                    ge_.record(side)
+                    flush()
+            torch.cuda.synchronize()
+            step_stats = stats_ms([a.elapsed_time(b) for a, b in gev])
+            ms_step = step_stats["mean"]
         gs, ge = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         gs.record(side)
         for _ in range(args.steps):
             graph.launch()
         ge.record(side)
         torch.cuda.synchronize()
-        ms_step = gs.elapsed_time(ge) / args.steps
+        ms_step_nf = gs.elapsed_time(ge) / args.steps
+        if flush is None:
+            ms_step = ms_step_nf
+            step_stats = {"mean": ms_step}
         graph.close()
-        log(f"graph replay: step {ms_step:.3f} ms (eager {eager_ms_step:.3f} ms)")
+        log(f"graph replay: step {ms_step:.3f} ms (back to back without flush {ms_step_nf:.3f} ms; "
+            f"eager {eager_ms_step:.3f} ms)")
 
     copies = None
     if not args.no_block_copies:
@@ -683,9 +744,11 @@ def main():
     nparts = pkv.pa_num_partitions(step.mcl, args.partition_size)
     traffic = read_traffic(f"pa_decode_{args.workload}{'_fp8' if kv_fp8 else ''}_counters.txt", source_digest(DECODE_SRC))
     used_blocks = int(sum(-(-int(L) // 16) for L in inp.seq_lens))
-    kernels = {"decode": {"ms": decode_ms, "kv_read_GBps": achieved,
+    kernels = {"decode": {"ms": decode_ms, "ms_median": decode_stats["median"],
+                          "ms_min": decode_stats["min"], "kv_read_GBps": achieved,
                           "frac_hbm_peak": achieved / HBM_PEAK_GBPS, "partitions": nparts,
-                          "kv_stream": kv_stream}}
+                          "kv_stream": kv_stream, "ms_no_flush": decode_nf_ms,
+                          "kv_read_GBps_no_flush": kv_bytes / (decode_nf_ms * 1e-3) / 1e9}}
     if len(inp.slot_mapping):
         kernels["append"] = {"us": append_ms * 1e3, "tokens": len(inp.slot_mapping),
                              "GBps": append_bytes(inp, elem_bytes) / (append_ms * 1e-3) / 1e9}
@@ -706,6 +769,11 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": ms_step,
+        "ms_per_step_median": step_stats.get("median"),
+        "ms_per_step_min": step_stats.get("min"),
+        "ms_per_step_no_flush": ms_step_nf,
+        "cache_flush": ("an untimed 1 GiB read between timed steps; each step timed on its "
+                        "own with HIP events" if flush is not None else None),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,

@@ -85,10 +85,19 @@ int64_t pa_num_blocks_fit(int64_t free_bytes, double utilization, int32_t block_
                           int32_t num_kv_heads, int32_t head_size, int32_t elem_bytes);
 
 /* Slot of logical position `pos` of a sequence whose block-table row (host
- * memory, at least pos / block_size + 1 entries) is `block_table_row`. */
+ * memory, at least pos / block_size + 1 entries) is `block_table_row`:
+ * block_table_row[pos / block_size] * block_size + pos % block_size. Logical
+ * block j of a sequence is held by whichever physical block its table names
+ * (page "vLLM GitHub 项目 …", section 二, item 1; page "vLLM 部署深度指南",
+ * section "PagedAttention 原理": the block-table figure maps logical to
+ * physical blocks). -1 for a NULL row, pos < 0 or a negative entry. */
 int64_t pa_slot(const int32_t* block_table_row, int64_t pos, int32_t block_size);
 
-/* Element offset in the pool of (slot, kv, head, dim); kv 0 = key, 1 = value. */
+/* Element offset in the pool of (slot, kv, head, dim); kv 0 = key, 1 = value:
+ * ((slot * 2 + kv) * num_kv_heads + head) * head_size + dim, the row-major index of
+ * the pool tensor [num_blocks][block_size][2][num_kv_heads][head_size] of the
+ * simplified KV-cache listing (page "vLLM 部署深度指南", section "PagedAttention
+ * 原理"). -1 when an index is out of range. */
 int64_t pa_kv_elem_offset(int64_t slot, int32_t kv, int32_t head, int32_t dim,
                           int32_t num_kv_heads, int32_t head_size);
 
@@ -142,7 +151,11 @@ pa_status pa_kv_append(void* kv_pool, const void* key, const void* value,
 
 /* One decode step of paged attention: query row b (one token per sequence, at the
  * sequence's last position) attends to the first context_lens[b] tokens of
- * sequence b, the token appended this step included.
+ * sequence b, the token appended this step included. The keys and values are
+ * found block by block through the sequence's table (page "vLLM GitHub 项目 …",
+ * section 二, item 1: logical blocks mapped to non-contiguous physical blocks;
+ * page "vLLM 部署深度指南", section "PagedAttention 原理": the pool layout), and
+ * the attention is textbook softmax attention over them.
  *
  *   out           device fp16 [num_seqs][num_q_heads][head_size], written
  *   q             device fp16 [num_seqs][num_q_heads][head_size]
@@ -154,7 +167,8 @@ pa_status pa_kv_append(void* kv_pool, const void* key, const void* value,
  *                 max_blocks_per_seq * block_size. A length of 0 gives a zero row; a
  *                 length outside these bounds, or a table entry outside
  *                 [0, num_blocks), gives a NaN row.
- *   scale         softmax scale, normally 1 / sqrt(head_size)
+ *   scale         softmax scale, finite and > 0, normally 1 / sqrt(head_size)
+ *                 (PA_ERR_INVALID otherwise)
  *   partition_size  tokens per split-context partition, a positive multiple of
  *                 block_size; a context longer than one partition is computed as
  *                 partitions merged by a log-sum-exp reduction
@@ -168,7 +182,18 @@ pa_status pa_kv_append(void* kv_pool, const void* key, const void* value,
  *                 served from cache (neighbouring sequences then run together). Results
  *                 are identical.
  * Query head h reads KV head h / (num_q_heads / num_kv_heads). Arithmetic: fp16
- * inputs, fp32 products, sums and softmax, fp16 output rounded to nearest even. */
+ * inputs, fp32 products, sums and online softmax (base-2 exponentials of
+ * log2(e)-scaled scores), fp16 output rounded to nearest even.
+ *  - One query head per KV head: the probabilities p stay fp32 and the running max is
+ *    the exact running max.
+ *  - Grouped query heads (2, 4 or 8 per KV head): the scores and the P.V product run
+ *    on the matrix cores, which take p rounded to fp16 (nearest even); the row sum l
+ *    adds those same fp16 values in fp32, so out = sum p v / sum p holds for the values
+ *    used. The reference max a row subtracts moves only when a score beats it by more
+ *    than 2^8 (in base-2 units), so p <= 2^8 and the accumulator is rescaled rarely;
+ *    the result is unchanged up to rounding.
+ * With several partitions each writes fp32 partial results (o, m, l) that a second
+ * kernel merges by log-sum-exp. */
 #define PA_DECODE_KV_STREAM 1u
 pa_status pa_decode(void* out, const void* q, const void* kv_pool, const int32_t* block_tables,
                     const int32_t* context_lens, int32_t num_seqs, int32_t num_q_heads,
@@ -198,7 +223,9 @@ pa_status pa_decode(void* out, const void* q, const void* kv_pool, const int32_t
  *   workspace       pa_decode_shared_prefix_workspace_bytes(...) bytes, 256-byte aligned
  * Other arguments as pa_decode (fp16 pool; K/V loads keep the cache hint, since blocks are
  * shared). A row whose group, prefix or length breaks these bounds is NaN; a length of 0
- * gives zeros. */
+ * gives zeros. Arithmetic as pa_decode's grouped-query path for every group size (the
+ * tiles run on the matrix cores with p rounded to fp16, the reference max lagging by
+ * up to 2^8), the prefix and own-token passes merged by log-sum-exp in fp32. */
 pa_status pa_decode_shared_prefix(void* out, const void* q, const void* kv_pool,
                                   const int32_t* block_tables, const int32_t* context_lens,
                                   int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
@@ -287,8 +314,12 @@ pa_status pa_decode_shared_prefix_fp8(void* out, const void* q, const void* kv_p
  *                    second kernel (the same split-context merge as decode), so that few
  *                    or uneven requests still fill the GPU. Fewer bytes than needed:
  *                    PA_ERR_WORKSPACE.
- * Arithmetic: fp16 inputs on the matrix cores with fp32 accumulation, fp32 softmax,
- * fp16 output rounded to nearest even. */
+ *   scale            finite and > 0 (PA_ERR_INVALID otherwise)
+ * Arithmetic: fp16 inputs on the matrix cores with fp32 accumulation; fp32 online
+ * softmax whose probabilities p are rounded to fp16 (nearest even) for the P.V product,
+ * with the row sum l taken over those same fp16 values in fp32; the reference max of a
+ * row moves only when a score beats it by more than 2^8 (base-2 units); fp16 output
+ * rounded to nearest even. A split context merges fp32 partials by log-sum-exp. */
 pa_status pa_prefill_chunk(void* out, const void* q, const void* kv_pool,
                            const int32_t* block_tables, const int32_t* query_start_loc,
                            const int32_t* seq_lens, int32_t num_reqs, int32_t total_q,
@@ -306,7 +337,10 @@ int64_t pa_prefill_workspace_bytes(int32_t num_reqs, int32_t num_q_heads, int32_
                                    int32_t max_seq_len, int32_t head_size);
 
 /* Copy one sequence's keys and values, in logical order, out of the pool: the
- * block-table indexing of the attention kernels, made visible bit for bit.
+ * block-table indexing of the attention kernels, made visible bit for bit. Logical
+ * position t is read from slot block_table_row[t / block_size] * block_size +
+ * t % block_size (page "vLLM GitHub 项目 …", section 二, item 1; the block-table
+ * figure in section "PagedAttention 原理" of page "vLLM 部署深度指南").
  *
  *   k_out, v_out     device fp16 [len][num_kv_heads][head_size], written
  *   block_table_row  device int32 [ceil(len / block_size)]; an entry outside
@@ -338,10 +372,15 @@ int64_t pa_stream_read_sink_len(int64_t bytes);
  * page "vLLM 部署深度指南"). dst, src and pairs may each be device memory or pinned host
  * memory (hipHostMalloc; the kernel reads and writes it over the host link); any other
  * host memory is refused with PA_ERR_INVALID before a launch. Same rules on pairs.
+ * pa_copy_blocks_fp8: pa_copy_blocks over an E4M3 pool (one byte per element, the
+ * layout of the FP8 section above): copy-on-write for a --kv-cache-dtype fp8 cache.
  * Both are asynchronous on `stream`. */
 pa_status pa_copy_blocks(void* kv_pool, const int64_t* pairs, int32_t num_pairs,
                          int32_t block_size, int32_t num_kv_heads, int32_t head_size,
                          int64_t num_blocks, void* stream);
+pa_status pa_copy_blocks_fp8(void* kv_pool, const int64_t* pairs, int32_t num_pairs,
+                             int32_t block_size, int32_t num_kv_heads, int32_t head_size,
+                             int64_t num_blocks, void* stream);
 pa_status pa_move_blocks(void* dst, const void* src, const int64_t* pairs, int32_t num_pairs,
                          int64_t block_bytes, int64_t dst_blocks, int64_t src_blocks,
                          void* stream);

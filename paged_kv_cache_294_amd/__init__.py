@@ -19,6 +19,7 @@ from ._lib import (  # noqa: F401
     pa_abi_version,
     pa_block_bytes,
     pa_copy_blocks,
+    pa_copy_blocks_fp8,
     pa_blocks_for_len,
     pa_decode,
     pa_decode_fp8,

@@ -63,6 +63,7 @@ SIGNATURES = {
     "pa_stream_read": (ctypes.c_int, [_vp, _i64, _vp, _vp]),
     "pa_stream_read_sink_len": (_i64, [_i64]),
     "pa_copy_blocks": (ctypes.c_int, [_vp, _vp, _i32, _i32, _i32, _i32, _i64, _vp]),
+    "pa_copy_blocks_fp8": (ctypes.c_int, [_vp, _vp, _i32, _i32, _i32, _i32, _i64, _vp]),
     "pa_move_blocks": (ctypes.c_int, [_vp, _vp, _vp, _i32, _i64, _i64, _i64, _vp]),
     "pa_graph_begin": (ctypes.c_int, [_vp]),
     "pa_graph_end": (ctypes.c_int, [_vp, ctypes.POINTER(_vp)]),
@@ -127,6 +128,22 @@ def _stream(stream):
     if isinstance(stream, int):
         return stream
     return stream.cuda_stream
+
+
+def _own_workspace(nbytes, device, stream):
+    """A workspace the binding allocates for one call.
+
+    It comes from torch's caching allocator on the current stream and is freed when the
+    call returns. When the call's kernels run on another stream (``stream`` a torch stream
+    or a raw handle), the tensor is recorded on that stream, so the allocator does not
+    hand its memory to a later allocation until the kernels queued there have finished.
+    """
+    ws = torch.empty(nbytes, dtype=torch.uint8, device=device)
+    if stream is not None:
+        s = torch.cuda.ExternalStream(stream, device=device) if isinstance(stream, int) else stream
+        if s.cuda_stream != torch.cuda.current_stream(device).cuda_stream:
+            ws.record_stream(s)
+    return ws
 
 
 def _dev(t, name, dtype):
@@ -237,7 +254,7 @@ def pa_kv_append_fp8(kv_pool, key, value, slot_mapping, k_scale=1.0, v_scale=1.0
 
 
 def _decode_args(out, q, kv_pool, block_tables, context_lens, max_context_len, scale,
-                 partition_size, workspace, pool_dtype):
+                 partition_size, workspace, pool_dtype, stream):
     nb, bs, hkv, d = _pool_geometry(kv_pool)
     B, hq, dq = q.shape
     if dq != d or tuple(out.shape) != (B, hq, d):
@@ -258,7 +275,7 @@ def _decode_args(out, q, kv_pool, block_tables, context_lens, max_context_len, s
             # a buffer allocated here would be freed after the call while the graph
             # keeps writing it on every replay
             raise ValueError("pa_decode under capture needs a caller-owned workspace")
-        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+        workspace = _own_workspace(need, q.device, stream)
     ws_p, ws_n = (0, 0) if workspace is None else (_dense(workspace, "workspace", torch.uint8),
                                                     workspace.numel())
     head = (_dense(out, "out", torch.float16), _dense(q, "q", torch.float16),
@@ -275,12 +292,14 @@ def pa_decode(out, q, kv_pool, block_tables, context_lens, max_context_len, scal
     ``max_context_len`` is a host upper bound of context_lens. ``partition_size`` None:
     :func:`pa_decode_default_partition_size`. ``workspace`` is a device uint8 tensor of at
     least :func:`pa_decode_workspace_bytes` bytes; one is allocated here when it is None
-    (with one partition it is optional and only orders the work). ``flags``: 0 or
+    (with one partition it is optional and only orders the work), on the current stream
+    and recorded on ``stream`` when the call runs elsewhere. A caller-owned workspace must
+    stay untouched until the call's kernels on ``stream`` are done. ``flags``: 0 or
     ``PA_DECODE_KV_STREAM`` (no block is shared between the sequences of the call: K/V
     loads bypass cache retention and the longest partitions are scheduled first).
     """
     head, tail, ws = _decode_args(out, q, kv_pool, block_tables, context_lens, max_context_len,
-                                  scale, partition_size, workspace, torch.float16)
+                                  scale, partition_size, workspace, torch.float16, stream)
     st = load().pa_decode(*head, *tail, int(flags), _stream(stream))
     _check("pa_decode", st)
 
@@ -293,7 +312,7 @@ def pa_decode_shared_prefix_workspace_bytes(num_seqs, num_q_heads, max_context_l
 
 def _shared_prefix_args(out, q, kv_pool, block_tables, context_lens, max_context_len,
                         group_start, prefix_lens, max_group_size, max_prefix_len, scale,
-                        partition_size, workspace, pool_dtype):
+                        partition_size, workspace, pool_dtype, stream):
     nb, bs, hkv, d = _pool_geometry(kv_pool)
     B, hq, dq = q.shape
     if dq != d or tuple(out.shape) != (B, hq, d):
@@ -312,7 +331,7 @@ def _shared_prefix_args(out, q, kv_pool, block_tables, context_lens, max_context
     if workspace is None:
         if _CAPTURING:
             raise ValueError("pa_decode_shared_prefix under capture needs a caller-owned workspace")
-        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
+        workspace = _own_workspace(max(need, 256), q.device, stream)
     head = (_dense(out, "out", torch.float16), _dense(q, "q", torch.float16),
             _dense(kv_pool, "kv_pool", pool_dtype), _dense(block_tables, "block_tables", torch.int32),
             _dense(context_lens, "context_lens", torch.int32), B, hq, hkv, d, bs,
@@ -332,7 +351,7 @@ def pa_decode_shared_prefix(out, q, kv_pool, block_tables, context_lens, max_con
     head, tail, ws = _shared_prefix_args(out, q, kv_pool, block_tables, context_lens,
                                          max_context_len, group_start, prefix_lens,
                                          max_group_size, max_prefix_len, scale, partition_size,
-                                         workspace, torch.float16)
+                                         workspace, torch.float16, stream)
     st = load().pa_decode_shared_prefix(*head, *tail, _stream(stream))
     _check("pa_decode_shared_prefix", st)
 
@@ -346,7 +365,7 @@ def pa_decode_shared_prefix_fp8(out, q, kv_pool, block_tables, context_lens, max
     head, tail, ws = _shared_prefix_args(out, q, kv_pool, block_tables, context_lens,
                                          max_context_len, group_start, prefix_lens,
                                          max_group_size, max_prefix_len, scale, partition_size,
-                                         workspace, torch.uint8)
+                                         workspace, torch.uint8, stream)
     st = load().pa_decode_shared_prefix_fp8(*head, float(k_scale), float(v_scale), *tail,
                                             _stream(stream))
     _check("pa_decode_shared_prefix_fp8", st)
@@ -357,7 +376,7 @@ def pa_decode_fp8(out, q, kv_pool, block_tables, context_lens, max_context_len, 
                   stream=None):
     """pa_decode over an FP8 (E4M3) pool held as a uint8 tensor, with its per-tensor scales."""
     head, tail, ws = _decode_args(out, q, kv_pool, block_tables, context_lens, max_context_len,
-                                  scale, partition_size, workspace, torch.uint8)
+                                  scale, partition_size, workspace, torch.uint8, stream)
     st = load().pa_decode_fp8(*head, float(k_scale), float(v_scale), *tail, int(flags),
                               _stream(stream))
     _check("pa_decode_fp8", st)
@@ -387,10 +406,11 @@ def pa_prefill_workspace_bytes(num_reqs, num_q_heads, max_q_len, max_seq_len, he
                                              int(max_seq_len), int(head_size))
 
 
-def _prefill_workspace(args, workspace, split, device):
+def _prefill_workspace(args, workspace, split, device, stream=None):
     """(pointer, bytes) of the workspace for a prefill call: none when split is off or no
     split helps; one the caller gave; else a new one (not under graph capture, where the
-    call then runs unsplit)."""
+    call then runs unsplit), recorded on the call's stream when that is not the current
+    one."""
     if not split:
         return 0, 0
     R, hq, mq, ms, d = args[6], args[10], args[8], args[9], args[12]
@@ -402,7 +422,7 @@ def _prefill_workspace(args, workspace, split, device):
     if workspace is None:
         if _CAPTURING:
             return 0, 0
-        workspace = torch.empty(need, dtype=torch.uint8, device=device)
+        workspace = _own_workspace(need, device, stream)
     return _dense(workspace, "workspace", torch.uint8), workspace.numel()
 
 
@@ -413,7 +433,7 @@ def pa_prefill_chunk(out, q, kv_pool, block_tables, query_start_loc, seq_lens, m
     `workspace`, a uint8 tensor of pa_prefill_workspace_bytes bytes, allocated if None)."""
     args = _prefill_args(out, q, kv_pool, block_tables, query_start_loc, seq_lens, max_q_len,
                          max_seq_len, scale, torch.float16)
-    ws = _prefill_workspace(args, workspace, split, q.device)
+    ws = _prefill_workspace(args, workspace, split, q.device, stream)
     st = load().pa_prefill_chunk(*args, *ws, _stream(stream))
     _check("pa_prefill_chunk", st)
 
@@ -424,7 +444,7 @@ def pa_prefill_chunk_fp8(out, q, kv_pool, block_tables, query_start_loc, seq_len
     """pa_prefill_chunk over an FP8 (E4M3) pool held as a uint8 tensor, with its scales."""
     args = _prefill_args(out, q, kv_pool, block_tables, query_start_loc, seq_lens, max_q_len,
                          max_seq_len, scale, torch.uint8)
-    ws = _prefill_workspace(args, workspace, split, q.device)
+    ws = _prefill_workspace(args, workspace, split, q.device, stream)
     st = load().pa_prefill_chunk_fp8(*args, float(k_scale), float(v_scale), *ws, _stream(stream))
     _check("pa_prefill_chunk_fp8", st)
 
@@ -454,12 +474,24 @@ def _pairs(pairs):
 
 
 def pa_copy_blocks(kv_pool, pairs, stream=None):
-    """Copy-on-write copies inside the pool: block pairs[k, 1] = block pairs[k, 0]."""
+    """Copy-on-write copies inside the pool: block pairs[k, 1] = block pairs[k, 0]. An fp16
+    pool goes to pa_copy_blocks, an FP8 (E4M3) pool held as uint8 to pa_copy_blocks_fp8."""
+    if kv_pool.dtype == torch.uint8:
+        return pa_copy_blocks_fp8(kv_pool, pairs, stream)
     nb, bs, hkv, d = _pool_geometry(kv_pool)
     pp, n = _pairs(pairs)
     st = load().pa_copy_blocks(_dense(kv_pool, "kv_pool", torch.float16), pp, n, bs, hkv, d, nb,
                                _stream(stream))
     _check("pa_copy_blocks", st)
+
+
+def pa_copy_blocks_fp8(kv_pool, pairs, stream=None):
+    """pa_copy_blocks over an FP8 (E4M3) pool held as a uint8 tensor."""
+    nb, bs, hkv, d = _pool_geometry(kv_pool)
+    pp, n = _pairs(pairs)
+    st = load().pa_copy_blocks_fp8(_dense(kv_pool, "kv_pool", torch.uint8), pp, n, bs, hkv, d, nb,
+                                   _stream(stream))
+    _check("pa_copy_blocks_fp8", st)
 
 
 def pa_move_blocks(dst, src, pairs, stream=None):

@@ -32,9 +32,10 @@ HIPCC_FLAGS = [
     "-Wno-unused-result",
     # no packed-fp32 instructions in generated code
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-    # matrix-core results in ordinary VGPRs rather than accumulation registers: the
+    # matrix-core results in ordinary VGPRs rather than accumulation registers: the fp16
     # grouped-query decode kernel then needs 155 registers instead of 155 + 32 (three
-    # waves per SIMD instead of two)
+    # waves per SIMD instead of two); its FP8 variant, which keeps the loaded codes packed,
+    # needs 117-120 (four waves per SIMD)
     "-mllvm", "-amdgpu-mfma-vgpr-form",
 ]
 

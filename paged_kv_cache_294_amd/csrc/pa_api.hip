@@ -248,7 +248,9 @@ pa_status decode_impl(void* out, const void* q, const void* kv_pool, const int32
   if (pa_status s = check_geometry(block_size, num_kv_heads, head_size)) return s;
   if (pa_status s = check_heads(num_q_heads, num_kv_heads)) return s;
   if (partition_size <= 0 || partition_size % block_size) return PA_ERR_INVALID;
-  if (!std::isfinite(scale)) return PA_ERR_INVALID;
+  // the matrix-core kernels mask scores with -inf and track the running max in scaled
+  // units, which holds only for a positive scale
+  if (!std::isfinite(scale) || !(scale > 0.0f)) return PA_ERR_INVALID;
   if (flags & ~PA_DECODE_KV_STREAM) return PA_ERR_INVALID;
   if (num_seqs > 65535) return PA_ERR_UNSUPPORTED;
   if ((int64_t)max_blocks_per_seq * block_size > INT32_MAX) return PA_ERR_INVALID;
@@ -391,7 +393,7 @@ pa_status prefill_impl(void* out, const void* q, const void* kv_pool, const int3
     return PA_ERR_INVALID;
   if (pa_status s = check_geometry(block_size, num_kv_heads, head_size)) return s;
   if (pa_status s = check_heads(num_q_heads, num_kv_heads)) return s;
-  if (!std::isfinite(scale)) return PA_ERR_INVALID;
+  if (!std::isfinite(scale) || !(scale > 0.0f)) return PA_ERR_INVALID;
   if (max_q_len > max_seq_len) return PA_ERR_INVALID;
   if ((int64_t)max_blocks_per_seq * block_size > INT32_MAX) return PA_ERR_INVALID;
   if ((int64_t)block_size * 2 * num_kv_heads * head_size > INT32_MAX) return PA_ERR_UNSUPPORTED;
@@ -547,15 +549,35 @@ PA_EXPORT pa_status pa_move_blocks(void* dst, const void* src, const int64_t* pa
                                             static_cast<hipStream_t>(stream)));
 }
 
-PA_EXPORT pa_status pa_copy_blocks(void* kv_pool, const int64_t* pairs, int32_t num_pairs,
-                                   int32_t block_size, int32_t num_kv_heads, int32_t head_size,
-                                   int64_t num_blocks, void* stream) {
+namespace {
+
+// Copy-on-write copies inside a pool whose elements take elem_bytes bytes (2: fp16,
+// 1: E4M3 codes); a block is block_size * 2 * num_kv_heads * head_size elements.
+pa_status copy_blocks_impl(void* kv_pool, const int64_t* pairs, int32_t num_pairs,
+                           int32_t block_size, int32_t num_kv_heads, int32_t head_size,
+                           int64_t num_blocks, int64_t elem_bytes, void* stream) {
   pa_status st = check_geometry(block_size, num_kv_heads, head_size);
   if (st != PA_OK) return st;
   if (num_blocks <= 0) return PA_ERR_INVALID;
-  const int64_t block_bytes = (int64_t)block_size * 2 * num_kv_heads * head_size * 2;
+  const int64_t block_bytes = (int64_t)block_size * 2 * num_kv_heads * head_size * elem_bytes;
   return pa_move_blocks(kv_pool, kv_pool, pairs, num_pairs, block_bytes, num_blocks, num_blocks,
                         stream);
+}
+
+}  // namespace
+
+PA_EXPORT pa_status pa_copy_blocks(void* kv_pool, const int64_t* pairs, int32_t num_pairs,
+                                   int32_t block_size, int32_t num_kv_heads, int32_t head_size,
+                                   int64_t num_blocks, void* stream) {
+  return copy_blocks_impl(kv_pool, pairs, num_pairs, block_size, num_kv_heads, head_size,
+                          num_blocks, 2, stream);
+}
+
+PA_EXPORT pa_status pa_copy_blocks_fp8(void* kv_pool, const int64_t* pairs, int32_t num_pairs,
+                                       int32_t block_size, int32_t num_kv_heads,
+                                       int32_t head_size, int64_t num_blocks, void* stream) {
+  return copy_blocks_impl(kv_pool, pairs, num_pairs, block_size, num_kv_heads, head_size,
+                          num_blocks, 1, stream);
 }
 
 // ---------------------------------------------------------------------------------------

@@ -135,6 +135,8 @@ def decode_call(lib, **kw):
     (dict(ps=0), pkv.PA_ERR_INVALID),
     (dict(maxlen=2048), pkv.PA_ERR_WORKSPACE),
     (dict(scale=float("nan")), pkv.PA_ERR_INVALID),
+    (dict(scale=0.0), pkv.PA_ERR_INVALID),
+    (dict(scale=-0.125), pkv.PA_ERR_INVALID),
     (dict(B=-1), pkv.PA_ERR_INVALID),
     (dict(nb=0), pkv.PA_ERR_INVALID),
     (dict(flags=2), pkv.PA_ERR_INVALID),
@@ -168,6 +170,9 @@ def test_prefill_rejects(lib):
     assert call(a12=80) == pkv.PA_ERR_UNSUPPORTED        # head size
     assert call(a0=0) == pkv.PA_ERR_INVALID              # null out
     assert call(a8=65) == pkv.PA_ERR_INVALID             # max_q_len > max_seq_len
+    assert call(a16=0.0) == pkv.PA_ERR_INVALID           # scale must be > 0
+    assert call(a16=-0.125) == pkv.PA_ERR_INVALID
+    assert call(a16=float("inf")) == pkv.PA_ERR_INVALID
     assert call(a6=0) == pkv.PA_OK                       # no requests
     assert call(a17=FAKE, a18=-1) == pkv.PA_ERR_INVALID  # negative workspace size
     assert call(a17=FAKE + 8, a18=1 << 20) == pkv.PA_ERR_INVALID  # workspace not 16-byte aligned
@@ -207,6 +212,10 @@ def test_block_copies_reject_before_any_launch(lib):
     assert lib.pa_copy_blocks(FAKE, FAKE, 1, 16, 4, 80, 16, None) == pkv.PA_ERR_UNSUPPORTED
     assert lib.pa_copy_blocks(FAKE, FAKE, 1, 16, 4, 64, 0, None) == pkv.PA_ERR_INVALID
     assert lib.pa_copy_blocks(FAKE, FAKE, 0, 16, 4, 64, 16, None) == pkv.PA_OK
+    assert lib.pa_copy_blocks_fp8(FAKE, FAKE, 1, 32, 4, 64, 16, None) == pkv.PA_ERR_UNSUPPORTED
+    assert lib.pa_copy_blocks_fp8(FAKE, FAKE, 1, 16, 4, 64, 0, None) == pkv.PA_ERR_INVALID
+    assert lib.pa_copy_blocks_fp8(FAKE, FAKE, -1, 16, 4, 64, 16, None) == pkv.PA_ERR_INVALID
+    assert lib.pa_copy_blocks_fp8(FAKE, FAKE, 0, 16, 4, 64, 16, None) == pkv.PA_OK
     assert lib.pa_move_blocks(FAKE, FAKE, FAKE, 1, 100, 4, 4, None) == pkv.PA_ERR_INVALID  # % 16
     assert lib.pa_move_blocks(FAKE, FAKE, FAKE, -1, 256, 4, 4, None) == pkv.PA_ERR_INVALID
     assert lib.pa_move_blocks(0, FAKE, FAKE, 1, 256, 4, 4, None) == pkv.PA_ERR_INVALID

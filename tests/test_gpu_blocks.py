@@ -9,6 +9,7 @@ import pytest
 import torch
 
 import oracle
+from oracle import fp8
 import paged_kv_cache_294_amd as pkv
 from gpu_util import check_attention, dev, host, note
 
@@ -116,3 +117,58 @@ def test_copy_on_write_step_end_to_end():
     pkv.pa_decode(out, dev(q), pd, dev(tables), dev(lens), 21, 1 / 8)
     assert np.array_equal(bits(host(pd)[:3]), bits(want_pool[:3]))
     check_attention(host(out), want, "copy-on-write decode")
+
+
+def test_copy_blocks_fp8_bit_exact():
+    nb, hkv, d = 300, 8, 128
+    rng = np.random.default_rng(12)
+    pool = rng.integers(0, 256, (nb, 16, 2, hkv, d)).astype(np.uint8)
+    perm = rng.permutation(nb)
+    pairs = np.stack([perm[:40], perm[40:80]], 1).astype(np.int64)
+    skip = np.array([[-1, perm[-1]], [perm[-2], nb]], dtype=np.int64)
+    pd = dev(pool)
+    note("copy_blocks fp8 (E4M3 pool, 40 pairs + 2 skipped)")
+    pkv.pa_copy_blocks(pd, dev(np.concatenate([pairs, skip])))  # uint8 pool -> pa_copy_blocks_fp8
+    assert np.array_equal(host(pd), oracle.copy_blocks(pool, pairs))
+
+
+def test_copy_on_write_step_fp8_end_to_end():
+    """The copy-on-write step of an E4M3 cache: block manager -> pa_copy_blocks_fp8 ->
+    pa_kv_append_fp8 -> pa_decode_fp8, against the oracle's copies, its quantizing append
+    and its decode over the dequantized pool. Two samples share a 40-token prompt (blocks
+    0..2, the last one partly filled); both append a token. Sample 0 appends first, while
+    block 2 is still shared, so its token goes into a copy (block 3); sample 1 then holds
+    block 2 alone and writes into it."""
+    hkv, hq, d = 4, 16, 128
+    nb, ks, vs = 8, 0.04, 0.03
+    rng = np.random.default_rng(13)
+    prompt_k = rng.standard_normal((40, hkv, d)).astype(np.float16)
+    prompt_v = rng.standard_normal((40, hkv, d)).astype(np.float16)
+    new_k = rng.standard_normal((2, hkv, d)).astype(np.float16)
+    new_v = rng.standard_normal((2, hkv, d)).astype(np.float16)
+    q = rng.standard_normal((2, hq, d)).astype(np.float16)
+    pool = np.full((nb, 16, 2, hkv, d), 0x7F, np.uint8)  # E4M3 NaN everywhere
+
+    m = pkv.BlockManager(nb)
+    m.allocate(0, 0)
+    slots0, _ = m.append_slots(np.zeros(40, np.int64))
+    m.fork(0, 1)
+    slots, copies = m.append_slots(np.array([0, 1], np.int64))
+    assert copies.tolist() == [[2, 3]] and slots.tolist() == [3 * 16 + 8, 2 * 16 + 8]
+    tables, lens = m.block_tables(np.array([0, 1], np.int64), 3, pad=0)
+    assert tables.tolist() == [[0, 1, 3], [0, 1, 2]] and lens.tolist() == [41, 41]
+
+    want_pool = fp8.kv_append_fp8(pool, prompt_k, prompt_v, slots0, ks, vs)
+    want_pool = oracle.copy_blocks(want_pool, copies)
+    want_pool = fp8.kv_append_fp8(want_pool, new_k, new_v, slots, ks, vs)
+    want = oracle.decode(q, fp8.dequantize_pool(want_pool, ks, vs), tables, lens, 1 / np.sqrt(d))
+
+    note("copy-on-write step on an E4M3 pool")
+    pd = dev(pool)
+    pkv.pa_kv_append_fp8(pd, dev(prompt_k), dev(prompt_v), dev(slots0), ks, vs)
+    pkv.pa_copy_blocks_fp8(pd, dev(copies))
+    pkv.pa_kv_append_fp8(pd, dev(new_k), dev(new_v), dev(slots), ks, vs)
+    out = torch.empty(2, hq, d, dtype=torch.float16, device="cuda")
+    pkv.pa_decode_fp8(out, dev(q), pd, dev(tables), dev(lens), 41, 1 / np.sqrt(d), ks, vs)
+    assert np.array_equal(host(pd), want_pool)
+    check_attention(host(out), want, "copy-on-write decode fp8")

@@ -10,7 +10,8 @@ import torch
 import oracle
 import paged_kv_cache_294_amd as pkv
 import workloads
-from gpu_util import bits, check_attention, dev, host, note
+from gpu_util import (bits, check_attention, dev, host, note, tie_base, tie_expectations,
+                      write_tie_values)
 
 pytestmark = pytest.mark.gpu
 
@@ -181,6 +182,65 @@ def test_decode_small(D, G, ps):
     check_attention(got, oracle_decode(inp), f"D{D} G{G} ps{ps}")
 
 
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("G", [1, 2, 4, 8])
+def test_decode_past_64_blocks_per_partition(D, G):
+    """Partitions of 128 and 256 blocks: each wave reloads its vector of table entries
+    every 64 blocks. One partition per sequence (ps 4096) and 2048-token partitions."""
+    lens = [1100, 1500, 2100, 17, 1024, 1025, 4096, 3000]
+    hkv = 4 if G < 8 else 2
+    inp = workloads.decode_case(70 + D + G, lens, hkv * G, hkv, D)
+    ref = oracle_decode(inp)
+    d = Dev(inp)
+    for ps in (2048, 4096):
+        for flags in (0, pkv.PA_DECODE_KV_STREAM):
+            note(f"decode past 64 blocks D={D} G={G} ps={ps} flags={flags}")
+            check_attention(d.decode(partition_size=ps, flags=flags), ref,
+                            f"D{D} G{G} ps{ps} flags{flags}")
+
+
+@pytest.mark.parametrize("G,D,n,ps", [(1, 128, 2, 512), (1, 64, 2, 512), (1, 128, 32, 16),
+                                      (2, 64, 32, 16), (4, 128, 2, 512), (4, 128, 32, 16),
+                                      (8, 128, 2, 512)])
+def test_output_store_rounds_to_nearest_even(G, D, n, ps):
+    """With q = 0 every weight is 1, so a row is the exact mean of its value rows, built
+    here to lie exactly halfway between two fp16 numbers (n = 2 tokens, or 32 tokens over
+    two 16-token partitions merged by the reduce kernel). The fp16 store must give the
+    neighbour with the even last bit: truncation and rounding half away from zero each
+    give a different result on some of these elements."""
+    hkv = 2
+    inp = workloads.decode_case(60 + G + D + n, [n] * 3, hkv * G, hkv, D, append=False)
+    x, u = tie_base(np.random.default_rng(61 + G + n), (hkv, D))
+    pool = inp.pool.copy()
+    for b in range(3):
+        write_tie_values(pool, inp.block_tables[b], n, x, u)
+    case = dataclasses.replace(inp, pool=pool, q=np.zeros_like(inp.q))
+    note(f"fp16 store rounding G={G} D={D} tokens={n} ps={ps}")
+    got = Dev(case, append=False).decode(partition_size=ps)
+    rne, toward0, away = tie_expectations(x, u)
+    want = rne[np.arange(hkv * G) // G]  # query head h reads KV head h // G
+    for b in range(3):
+        assert np.array_equal(bits(got[b]), bits(want)), b
+    assert (bits(rne) != bits(toward0)).any() and (bits(rne) != bits(away)).any()
+
+
+def test_decode_on_a_side_stream():
+    """The call's kernels on a stream other than the current one, with the workspace
+    the binding allocates (recorded on that stream)."""
+    inp = workloads.decode_case(48, [700, 1300, 2000, 33], 8, 8, 128)
+    d = Dev(inp)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    q = d.q
+    out = torch.empty_like(q)
+    pkv.pa_decode(out, q, d.pool, d.bt, d.lens, 2000, inp.scale, 256, stream=side)
+    # another allocation on the current stream while the call may still run on `side`
+    scratch = torch.full((1 << 20,), 7, dtype=torch.uint8, device="cuda")
+    torch.cuda.current_stream().wait_stream(side)
+    check_attention(host(out), oracle_decode(inp), "side stream")
+    del scratch
+
+
 def test_decode_length_one_rows_are_exact():
     inp = workloads.decode_case(41, [1] * 8, 16, 4, 128)
     got = Dev(inp).decode()
@@ -213,19 +273,23 @@ def test_decode_decode256_full():
     assert np.array_equal(bits(got), bits(streamed))
 
 
-def test_decode_long32k_sampled():
+def test_decode_long32k_full():
+    """All 8 x 32 rows of the long-context workload, at the 512-token partitions it is
+    specified with (64 partitions per sequence, merged by the reduce kernel) and at 2048
+    tokens (16 partitions, the library's default size for it)."""
     inp = cfg("long32k")
-    d = Dev(inp)
-    outs = {ps: d.decode(partition_size=ps, flags=pkv.PA_DECODE_KV_STREAM) for ps in (512, 2048)}
+    assert len(inp.slot_mapping) == 0  # cache pre-filled, nothing appended
+    d = Dev(inp, append=False)
+    sizes = (512, 2048)
+    outs = {ps: d.decode(partition_size=ps, flags=pkv.PA_DECODE_KV_STREAM) for ps in sizes}
     del d
     free()
-    rng = np.random.default_rng(0)
-    pairs = [(b, int(h)) for b in range(8) for h in rng.choice(32, 4, replace=False)]
-    ref = oracle.decode_rows(inp.q, inp.pool, inp.block_tables, inp.seq_lens, inp.scale, pairs)
+    note("oracle decode of long32k (8 x 32768 tokens x 32 heads)")
+    ref = oracle.decode(inp.q, inp.pool, inp.block_tables, inp.seq_lens, inp.scale)
     for ps, got in outs.items():
-        rows = np.stack([got[b, h] for b, h in pairs])
-        check_attention(rows, ref, f"long32k ps{ps}")
-    assert np.abs(outs[512].astype(np.float64) - outs[2048].astype(np.float64)).max() <= 1e-4
+        check_attention(got, ref, f"long32k ps{ps}")
+    for ps in sizes:
+        assert np.abs(outs[ps].astype(np.float64) - outs[512].astype(np.float64)).max() <= 1e-4
 
 
 def test_decode_prefix_groups_full_and_shared_equals_private():

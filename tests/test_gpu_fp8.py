@@ -127,6 +127,53 @@ def test_decode_fp8_decode256_sampled():
         check_attention(host(out)[rows], want, f"fp8 decode256 ps{ps}")
 
 
+def test_decode_fp8_prefix_private_as_bench_sampled():
+    """The 64 x 4 prompt-group batch with private copies of the prompt blocks on an E4M3
+    pool, in bench.py's launch: the library's default partition size (one partition of up
+    to 80 blocks, so each wave reloads its vector of table entries past block 64), no block
+    shared, longest first. 24 sequences sampled, all 32 query heads."""
+    inp = workloads.unshare_prefix(workloads.shared_prompt_groups())
+    q, bt, lens = inp.decode_part()
+    rows = np.sort(np.random.default_rng(3).choice(len(lens), 24, replace=False))
+    rows[0] = int(np.argmax(lens))  # the longest context is among them
+    rows = np.unique(rows)
+    ks, vs = 0.05, 0.04
+    pool = quantized_pool(inp, ks, vs, seqs=rows)
+    ps = pkv.pa_decode_default_partition_size(len(lens), 32, 8, int(lens.max()))
+    assert ps >= int(lens.max()) and int(lens.max()) > 64 * 16
+    want = oracle_decode_fp8(inp, pool, ks, vs, rows)
+    out = torch.empty(q.shape, dtype=torch.float16, device="cuda")
+    ws = torch.empty(pkv.pa_decode_workspace_bytes(len(lens), 32, int(lens.max()), ps, 128),
+                     dtype=torch.uint8, device="cuda")
+    note(f"decode fp8 prefix-private, {len(rows)} sampled sequences, partitions of {ps}")
+    pkv.pa_decode_fp8(out, dev(q), dev(pool), dev(bt), dev(lens), int(lens.max()), inp.scale,
+                      ks, vs, ps, ws, pkv.PA_DECODE_KV_STREAM)
+    check_attention(host(out)[rows], want, f"fp8 prefix-private ps{ps}")
+
+
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("G", [1, 2, 4, 8])
+def test_decode_fp8_past_64_blocks_per_partition(D, G):
+    """FP8 decode with partitions of 128 and 256 blocks (table-entry vector reloaded every
+    64 blocks), with and without the streaming flag."""
+    hkv = 4 if G < 8 else 2
+    inp = workloads.decode_case(100 + D + G, [1100, 1500, 2100, 17, 1025, 4096, 3000],
+                                hkv * G, hkv, D, append=False)
+    ks, vs = 0.03, 0.02
+    pool = quantized_pool(inp, ks, vs)
+    q, bt, lens = inp.decode_part()
+    want = oracle_decode_fp8(inp, pool, ks, vs)
+    for ps in (2048, 4096):
+        for flags in (0, pkv.PA_DECODE_KV_STREAM):
+            out = torch.empty(q.shape, dtype=torch.float16, device="cuda")
+            ws = torch.empty(pkv.pa_decode_workspace_bytes(len(lens), hkv * G, int(lens.max()), ps, D),
+                             dtype=torch.uint8, device="cuda")
+            note(f"decode fp8 past 64 blocks D={D} G={G} ps={ps} flags={flags}")
+            pkv.pa_decode_fp8(out, dev(q), dev(pool), dev(bt), dev(lens), int(lens.max()),
+                              inp.scale, ks, vs, ps, ws, flags)
+            check_attention(host(out), want, f"fp8 D{D} G{G} ps{ps} flags{flags}")
+
+
 def test_decode_fp8_bad_rows_are_nan():
     inp = workloads.decode_case(96, [40, 50, 60], 4, 4, 64, append=False)
     pool = quantized_pool(inp, 1.0, 1.0)

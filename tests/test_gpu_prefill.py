@@ -9,7 +9,8 @@ import torch
 import oracle
 import paged_kv_cache_294_amd as pkv
 import workloads
-from gpu_util import check_attention, dev, host, note
+from gpu_util import (bits, check_attention, dev, host, note, tie_base, tie_expectations,
+                      write_tie_values)
 
 pytestmark = pytest.mark.gpu
 
@@ -273,3 +274,29 @@ def test_prefill_2048_row_chunk():
     got, _ = gpu_prefill(inp)
     rows = np.concatenate([np.arange(0, 2088, 29), [127, 128, 1023, 1024, 2047, 2048, 2087]])
     check_attention(got[rows], oracle_prefill(inp, rows=set(rows.tolist()))[rows], "2048 rows")
+
+
+@pytest.mark.parametrize("G,D", [(1, 128), (4, 128), (1, 64)])
+def test_output_store_rounds_to_nearest_even(G, D):
+    """q = 0 makes a chunk row the exact mean of the value rows it sees. Request 0 (no
+    prior, chunk of 2): row 1 sees 2 tokens; request 1 (31 prior tokens, chunk of 1): its
+    row sees 32. Both means lie halfway between two fp16 numbers, and the store must give
+    the neighbour with the even last bit; row 0 of request 0 sees one token, its value."""
+    hkv = 2
+    inp = workloads.mixed_case(230 + G + D, [0, 31], [2, 1], [], hkv * G, hkv, D)
+    pool = oracle.kv_append(inp.pool, inp.key_new, inp.value_new, inp.slot_mapping)
+    x, u = tie_base(np.random.default_rng(231), (hkv, D))
+    write_tie_values(pool, inp.block_tables[0], 2, x, u)
+    write_tie_values(pool, inp.block_tables[1], 32, x, u)
+    q, bt, qsl, lens = inp.prefill_part()
+    out = torch.empty(q.shape, dtype=torch.float16, device="cuda")
+    note(f"prefill fp16 store rounding G={G} D={D}")
+    pkv.pa_prefill_chunk(out, dev(np.zeros_like(q)), dev(pool), dev(bt), dev(qsl), dev(lens), 2,
+                         32, inp.scale)
+    got = host(out)
+    rne, toward0, away = tie_expectations(x, u)
+    kv = np.arange(hkv * G) // G
+    assert np.array_equal(bits(got[0]), bits((x + u).astype(np.float16)[kv]))
+    assert np.array_equal(bits(got[1]), bits(rne[kv]))
+    assert np.array_equal(bits(got[2]), bits(rne[kv]))
+    assert (bits(rne) != bits(toward0)).any() and (bits(rne) != bits(away)).any()
