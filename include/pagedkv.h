@@ -202,6 +202,28 @@ pa_status pa_decode(void* out, const void* q, const void* kv_pool, const int32_t
                     float scale, int32_t partition_size, void* workspace,
                     int64_t workspace_bytes, uint32_t flags, void* stream);
 
+/* ---- decode that allocates nothing ----------------------------------------------------
+ * For callers that cannot allocate device memory or pass a workspace of their own: code
+ * being captured into a HIP graph, tight serving loops, harnesses that forbid hipMalloc.
+ * pa_decode_noalloc is pa_decode (same arguments without the workspace, same kernels,
+ * bit-identical results) whose workspace is a fixed device array inside the library,
+ * PA_DECODE_NOALLOC_SCRATCH_BYTES bytes, one per GPU, held from the first call on that GPU
+ * until the process ends. It runs on the current device (hipGetDevice), which must be the
+ * device of `stream` and of every buffer. It calls no allocator.
+ *  - A call whose pa_decode_workspace_bytes(...) exceeds the array returns
+ *    PA_ERR_WORKSPACE before any device access (pa_last_error gives the sizes); bad sizes
+ *    return PA_ERR_INVALID.
+ *  - Every call on one GPU uses that GPU's one array, which keeps the last call's
+ *    contents. Nothing in it needs to start at zero. Calls whose work may overlap on one
+ *    GPU (several streams, several threads) race on it: the caller serialises them. */
+#define PA_DECODE_NOALLOC_SCRATCH_BYTES (32ll << 20)
+pa_status pa_decode_noalloc(void* out, const void* q, const void* kv_pool,
+                            const int32_t* block_tables, const int32_t* context_lens,
+                            int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                            int32_t head_size, int32_t block_size, int32_t max_blocks_per_seq,
+                            int64_t num_blocks, int32_t max_context_len, float scale,
+                            int32_t partition_size, uint32_t flags, void* stream);
+
 /* ---- shared-prefix decode ------------------------------------------------------------
  * Sequences that share a prompt point their tables at the same blocks, which avoids
  * storing and computing the prompt twice (page "vLLM GitHub 项目 …", section 二, item 4:

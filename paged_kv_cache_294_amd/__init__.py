@@ -23,6 +23,7 @@ from ._lib import (  # noqa: F401
     pa_blocks_for_len,
     pa_decode,
     pa_decode_fp8,
+    pa_decode_noalloc,
     pa_decode_shared_prefix,
     pa_decode_shared_prefix_fp8,
     pa_decode_shared_prefix_workspace_bytes,
@@ -43,6 +44,7 @@ from ._lib import (  # noqa: F401
     pa_stream_read,
     pa_stream_read_sink_len,
     PA_DECODE_KV_STREAM,
+    PA_DECODE_NOALLOC_SCRATCH_BYTES,
     PA_OK,
     PA_ERR_INVALID,
     PA_ERR_UNSUPPORTED,

@@ -21,6 +21,7 @@ LIB_PATH = os.path.join(_HERE, "libpagedkv.so")
 
 PA_OK, PA_ERR_INVALID, PA_ERR_UNSUPPORTED, PA_ERR_WORKSPACE, PA_ERR_HIP, PA_ERR_EXHAUSTED = range(6)
 PA_DECODE_KV_STREAM = 1
+PA_DECODE_NOALLOC_SCRATCH_BYTES = 32 << 20  # the library's fixed scratch for pa_decode_noalloc
 
 _i32, _i64, _f32, _f64, _vp = ctypes.c_int32, ctypes.c_int64, ctypes.c_float, ctypes.c_double, ctypes.c_void_p
 
@@ -41,6 +42,8 @@ SIGNATURES = {
     "pa_kv_append": (ctypes.c_int, [_vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i64, _i64, _i64, _vp]),
     "pa_decode": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _i64,
                                  _i32, _f32, _i32, _vp, _i64, ctypes.c_uint32, _vp]),
+    "pa_decode_noalloc": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32,
+                                         _i64, _i32, _f32, _i32, ctypes.c_uint32, _vp]),
     "pa_kv_append_fp8": (ctypes.c_int, [_vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i64, _i64, _i64,
                                         _f32, _f32, _vp]),
     "pa_decode_fp8": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32,
@@ -302,6 +305,30 @@ def pa_decode(out, q, kv_pool, block_tables, context_lens, max_context_len, scal
                                   scale, partition_size, workspace, torch.float16, stream)
     st = load().pa_decode(*head, *tail, int(flags), _stream(stream))
     _check("pa_decode", st)
+
+
+def pa_decode_noalloc(out, q, kv_pool, block_tables, context_lens, max_context_len, scale=None,
+                      partition_size=None, flags=0, stream=None):
+    """pa_decode without a workspace: the library uses its own fixed device scratch
+    (PA_DECODE_NOALLOC_SCRATCH_BYTES per GPU), so nothing is allocated, here or in the
+    library. Calls that may overlap on one GPU race on that scratch."""
+    nb, bs, hkv, d = _pool_geometry(kv_pool)
+    B, hq, dq = q.shape
+    if dq != d or tuple(out.shape) != (B, hq, d):
+        raise ValueError("q and out must be [num_seqs, num_q_heads, head_size]")
+    if block_tables.dim() != 2 or block_tables.shape[0] != B or tuple(context_lens.shape) != (B,):
+        raise ValueError("block_tables must be [num_seqs, max_blocks], context_lens [num_seqs]")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if partition_size is None:
+        partition_size = pa_decode_default_partition_size(B, hq, hkv, int(max_context_len))
+    st = load().pa_decode_noalloc(
+        _dense(out, "out", torch.float16), _dense(q, "q", torch.float16),
+        _dense(kv_pool, "kv_pool", torch.float16), _dense(block_tables, "block_tables", torch.int32),
+        _dense(context_lens, "context_lens", torch.int32), B, hq, hkv, d, bs,
+        int(block_tables.shape[1]), nb, int(max_context_len), float(scale), int(partition_size),
+        int(flags), _stream(stream))
+    _check("pa_decode_noalloc", st)
 
 
 def pa_decode_shared_prefix_workspace_bytes(num_seqs, num_q_heads, max_context_len,

@@ -6,6 +6,7 @@
 #include <cstdint>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 #include <new>
 
 #include "../../include/pagedkv.h"
@@ -375,6 +376,76 @@ PA_EXPORT pa_status pa_decode_fp8(void* out, const void* q, const void* kv_pool,
                      num_kv_heads, head_size, block_size, max_blocks_per_seq, num_blocks,
                      max_context_len, scale, partition_size, workspace, workspace_bytes, flags,
                      true, k_scale, v_scale, stream);
+}
+
+// ---------------------------------------------------------------------------------------
+// decode with the library's own scratch (no allocation, no caller workspace)
+// ---------------------------------------------------------------------------------------
+
+namespace {
+
+// Scratch of pa_decode_noalloc: the decode workspace (partial results and the work order)
+// in a fixed device array, one copy per GPU, held until the process ends. On the host the
+// name is only a stand-in for the symbol, never a device address: host code uses the
+// address the runtime reports for the current device (scratch_of_current_device).
+__device__ __align__(256) unsigned char scratch[PA_DECODE_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mutex;
+void* g_scratch[kMaxDevices] = {};
+
+// Device address of `scratch` on the current device, looked up once per device.
+pa_status scratch_of_current_device(void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_status(e);
+  if (dev < 0 || dev >= kMaxDevices) return PA_ERR_UNSUPPORTED;
+  std::lock_guard<std::mutex> lock(g_scratch_mutex);
+  if (g_scratch[dev] == nullptr) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_status(e);
+    if (ptr == nullptr) {
+      std::snprintf(g_last_error, sizeof(g_last_error), "no device address for the scratch array");
+      return PA_ERR_HIP;
+    }
+    g_scratch[dev] = ptr;
+  }
+  *out = g_scratch[dev];
+  return PA_OK;
+}
+
+}  // namespace
+
+PA_EXPORT pa_status pa_decode_noalloc(void* out, const void* q, const void* kv_pool,
+                                      const int32_t* block_tables, const int32_t* context_lens,
+                                      int32_t num_seqs, int32_t num_q_heads,
+                                      int32_t num_kv_heads, int32_t head_size,
+                                      int32_t block_size, int32_t max_blocks_per_seq,
+                                      int64_t num_blocks, int32_t max_context_len, float scale,
+                                      int32_t partition_size, uint32_t flags, void* stream) {
+  // sizes first: a call that needs more scratch than the array holds is refused before
+  // any device access
+  const int64_t need = pa_decode_workspace_bytes(num_seqs, num_q_heads, max_context_len,
+                                                 partition_size, head_size);
+  if (need < 0) return PA_ERR_INVALID;
+  if (need > (int64_t)PA_DECODE_NOALLOC_SCRATCH_BYTES) {
+    std::snprintf(g_last_error, sizeof(g_last_error),
+                  "pa_decode_noalloc needs %lld bytes of scratch, more than its %lld",
+                  (long long)need, (long long)PA_DECODE_NOALLOC_SCRATCH_BYTES);
+    return PA_ERR_WORKSPACE;
+  }
+  void* ws = nullptr;
+  if (num_seqs > 0) {
+    if (pa_status st = scratch_of_current_device(&ws)) return st;
+  }
+  // nothing in the scratch has to start at zero: the work-order pre-pass writes its count
+  // and list before the partition kernel reads them, and every partial result is written
+  // before the reduce reads it
+  return decode_impl(out, q, kv_pool, block_tables, context_lens, num_seqs, num_q_heads,
+                     num_kv_heads, head_size, block_size, max_blocks_per_seq, num_blocks,
+                     max_context_len, scale, partition_size, ws,
+                     (int64_t)PA_DECODE_NOALLOC_SCRATCH_BYTES, flags, false, 1.0f, 1.0f, stream);
 }
 
 namespace {

@@ -145,6 +145,23 @@ def test_decode_rejects(lib, kw, status):
     assert decode_call(lib, **kw) == status
 
 
+def test_decode_noalloc_refuses_what_its_scratch_cannot_hold(lib):
+    """pa_decode_noalloc checks the workspace its call needs against the library's fixed
+    scratch before any device access."""
+    f = lib.pa_decode_noalloc
+    def call(B, hq, maxlen, ps, d=128):
+        return f(FAKE, FAKE, FAKE, FAKE, FAKE, B, hq, hq, d, 16, 4096, 1 << 20, maxlen, 0.1, ps, 0,
+                 None)
+    need = pkv.pa_decode_workspace_bytes(256, 32, 32768, 512, 128)
+    assert need > pkv.PA_DECODE_NOALLOC_SCRATCH_BYTES
+    assert call(256, 32, 32768, 512) == pkv.PA_ERR_WORKSPACE
+    assert b"scratch" in lib.pa_last_error()
+    assert call(4, 0, 100, 16) == pkv.PA_ERR_INVALID      # bad sizes
+    assert call(4, 8, 100, 0) == pkv.PA_ERR_INVALID
+    assert call(0, 8, 100, 16) == pkv.PA_OK               # nothing to do, no device access
+    assert pkv.pa_decode_workspace_bytes(8, 32, 32768, 512, 128) <= pkv.PA_DECODE_NOALLOC_SCRATCH_BYTES
+
+
 def test_decode_empty_batch_is_ok(lib):
     assert decode_call(lib, B=0) == pkv.PA_OK
 
