@@ -241,6 +241,18 @@ def test_decode_on_a_side_stream():
     del scratch
 
 
+@pytest.mark.parametrize("hkv,G", [(3, 1), (5, 1), (3, 2), (5, 4), (6, 8)])
+def test_decode_kv_heads_not_a_multiple_of_four(hkv, G):
+    """A workgroup holds four KV heads of one (sequence, partition): with 3, 5 or 6 KV heads
+    the last group is partly empty. One partition and several, ordered and not."""
+    inp = workloads.decode_case(75 + hkv + G, [1, 17, 300, 700, 1200, 64], hkv * G, hkv, 128)
+    ref = oracle_decode(inp)
+    d = Dev(inp)
+    for ps, flags in ((4096, 0), (256, 0), (256, pkv.PA_DECODE_KV_STREAM)):
+        note(f"decode Hkv={hkv} G={G} ps={ps} flags={flags}")
+        check_attention(d.decode(partition_size=ps, flags=flags), ref, f"Hkv{hkv} G{G} ps{ps}")
+
+
 def test_decode_length_one_rows_are_exact():
     inp = workloads.decode_case(41, [1] * 8, 16, 4, 128)
     got = Dev(inp).decode()

@@ -116,3 +116,61 @@ def test_capture_needs_caller_workspace():
                 pkv.pa_decode(out, q, pool, bt, lens, 1500, inp.scale, 512, None, stream=side)
     side.synchronize()
     g.close()
+
+
+def test_captured_noalloc_decode_replays_bit_exact():
+    """pa_decode_noalloc (the library's fixed scratch, no allocation) captured into a graph:
+    several partitions (so the reduce kernel runs) and PA_DECODE_KV_STREAM (so the
+    longest-first order pre-pass runs). Before each replay an eager call on another batch
+    rewrites the scratch; every replay still equals pa_decode with a caller workspace,
+    before and after the queries change in place."""
+    rng = np.random.default_rng(73)
+    inp = workloads.decode_case(73, rng.integers(1, 1500, 600), 8, 8, 64)
+    other = workloads.decode_case(74, [900, 33, 1400], 8, 8, 64, append=False)
+    q, bt, lens = (dev(a) for a in inp.decode_part())
+    pool = dev(inp.pool)
+    pkv.pa_kv_append(pool, dev(inp.key_new), dev(inp.value_new), dev(inp.slot_mapping))
+    mcl = int(inp.seq_lens.max())
+    ps, flags = 256, pkv.PA_DECODE_KV_STREAM
+    assert pkv.pa_decode_workspace_bytes(600, 8, mcl, ps, 64) <= pkv.PA_DECODE_NOALLOC_SCRATCH_BYTES
+
+    def reference(qq):
+        want = torch.empty_like(qq)
+        pkv.pa_decode(want, qq, pool, bt, lens, mcl, inp.scale, ps, flags=flags)
+        torch.cuda.synchronize()
+        return want
+
+    q2 = torch.randn(q.shape, generator=torch.Generator().manual_seed(7)).half().cuda()
+    want1, want2 = reference(q), reference(q2)
+    oq, obt, olens = (dev(a) for a in other.decode_part())
+    opool = dev(other.pool)
+    oout = torch.empty_like(oq)
+
+    side = torch.cuda.Stream()
+    out = torch.full_like(q, float("nan"))
+    g = pkv.StepGraph(side)
+    torch.cuda.synchronize()
+    note("graph: capture pa_decode_noalloc")
+    with torch.cuda.stream(side):
+        with g:
+            pkv.pa_decode_noalloc(out, q, pool, bt, lens, mcl, inp.scale, ps, flags, stream=side)
+    torch.cuda.synchronize()
+    assert torch.isnan(out.float()).all()  # captured, not run
+    q1 = q.clone()
+    try:
+        for rep, (qq, want) in enumerate([(q1, want1), (q2, want2), (q1, want1)]):
+            q.copy_(qq)
+            out.fill_(float("nan"))
+            # another batch through the same scratch, eagerly, before the replay
+            pkv.pa_decode_noalloc(oout, oq, opool, obt, olens, 1400, other.scale, 128)
+            torch.cuda.synchronize()
+            note(f"graph: noalloc replay {rep}")
+            g.launch()
+            side.synchronize()
+            assert torch.equal(out.view(torch.int16), want.view(torch.int16)), rep
+    finally:
+        g.close()
+    check_attention(host(out), oracle.decode(inp.q, oracle.kv_append(inp.pool, inp.key_new,
+                                                                       inp.value_new, inp.slot_mapping),
+                                             inp.block_tables, inp.seq_lens, inp.scale),
+                    "noalloc graph replay")

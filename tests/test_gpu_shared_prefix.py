@@ -106,3 +106,14 @@ def test_output_store_rounds_to_nearest_even(G):
     for b in range(2):
         assert np.array_equal(bits(got[b]), bits(want)), b
     assert (bits(rne) != bits(toward0)).any() and (bits(rne) != bits(away)).any()
+
+
+@pytest.mark.parametrize("hkv,G", [(3, 4), (5, 2)])
+def test_kv_heads_not_a_multiple_of_four(hkv, G):
+    rng = np.random.default_rng(240 + hkv)
+    priv = rng.integers(0, 70, 12)
+    inp = workloads.prefix_shared_case(240 + hkv + G, 3, 4, 3, priv, hkv * G, hkv, 128)
+    exp = oracle_out(inp)
+    for ps in (16, 512):
+        note(f"shared prefix Hkv={hkv} G={G} ps={ps}")
+        check_attention(run(inp, [0, 4, 8, 12], [48, 48, 48], ps), exp, f"shared Hkv{hkv} G{G} ps{ps}")
