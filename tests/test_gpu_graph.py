@@ -3,7 +3,9 @@
 The step is kv_append -> chunked prefill (its context split, so the merge kernel runs
 too) -> decode (grouped-query tile, several partitions, so the log-sum-exp reduce runs
 too). Replays are separated by eager work
-and host synchronisations, and the queries are changed in place between them."""
+and host synchronisations, and the queries are changed in place between them. The same
+for the step over an E4M3 pool, for shared-prefix decode, and for pa_decode_noalloc (its
+fixed scratch rewritten by an eager call before each replay)."""
 
 import numpy as np
 import pytest
@@ -174,3 +176,126 @@ def test_captured_noalloc_decode_replays_bit_exact():
                                                                        inp.value_new, inp.slot_mapping),
                                              inp.block_tables, inp.seq_lens, inp.scale),
                     "noalloc graph replay")
+
+
+def test_captured_fp8_step_replays_bit_exact():
+    """The same step over an E4M3 pool (quantizing append, prefill with its context split,
+    decode over several partitions) captured and replayed: every replay equals the eager
+    step bit for bit, and the eager step matches the oracle on the dequantized pool."""
+    from oracle import fp8
+    ks, vs = 0.03, 0.02
+    inp = workloads.mixed_case(76, [0, 1500, 40], [64, 100, 33], [1, 50, 700, 2000, 1100], 8, 4, 128)
+    pool_u8 = np.concatenate([fp8.quantize(inp.pool[:, :, 0:1], ks),
+                              fp8.quantize(inp.pool[:, :, 1:2], vs)], axis=2)
+    key, value, slots = dev(inp.key_new), dev(inp.value_new), dev(inp.slot_mapping)
+    qd, btd, lensd = inp.decode_part()
+    dq, dbt, dlens = dev(qd), dev(btd), dev(lensd)
+    qp, btp, qsl, lensp = inp.prefill_part()
+    pq, pbt, pqsl, plens = dev(qp), dev(btp), dev(qsl), dev(lensp)
+    mcl, max_q, max_s = int(lensd.max()), int(np.diff(qsl).max()), int(lensp.max())
+    ws = torch.empty(pkv.pa_decode_workspace_bytes(len(lensd), 8, mcl, 512, 128), dtype=torch.uint8,
+                     device="cuda")
+    pws_n = pkv.pa_prefill_workspace_bytes(len(lensp), 8, max_q, max_s, 128)
+    assert pws_n > 0
+    pws = torch.empty(pws_n, dtype=torch.uint8, device="cuda")
+    pool = dev(pool_u8)
+    dout = torch.full_like(dq, float("nan"))
+    pout = torch.full_like(pq, float("nan"))
+
+    def step(stream):
+        pkv.pa_kv_append_fp8(pool, key, value, slots, ks, vs, stream=stream)
+        pkv.pa_prefill_chunk_fp8(pout, pq, pool, pbt, pqsl, plens, max_q, max_s, inp.scale, ks, vs,
+                                 workspace=pws, stream=stream)
+        pkv.pa_decode_fp8(dout, dq, pool, dbt, dlens, mcl, inp.scale, ks, vs, 512, ws, stream=stream)
+
+    side = torch.cuda.Stream()
+    note("graph fp8: eager step")
+    with torch.cuda.stream(side):
+        step(side)
+    side.synchronize()
+    ref_d, ref_p = dout.clone(), pout.clone()
+    want_pool = fp8.kv_append_fp8(pool_u8, inp.key_new, inp.value_new, inp.slot_mapping, ks, vs)
+    assert np.array_equal(host(pool), want_pool)
+    vals = fp8.dequantize_pool(want_pool, ks, vs)
+    check_attention(host(ref_d), oracle.decode(qd, vals, btd, lensd, inp.scale), "graph fp8 eager decode")
+    check_attention(host(ref_p), oracle.prefill_chunk(qp, vals, btp, qsl, lensp, inp.scale),
+                    "graph fp8 eager prefill")
+
+    g = pkv.StepGraph(side)
+    dout.fill_(float("nan"))
+    pout.fill_(float("nan"))
+    torch.cuda.synchronize()
+    with torch.cuda.stream(side):
+        with g:
+            step(side)
+    torch.cuda.synchronize()
+    assert torch.isnan(dout.float()).all() and torch.isnan(pout.float()).all()
+    try:
+        for rep in range(3):
+            note(f"graph fp8: replay {rep}")
+            dout.fill_(float("nan"))
+            pout.fill_(float("nan"))
+            pool.copy_(dev(pool_u8))  # the append rewrites the same slots each replay
+            torch.cuda.synchronize()
+            g.launch()
+            side.synchronize()
+            assert torch.equal(dout.view(torch.int16), ref_d.view(torch.int16)), f"decode replay {rep}"
+            assert torch.equal(pout.view(torch.int16), ref_p.view(torch.int16)), f"prefill replay {rep}"
+            _ = (dout.float().sum() + 1).item()  # eager work between replays
+    finally:
+        g.close()
+
+
+def test_captured_shared_prefix_decode_replays_bit_exact():
+    """Shared-prefix decode (prefix pass, own-token pass and the cascade reduce) captured
+    and replayed, with the queries changed in place between replays."""
+    rng = np.random.default_rng(77)
+    priv = rng.integers(0, 70, 24)
+    inp = workloads.prefix_shared_case(77, 3, 8, 4, priv, 16, 4, 128)
+    q, bt, L = inp.decode_part()
+    dq, dbt, dL, pool = dev(q), dev(bt), dev(L), dev(inp.pool)
+    gs = dev(np.array([0, 8, 16, 24], np.int32))
+    pl = dev(np.array([64, 64, 64], np.int32))
+    mcl = int(L.max())
+    ws = torch.empty(pkv.pa_decode_shared_prefix_workspace_bytes(24, 16, mcl, 64, 32, 128),
+                     dtype=torch.uint8, device="cuda")
+    out = torch.full_like(dq, float("nan"))
+
+    def call(stream):
+        pkv.pa_decode_shared_prefix(out, dq, pool, dbt, dL, mcl, gs, pl, 8, 64, inp.scale, 32,
+                                    workspace=ws, stream=stream)
+
+    side = torch.cuda.Stream()
+    with torch.cuda.stream(side):
+        call(side)
+    side.synchronize()
+    ref1 = out.clone()
+    check_attention(host(ref1), oracle.decode(q, inp.pool, bt, L, inp.scale), "graph shared eager")
+    q1 = dq.clone()
+    q2 = torch.randn(dq.shape, generator=torch.Generator().manual_seed(8)).half().cuda()
+    dq.copy_(q2)
+    with torch.cuda.stream(side):
+        call(side)
+    side.synchronize()
+    ref2 = out.clone()
+
+    g = pkv.StepGraph(side)
+    out.fill_(float("nan"))
+    torch.cuda.synchronize()
+    with torch.cuda.stream(side):
+        with g:
+            call(side)
+    torch.cuda.synchronize()
+    assert torch.isnan(out.float()).all()
+    try:
+        for rep, (qq, want) in enumerate([(q1, ref1), (q2, ref2), (q1, ref1)]):
+            note(f"graph shared: replay {rep}")
+            dq.copy_(qq)
+            out.fill_(float("nan"))
+            torch.cuda.synchronize()
+            g.launch()
+            side.synchronize()
+            assert torch.equal(out.view(torch.int16), want.view(torch.int16)), rep
+            _ = (out.float().sum() + 1).item()
+    finally:
+        g.close()
