@@ -290,12 +290,13 @@ def block_manager_leg(pkv, inp):
     return out
 
 
-def block_copy_leg(torch, pkv, num_kv_heads, head_size, reps=10):
+def block_copy_leg(torch, pkv, num_kv_heads, head_size, reps=10, flush=None):
     """Rates of the block copies, on buffers of their own: copy-on-write copies inside a
     2 GiB pool, half its blocks onto the other half (disjoint pairs: every byte read once
     and written once, against HBM; 8x the 256 MB last-level cache), and swaps of 128
     blocks to pinned host memory and back (against a torch copy of the same bytes between
-    the same memories, the host-link rate)."""
+    the same memories, the host-link rate). With ``flush`` each repetition is timed on its
+    own after the flush (median); the copy-on-write rate back to back is reported too."""
     elems = 16 * 2 * num_kv_heads * head_size
     block_bytes = 2 * elems
     nb = (2 << 30) // block_bytes
@@ -307,24 +308,40 @@ def block_copy_leg(torch, pkv, num_kv_heads, head_size, reps=10):
     out_pairs = torch.stack([perm[:nswap], torch.arange(nswap)], 1).contiguous().cuda()
     in_pairs = torch.stack([torch.arange(nswap), perm[npairs:npairs + nswap]], 1).contiguous().cuda()
     flat_dev = torch.zeros((nswap, elems), dtype=torch.float16, device="cuda")
+    flat_pool = pool.view(nb, elems)
 
-    def rate(fn, nbytes):
+    def rate(fn, nbytes, flushed=True):
         fn()
         torch.cuda.synchronize()
-        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        a.record()
-        for _ in range(reps):
-            fn()
-        b.record()
-        torch.cuda.synchronize()
-        ms = a.elapsed_time(b) / reps
+        if flush is not None and flushed:
+            ts = []
+            for _ in range(reps):
+                flush()
+                a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                a.record()
+                fn()
+                b.record()
+                torch.cuda.synchronize()
+                ts.append(a.elapsed_time(b))
+            ms = float(np.median(ts))
+        else:
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            for _ in range(reps):
+                fn()
+            b.record()
+            torch.cuda.synchronize()
+            ms = a.elapsed_time(b) / reps
         return {"us": ms * 1e3, "GBps": nbytes / (ms * 1e-3) / 1e9}
+
+    def cow():
+        pkv.pa_copy_blocks(pool.view(nb, 16, 2, num_kv_heads, head_size), pairs)
 
     res = {
         "block_bytes": block_bytes,
-        "copy_on_write": rate(lambda: pkv.pa_copy_blocks(
-            pool.view(nb, 16, 2, num_kv_heads, head_size), pairs),
-                              2 * npairs * block_bytes),
+        "copy_on_write": rate(cow, 2 * npairs * block_bytes),
+        "copy_on_write_no_flush": rate(cow, 2 * npairs * block_bytes, flushed=False),
+        "torch_copy_d2d": rate(lambda: flat_pool[npairs:2 * npairs].copy_(flat_pool[:npairs]), 2 * npairs * block_bytes),
         "swap_out": rate(lambda: pkv.pa_move_blocks(host_area, pool, out_pairs), nswap * block_bytes),
         "swap_in": rate(lambda: pkv.pa_move_blocks(pool, host_area, in_pairs), nswap * block_bytes),
         "torch_copy_d2h": rate(lambda: host_area.copy_(flat_dev, non_blocking=True), nswap * block_bytes),
@@ -734,10 +751,11 @@ def main():
 
     copies = None
     if not args.no_block_copies:
-        copies = block_copy_leg(torch, pkv, inp.num_kv_heads, inp.head_size)
-        log("block copies: copy-on-write {:.0f} GB/s, swap out {:.1f} GB/s, swap in {:.1f} GB/s "
-            "(torch copies {:.1f} / {:.1f} GB/s)".format(
-                copies["copy_on_write"]["GBps"], copies["swap_out"]["GBps"], copies["swap_in"]["GBps"],
+        copies = block_copy_leg(torch, pkv, inp.num_kv_heads, inp.head_size, flush=flush)
+        log("block copies: copy-on-write {:.0f} GB/s ({:.0f} back to back; torch's contiguous copy "
+            "{:.0f}), swap out {:.1f} GB/s, swap in {:.1f} GB/s (torch copies {:.1f} / {:.1f} GB/s)".format(
+                copies["copy_on_write"]["GBps"], copies["copy_on_write_no_flush"]["GBps"],
+                copies["torch_copy_d2d"]["GBps"], copies["swap_out"]["GBps"], copies["swap_in"]["GBps"],
                 copies["torch_copy_d2h"]["GBps"], copies["torch_copy_h2d"]["GBps"]))
 
     achieved = kv_bytes / (decode_ms * 1e-3) / 1e9
