@@ -35,7 +35,8 @@ HIPCC_FLAGS = [
     # matrix-core results in ordinary VGPRs rather than accumulation registers: the fp16
     # grouped-query decode kernel then needs 155 registers instead of 155 + 32 (three
     # waves per SIMD instead of two); its FP8 variant, which keeps the loaded codes packed,
-    # needs 117-120 (four waves per SIMD)
+    # needs 117-120 (four waves per SIMD), 133 in shared-prefix decode with two blocks in
+    # flight (three)
     "-mllvm", "-amdgpu-mfma-vgpr-form",
 ]
 

@@ -648,10 +648,28 @@ __global__ __launch_bounds__(kThreads) void decode_gqa_kernel(const DecodeArgs a
 #pragma unroll
     for (int j = 0; j < VL; ++j) vc[j] = load_raw(base + voff[j]);
   }
+  // Blocks requested ahead of the one being consumed: one, or two for an FP8 cache in
+  // shared-prefix decode, where a block is half the bytes of an fp16 one and the long
+  // prefix waves end up alone on the GPU (16 more registers: three waves per SIMD
+  // instead of four; slower for plain FP8 decode, which keeps one)
+  constexpr int AHEAD = (kFp8 && Mode == kModeShared) ? 2 : 1;
+  Raw k1[KL], v1[VL];  // with AHEAD == 2: block jb + 1, in flight
+  if constexpr (AHEAD == 2) {
+    if (blk_begin + 1 < blk_end) {
+      const int phys = __builtin_amdgcn_readlane(bt_vec, 1);
+      const bool bad = phys < 0 || phys >= a.num_blocks;
+      bad_table = bad_table || bad;
+      const KV* base = pool + (bad ? 0 : (int64_t)phys * block_elems);
+#pragma unroll
+      for (int j = 0; j < KL; ++j) k1[j] = load_raw(base + koff + KSTEP * j);
+#pragma unroll
+      for (int j = 0; j < VL; ++j) v1[j] = load_raw(base + voff[j]);
+    }
+  }
 
   for (int jb = blk_begin; jb < blk_end && !bad_table; ++jb) {
     Raw kn[KL], vn[VL];
-    const int jn = jb + 1;
+    const int jn = jb + AHEAD;
     if (jn < blk_end) {
       const int k64 = (jn - blk_begin) & 63;
       if (k64 == 0) bt_vec = (lane < blk_end - jn) ? bt[jn + lane] : 0;
@@ -727,10 +745,23 @@ __global__ __launch_bounds__(kThreads) void decode_gqa_kernel(const DecodeArgs a
     }
     // the next block's V overwrites the stage only after these reads have returned
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    if constexpr (AHEAD == 2) {
 #pragma unroll
-    for (int j = 0; j < KL; ++j) kc[j] = kn[j];
+      for (int j = 0; j < KL; ++j) {
+        kc[j] = k1[j];
+        k1[j] = kn[j];
+      }
 #pragma unroll
-    for (int j = 0; j < VL; ++j) vc[j] = vn[j];
+      for (int j = 0; j < VL; ++j) {
+        vc[j] = v1[j];
+        v1[j] = vn[j];
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < KL; ++j) kc[j] = kn[j];
+#pragma unroll
+      for (int j = 0; j < VL; ++j) vc[j] = vn[j];
+    }
   }
 
   // column sums over the four 16-lane groups
@@ -930,12 +961,12 @@ hipError_t launch_shared_prefix_dg(const DecodeArgs& a, hipStream_t stream) {
   if (wpre + wown > INT32_MAX) return hipErrorInvalidValue;
   k.prefix_grid = (int)wpre;
   // one launch: prefix items, then every sequence's own tokens (independent outputs). Each
-  // physical block is read once here (the prefix once per group), so fp16 K/V loads carry
-  // the non-temporal hint (64 prompt groups x 4 samples: 103.5 -> 92.1 us); the FP8
-  // cache's loads (16 E4M3 codes per lane) keep the default, which was faster for them
-  // (53.7 against 69.6 us with the hint).
-  constexpr bool kStreamShared = sizeof(KV) == 2;
-  hipLaunchKernelGGL((decode_gqa_kernel<D, G, kStreamShared, KV, kModeShared>), dim3((unsigned)(wpre + wown)),
+  // physical block is read once here (the prefix once per group), so the K/V loads carry
+  // the non-temporal hint (64 prompt groups x 4 samples, fp16: 103.5 -> 92.1 us; FP8,
+  // after a cache flush and with two blocks in flight: 66.4 -> 64.3 us, where back to
+  // back, with the whole FP8 working set in the last-level cache, plain loads were
+  // faster).
+  hipLaunchKernelGGL((decode_gqa_kernel<D, G, true, KV, kModeShared>), dim3((unsigned)(wpre + wown)),
                      dim3(kThreads), 0, stream, k, nullptr);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
