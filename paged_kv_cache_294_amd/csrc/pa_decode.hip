@@ -720,7 +720,7 @@ __global__ __launch_bounds__(kThreads) void decode_gqa_kernel(const DecodeArgs a
     if (__builtin_amdgcn_ballot_w64(move)) {
       asm volatile("");
       const float mnew = move ? mb : m;
-      const float alpha = fast_exp2(m - mnew);
+      const float alpha = move ? fast_exp2(m - mnew) : 1.0f;  // a column still at -inf stays
       l *= alpha;
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt) o[dt] *= alpha;

@@ -505,7 +505,10 @@ __global__ __launch_bounds__(kThreads, 3) void prefill_kernel(const PrefillArgs 
         keep_branch();
         const float mrow = fmaxf(ms, __shfl_xor(ms, 32, kWave));
         const float mnew = mrow > m + kRescaleSlack ? mrow : m;
-        const float alpha = fast_exp2(m - mnew);  // 0 when m was -inf, 1 when not moved
+        // 0 when m was -inf; 1 when the row's max did not move, also when it stays at -inf
+        // (a row that sees none of this piece's tokens while other rows of the wave do:
+        // 2^(-inf - -inf) would be NaN)
+        const float alpha = mnew == m ? 1.0f : fast_exp2(m - mnew);
         l *= alpha;
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt) o[dt] *= alpha;

@@ -292,3 +292,20 @@ def test_prefill_fp8_split_matches_unsplit_and_oracle(D):
                                 rows=set(rows.tolist()))
     check_attention(outs[0][rows], want[rows], f"fp8 split D{D}")
     assert np.abs(outs[0] - outs[1]).max() <= 2e-3
+
+
+def test_prefill_fp8_split_piece_boundary_inside_a_wave():
+    """As for fp16: a piece's first token inside one wave's rows (prior 20, chunk 1100),
+    every row against the oracle on the dequantized pool, no NaN."""
+    inp = workloads.mixed_case(127, [20], [1100], [], 2, 1, 128)
+    q, bt, qsl, lens = inp.prefill_part()
+    mq, ms = int(np.diff(qsl).max()), int(lens.max())
+    assert pkv.pa_prefill_workspace_bytes(len(lens), 2, mq, ms, 128) > 0
+    ks, vs = 0.04, 0.03
+    pool_h = quantized_step_pool(inp, ks, vs)
+    out = torch.full(q.shape, float("nan"), dtype=torch.float16, device="cuda")
+    note("prefill fp8 split, piece boundary inside a wave")
+    pkv.pa_prefill_chunk_fp8(out, dev(q), dev(pool_h), dev(bt), dev(qsl), dev(lens), mq, ms,
+                             inp.scale, ks, vs, split=True)
+    want = oracle.prefill_chunk(q, fp8.dequantize_pool(pool_h, ks, vs), bt, qsl, lens, inp.scale)
+    check_attention(host(out), want, "fp8 split boundary")

@@ -180,6 +180,22 @@ def test_prefill_split_single_long_request():
     assert np.abs(got.astype(np.float64) - whole.astype(np.float64)).max() <= 2e-3
 
 
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("prior,chunk", [(20, 1100), (100, 1500), (1000, 1500), (300, 2000)])
+def test_prefill_split_piece_boundary_inside_a_wave(D, prior, chunk):
+    """Priors that are not a multiple of 32 put a piece's first token inside one wave's 32
+    rows, so some rows of that wave see none of the piece while the others do (those rows'
+    maxima stay at -inf while the wave rescales): every row against the oracle, no NaN."""
+    inp = workloads.mixed_case(62 + prior + D, [prior], [chunk], [], 2, 1, D)
+    assert workspace_bytes(inp) > 0
+    pool = appended_pool(inp)
+    note(f"prefill split, piece boundary inside a wave: D={D} P={prior} C={chunk}")
+    got = run_prefill(inp, pool, True)
+    check_attention(got, oracle_prefill(inp), f"split boundary D{D} P{prior}")
+    whole = run_prefill(inp, pool, False)
+    assert np.abs(got.astype(np.float64) - whole.astype(np.float64)).max() <= 2e-3
+
+
 def test_prefill_split_bad_entry_in_late_piece_is_nan():
     inp = workloads.mixed_case(58, [9000, 3000], [200, 64], [], 8, 8, 128)
     assert workspace_bytes(inp) > 0
