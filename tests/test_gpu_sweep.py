@@ -2,7 +2,7 @@
 own head size, query-group size, KV-head count, lengths and partition size (and for
 prefill the requests' priors and chunks; for shared-prefix decode the groups and their
 declared prefixes), so that combinations the hand-written cases do not list are checked
-too. Every case is small enough for the fp64 oracle to finish in well under a second."""
+too. Every case is small enough for the fp64 oracle to finish in a few seconds at most."""
 
 import numpy as np
 import pytest
@@ -110,3 +110,42 @@ def test_shared_prefix_sweep(seed):
     pkv.pa_decode_shared_prefix(out, dev(q), dev(inp.pool), dev(bt), dev(L), int(max(L.max(), mp)),
                                 dev(gs), dev(pl), samples, mp, inp.scale, ps)
     check_attention(host(out), oracle.decode(q, inp.pool, bt, L, inp.scale), f"shared sweep {seed}")
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_prefill_split_sweep(seed):
+    """Launches small enough for the context split (one or two requests, few heads) with
+    priors that are rarely a multiple of 32, so piece boundaries land anywhere in the rows;
+    fp16 or E4M3; every row against the oracle."""
+    rng = np.random.default_rng(4000 + seed)
+    D = int(rng.choice([64, 128]))
+    G = int(rng.choice([1, 2, 4]))
+    hkv = int(rng.integers(1, 3))
+    R = int(rng.integers(1, 3))
+    priors = rng.integers(0, 2500, R)
+    chunks = rng.integers(1, 1400, R)
+    chunks[0] = max(int(chunks[0]), 1100 - int(priors[0]))  # at least one context past 1024
+    inp = workloads.mixed_case(4000 + seed, priors, chunks, [], hkv * G, hkv, D)
+    q, bt, qsl, lens = inp.prefill_part()
+    mq, ms = int(np.diff(qsl).max()), int(lens.max())
+    assert pkv.pa_prefill_workspace_bytes(R, hkv * G, mq, ms, D) > 0  # the split is taken
+    fp8_pool = bool(rng.integers(0, 2))
+    note(f"prefill split sweep seed={seed} D={D} G={G} Hkv={hkv} priors={priors.tolist()} "
+         f"chunks={chunks.tolist()} fp8={fp8_pool}")
+    out = torch.full(q.shape, float("nan"), dtype=torch.float16, device="cuda")
+    if fp8_pool:
+        ks, vs = float(rng.uniform(0.01, 0.05)), float(rng.uniform(0.01, 0.05))
+        pool_u8 = fp8.kv_append_fp8(np.concatenate([fp8.quantize(inp.pool[:, :, 0:1], ks),
+                                                    fp8.quantize(inp.pool[:, :, 1:2], vs)], axis=2),
+                                    inp.key_new, inp.value_new, inp.slot_mapping, ks, vs)
+        pkv.pa_prefill_chunk_fp8(out, dev(q), dev(pool_u8), dev(bt), dev(qsl), dev(lens), mq, ms,
+                                 inp.scale, ks, vs, split=True)
+        vals = fp8.dequantize_pool(pool_u8, ks, vs)
+    else:
+        pool_d = dev(inp.pool)
+        pkv.pa_kv_append(pool_d, dev(inp.key_new), dev(inp.value_new), dev(inp.slot_mapping))
+        pkv.pa_prefill_chunk(out, dev(q), pool_d, dev(bt), dev(qsl), dev(lens), mq, ms, inp.scale,
+                             split=True)
+        vals = oracle.kv_append(inp.pool, inp.key_new, inp.value_new, inp.slot_mapping)
+    check_attention(host(out), oracle.prefill_chunk(q, vals, bt, qsl, lens, inp.scale),
+                    f"prefill split sweep {seed}")
