@@ -98,17 +98,23 @@ def test_shared_prefix_sweep(seed):
     pblocks = int(rng.integers(1, 6))
     priv = rng.integers(0, 90, groups * samples)
     inp = workloads.prefix_shared_case(3000 + seed, groups, samples, pblocks, priv, hkv * G, hkv, D)
-    # declared prefixes: up to the blocks the group really shares (fewer is still valid)
-    pl = (rng.integers(0, pblocks + 1, groups) * 16).astype(np.int32)
-    gs = (np.arange(groups + 1) * samples).astype(np.int32)
+    # declared groups: each generated group cut into one to three runs of consecutive
+    # sequences; declared prefixes up to the blocks the group really shares (fewer is valid)
+    starts = [0]
+    for g in range(groups):
+        cuts = sorted(rng.choice(np.arange(1, samples), size=min(int(rng.integers(0, 3)), samples - 1),
+                                 replace=False).tolist()) if samples > 1 else []
+        starts += [g * samples + c for c in cuts] + [(g + 1) * samples]
+    gs = np.asarray(starts, np.int32)
+    pl = (rng.integers(0, pblocks + 1, len(gs) - 1) * 16).astype(np.int32)
     ps = 16 * int(rng.integers(1, 40))
     note(f"shared-prefix sweep seed={seed} D={D} G={G} Hkv={hkv} groups={groups}x{samples} "
-         f"prefixes={pl.tolist()} ps={ps}")
+         f"declared={np.diff(gs).tolist()} prefixes={pl.tolist()} ps={ps}")
     q, bt, L = inp.decode_part()
     out = torch.full(q.shape, float("nan"), dtype=torch.float16, device="cuda")
     mp = int(pl.max())
     pkv.pa_decode_shared_prefix(out, dev(q), dev(inp.pool), dev(bt), dev(L), int(max(L.max(), mp)),
-                                dev(gs), dev(pl), samples, mp, inp.scale, ps)
+                                dev(gs), dev(pl), int(np.diff(gs).max()), mp, inp.scale, ps)
     check_attention(host(out), oracle.decode(q, inp.pool, bt, L, inp.scale), f"shared sweep {seed}")
 
 
