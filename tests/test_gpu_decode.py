@@ -253,6 +253,20 @@ def test_decode_kv_heads_not_a_multiple_of_four(hkv, G):
         check_attention(d.decode(partition_size=ps, flags=flags), ref, f"Hkv{hkv} G{G} ps{ps}")
 
 
+@pytest.mark.parametrize("G", [1, 4])
+def test_decode_many_short_sequences_ordered(G):
+    """5000 short sequences (more items than the GPU holds, up to five partitions each):
+    the longest-first pre-pass sorts 25k items; every row against the oracle."""
+    rng = np.random.default_rng(110 + G)
+    lens = rng.integers(1, 300, 5000)
+    inp = workloads.decode_case(110 + G, lens, 2 * G, 2, 64)
+    ref = oracle_decode(inp)
+    d = Dev(inp)
+    for ps, flags in ((64, pkv.PA_DECODE_KV_STREAM), (64, 0), (512, pkv.PA_DECODE_KV_STREAM)):
+        note(f"decode 5000 sequences G={G} ps={ps} flags={flags}")
+        check_attention(d.decode(partition_size=ps, flags=flags), ref, f"5000 seqs G{G} ps{ps}")
+
+
 def test_decode_length_one_rows_are_exact():
     inp = workloads.decode_case(41, [1] * 8, 16, 4, 128)
     got = Dev(inp).decode()
