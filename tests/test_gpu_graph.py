@@ -5,7 +5,8 @@ too) -> decode (grouped-query tile, several partitions, so the log-sum-exp reduc
 too). Replays are separated by eager work
 and host synchronisations, and the queries are changed in place between them. The same
 for the step over an E4M3 pool, for shared-prefix decode, and for pa_decode_noalloc (its
-fixed scratch rewritten by an eager call before each replay)."""
+fixed scratch rewritten by an eager call before each replay); and for one step replayed
+while the batch in its buffers changes (lengths, start offsets, tables and pool)."""
 
 import numpy as np
 import pytest
@@ -299,3 +300,85 @@ def test_captured_shared_prefix_decode_replays_bit_exact():
             _ = (out.float().sum() + 1).item()
     finally:
         g.close()
+
+
+def test_replays_follow_changed_lengths_and_tables():
+    """A serving loop replays one captured step while the batch changes: the host bounds
+    (max_context_len, max_q_len, max_seq_len) stay, the device lengths, start offsets and
+    tables change between replays. The decode's longest-first order and the prefill's
+    context-split plan are derived on the device from the new contents, so every replay
+    must equal an eager call on the same contents."""
+    big = workloads.mixed_case(78, [0, 1500, 40], [64, 100, 33], [1, 50, 700, 2000, 1100], 8, 4, 128)
+    small = workloads.mixed_case(79, [900, 20, 5], [33, 64, 100], [1600, 3, 1999, 40, 512], 8, 4, 128)
+    side = torch.cuda.Stream()
+    b = Batch(big)
+    # the second batch's metadata, padded to the first one's table width and pool
+    qd, btd, lensd = small.decode_part()
+    qp, btp, qsl, lensp = small.prefill_part()
+    assert btd.shape[1] <= b.dbt.shape[1] and btp.shape[1] <= b.pbt.shape[1]
+    assert int(lensd.max()) <= b.mcl and int(np.diff(qsl).max()) <= b.max_q and int(lensp.max()) <= b.max_s
+    assert qd.shape == tuple(b.dq.shape) and qp.shape == tuple(b.pq.shape)
+
+    def pad(t, width):
+        out = np.full((t.shape[0], width), int(t[0, -1]), np.int32)
+        out[:, :t.shape[1]] = t
+        return out
+
+    meta2 = dict(dq=dev(qd), dbt=dev(pad(btd, b.dbt.shape[1])), dlens=dev(lensd), pq=dev(qp),
+                 pbt=dev(pad(btp, b.pbt.shape[1])), qsl=dev(qsl), plens=dev(lensp))
+    meta1 = {k: getattr(b, k).clone() for k in meta2}
+    # the second batch's pool inside one of the first one's size (its blocks first, NaN after)
+    pool2 = torch.full_like(b.pool, float("nan"))
+    assert small.pool.shape[0] <= pool2.shape[0]
+    pool2[: small.pool.shape[0]] = dev(small.pool)
+    pkv.pa_kv_append(pool2, dev(small.key_new), dev(small.value_new), dev(small.slot_mapping))
+    pool1 = b.pool.clone()
+    pkv.pa_kv_append(pool1, b.key, b.value, b.slots)
+
+    def eager(meta, pool):
+        dout = torch.empty_like(b.dout)
+        pout = torch.empty_like(b.pout)
+        pkv.pa_prefill_chunk(pout, meta["pq"], pool, meta["pbt"], meta["qsl"], meta["plens"], b.max_q,
+                             b.max_s, big.scale, workspace=torch.empty_like(b.pws))
+        pkv.pa_decode(dout, meta["dq"], pool, meta["dbt"], meta["dlens"], b.mcl, big.scale, b.ps,
+                      torch.empty_like(b.ws), flags=pkv.PA_DECODE_KV_STREAM)
+        torch.cuda.synchronize()
+        return dout, pout
+
+    want = [eager(meta1, pool1), eager(meta2, pool2)]
+    # the step without the append (each pool already holds its batch's tokens)
+    work = b.pool
+
+    def step(stream):
+        pkv.pa_prefill_chunk(b.pout, b.pq, work, b.pbt, b.qsl, b.plens, b.max_q, b.max_s, big.scale,
+                             workspace=b.pws, stream=stream)
+        pkv.pa_decode(b.dout, b.dq, work, b.dbt, b.dlens, b.mcl, big.scale, b.ps, b.ws,
+                      flags=pkv.PA_DECODE_KV_STREAM, stream=stream)
+
+    g = pkv.StepGraph(side)
+    torch.cuda.synchronize()
+    with torch.cuda.stream(side):
+        with g:
+            step(side)
+    torch.cuda.synchronize()
+    try:
+        for rep, k in enumerate([0, 1, 0, 1]):
+            meta, pool = (meta1, pool1) if k == 0 else (meta2, pool2)
+            for name, t in meta.items():
+                getattr(b, name).copy_(t)
+            work.copy_(pool)
+            b.dout.fill_(float("nan"))
+            b.pout.fill_(float("nan"))
+            torch.cuda.synchronize()
+            note(f"graph: replay {rep} with batch {k}")
+            g.launch()
+            side.synchronize()
+            assert torch.equal(b.dout.view(torch.int16), want[k][0].view(torch.int16)), rep
+            assert torch.equal(b.pout.view(torch.int16), want[k][1].view(torch.int16)), rep
+    finally:
+        g.close()
+    # and the second batch's replay output against the oracle
+    vals = oracle.kv_append(small.pool, small.key_new, small.value_new, small.slot_mapping)
+    check_attention(host(want[1][0]), oracle.decode(qd, vals, btd, lensd, small.scale), "graph batch 2 decode")
+    check_attention(host(want[1][1]), oracle.prefill_chunk(qp, vals, btp, qsl, lensp, small.scale),
+                    "graph batch 2 prefill")
