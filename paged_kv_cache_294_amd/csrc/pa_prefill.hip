@@ -46,6 +46,7 @@ namespace pkv {
 namespace {
 
 typedef float float2_t __attribute__((ext_vector_type(2)));
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
 
 constexpr int kBM = 128;     // query rows per workgroup
 constexpr int kWRows = 32;   // query rows per wave
@@ -456,13 +457,19 @@ __global__ __launch_bounds__(kThreads, 3) void prefill_kernel(const PrefillArgs 
         *reinterpret_cast<half8_t*>(&sm.v16[t * ROW + 8 * ((2 * pc + 1) ^ vswz<D>(t))]) = hi;
       }
       lds_barrier();
-    } else if (__builtin_amdgcn_readfirstlane(t0 + kBN > S)) {
+    } else if (t0 + kBN > S) {  // uniform
       // the context's last stage: V rows past the end become zeros (their slots may hold
-      // anything, and 0 * NaN would reach the output)
+      // anything, and 0 * NaN would reach the output). The zero and the thread index are
+      // made here, behind volatile statements, so that the compiler keeps no address or
+      // zero vector of this rare path in registers across the stage loop.
       keep_branch();
-      for (int e = tid; e < kBN * PIECES; e += kThreads) {
+      int e0 = tid, z;
+      asm volatile("v_mov_b32 %0, 0" : "=v"(z) : "v"(e0));
+      asm volatile("" : "+v"(e0));
+      const u32x4_t zero = {(uint32_t)z, (uint32_t)z, (uint32_t)z, (uint32_t)z};
+      for (int e = e0; e < kBN * PIECES; e += kThreads) {
         const int t = e / PIECES;
-        if (t0 + t >= S) *reinterpret_cast<half8_t*>(&sm.v[ring][t * ROW + 8 * (e % PIECES)]) = half8_t{};
+        if (t0 + t >= S) *reinterpret_cast<u32x4_t*>(&sm.v[ring][t * ROW + 8 * (e % PIECES)]) = zero;
       }
       lds_barrier();
     }
@@ -473,21 +480,58 @@ __global__ __launch_bounds__(kThreads, 3) void prefill_kernel(const PrefillArgs 
       half8_t ka[KS];
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
-        if constexpr (kFp8)
+        if constexpr (kFp8) {
           ka[ks] = widen_fp8x8(*reinterpret_cast<const u32x2_t*>(
               &sm.k[ring][krow * ROW + 16 * (ks ^ kswz8<D>(krow)) + 8 * g]));
-        else
-          ka[ks] = *reinterpret_cast<const half8_t*>(
-              &sm.k[ring][krow * ROW + 8 * ((2 * ks + g) ^ kswz<D>(krow))]);
+        } else {
+          // piece (2 ks + g) ^ sw with sw = kswz(krow) < 8, written as 2 (4 (ks / 4) +
+          // ((ks % 4) ^ (sw / 2))) + (g ^ (sw % 2)): four lane addresses, ks / 4 an immediate
+          const int sw = kswz<D>(krow);
+          const int pc = 2 * (4 * (ks >> 2) + ((ks & 3) ^ (sw >> 1))) + (g ^ (sw & 1));
+          ka[ks] = *reinterpret_cast<const half8_t*>(&sm.k[ring][krow * ROW + 8 * pc]);
+        }
       }
       float16_t sacc = float16_t{};
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks)
         sacc = __builtin_amdgcn_mfma_f32_32x32x16_f16(ka[ks], qb[ks], sacc, 0, 0, 0);
 
+      // O^T += V^T P^T: k-step k covers stage tokens 16k .. 16k+15; the lane's 8 k-slots
+      // are tokens 16k + 4g + {0..3} (first read) and 16k + 8 + 4g + {0..3} (second)
+      half8_t va[2][DT];
+      auto read_v = [&](int k, int dt) {
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) {
+          const int t = 16 * k + 8 * hh + vtok;
+          const int dim = 32 * dt + 16 * dh + 4 * (li % 4);
+          const int piece = (dim / 8) ^ vswz<D>(t);
+          const half_t* vsrc = kFp8 ? &sm.v16[0] : reinterpret_cast<const half_t*>(&sm.v[ring][0]);
+          const short4_t x = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (__attribute__((address_space(3))) short4_t*)(vsrc + t * ROW + 8 * piece + (dim & 4)));
+          const half4_t y = __builtin_bit_cast(half4_t, x);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) va[k][dt][4 * hh + e] = y[e];
+        }
+      };
+      if constexpr (!kFp8) {
+        // K fragments read four ahead of the product that takes them (the compiler's own
+        // order waits for one pair of K reads after another: an LDS round trip every two
+        // products), then the first k-step's V^T fragments, which the scheduler places
+        // under the S^T products
+        constexpr int kAhead = KS < 4 ? KS : 4;
+        __builtin_amdgcn_sched_group_barrier(0x100, kAhead, 0);  // LDS reads
+#pragma unroll
+        for (int i = 0; i < KS - kAhead; ++i) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // a matrix product
+          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, kAhead, 0);
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) read_v(0, dt);
+      }
+
       // mask the diagonal / context-end stage: token t visible iff t <= min(S-1, P+qrow)
-      const int diag = __builtin_amdgcn_readfirstlane(!((t0 + kBN <= P + row_w + 1) && (t0 + kBN <= S)));
-      if (diag) {
+      if (!((t0 + kBN <= P + row_w + 1) && (t0 + kBN <= S))) {  // uniform
         keep_branch();
         const int lim = min(S - 1, P + qrow) - (t0 + 4 * g);
 #pragma unroll
@@ -530,25 +574,10 @@ __global__ __launch_bounds__(kThreads, 3) void prefill_kernel(const PrefillArgs 
           lsum = __builtin_amdgcn_fdot2(half2_t{pb[k][e], pb[k][e + 1]}, ones, lsum, false);
       l += lsum;  // this half's tokens; the halves are added at the end
 
-      // O^T += V^T P^T: k-step k covers stage tokens 16k .. 16k+15; the lane's 8 k-slots
-      // are tokens 16k + 4g + {0..3} (first read) and 16k + 8 + 4g + {0..3} (second)
-      half8_t va[2][DT];
 #pragma unroll
-      for (int k = 0; k < 2; ++k)
+      for (int k = kFp8 ? 0 : 1; k < 2; ++k)
 #pragma unroll
-        for (int dt = 0; dt < DT; ++dt)
-#pragma unroll
-          for (int hh = 0; hh < 2; ++hh) {
-            const int t = 16 * k + 8 * hh + vtok;
-            const int dim = 32 * dt + 16 * dh + 4 * (li % 4);
-            const int piece = (dim / 8) ^ vswz<D>(t);
-            const half_t* vsrc = kFp8 ? &sm.v16[0] : reinterpret_cast<const half_t*>(&sm.v[ring][0]);
-            const short4_t x = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                (__attribute__((address_space(3))) short4_t*)(vsrc + t * ROW + 8 * piece + (dim & 4)));
-            const half4_t y = __builtin_bit_cast(half4_t, x);
-#pragma unroll
-            for (int e = 0; e < 4; ++e) va[k][dt][4 * hh + e] = y[e];
-          }
+        for (int dt = 0; dt < DT; ++dt) read_v(k, dt);
 #pragma unroll
       for (int k = 0; k < 2; ++k)
 #pragma unroll
