@@ -567,8 +567,8 @@ def main():
                          "groups (reads each shared prefix once); auto: that when the workload "
                          "has prompt groups, else plain")
     ap.add_argument("--kv-dtype", choices=("fp16", "fp8"), default="fp16",
-                    help="cache element: fp16, or FP8 E4M3 codes (decode-only workloads; the "
-                         "prefill kernel reads fp16 caches only)")
+                    help="cache element: fp16, or FP8 E4M3 codes with per-tensor key and value "
+                         "scales (append, decode and prefill all read and write the codes)")
     ap.add_argument("--prefill-split", choices=("on", "off"), default="on",
                     help="on: pa_prefill_chunk gets its split-context workspace (long contexts "
                          "cut into pieces merged by log-sum-exp); off: one workgroup per row tile")
