@@ -33,10 +33,9 @@ HIPCC_FLAGS = [
     # no packed-fp32 instructions in generated code
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     # matrix-core results in ordinary VGPRs rather than accumulation registers: the fp16
-    # grouped-query decode kernel then needs 155 registers instead of 155 + 32 (three
-    # waves per SIMD instead of two); its FP8 variant, which keeps the loaded codes packed,
-    # needs 117-120 (four waves per SIMD), 133 in shared-prefix decode with two blocks in
-    # flight (three)
+    # grouped-query decode kernel then needs 154 registers instead of 154 + 32 (three
+    # waves per SIMD instead of two); its FP8 variant, which keeps the loaded codes packed
+    # and two blocks in flight, needs 138 (129 in shared-prefix decode; three waves)
     "-mllvm", "-amdgpu-mfma-vgpr-form",
 ]
 

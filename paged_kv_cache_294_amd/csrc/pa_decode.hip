@@ -638,49 +638,28 @@ __global__ __launch_bounds__(kThreads) void decode_gqa_kernel(const DecodeArgs a
 
   int bt_vec = (lane < blk_end - blk_begin) ? bt[blk_begin + lane] : 0;
   bool bad_table = false;
-  Raw kc[KL], vc[VL];
-  {
-    const int phys = __builtin_amdgcn_readfirstlane(bt_vec);
-    bad_table = phys < 0 || phys >= a.num_blocks;
-    const KV* base = pool + (bad_table ? 0 : (int64_t)phys * block_elems);
+  // Loads of block jb into kr / vr: its table entry from the lane vector (refilled every 64
+  // blocks); an entry outside the pool is not followed and flags the pass.
+  auto request = [&](Raw (&kr)[KL], Raw (&vr)[VL], int jb) {
+    const int k64 = (jb - blk_begin) & 63;
+    if (k64 == 0 && jb > blk_begin) bt_vec = (lane < blk_end - jb) ? bt[jb + lane] : 0;
+    const int phys = __builtin_amdgcn_readlane(bt_vec, k64);
+    const bool bad = phys < 0 || phys >= a.num_blocks;
+    bad_table = bad_table || bad;
+    const KV* base = pool + (bad ? 0 : (int64_t)phys * block_elems);
 #pragma unroll
-    for (int j = 0; j < KL; ++j) kc[j] = load_raw(base + koff + KSTEP * j);
+    for (int j = 0; j < KL; ++j) kr[j] = load_raw(base + koff + KSTEP * j);
 #pragma unroll
-    for (int j = 0; j < VL; ++j) vc[j] = load_raw(base + voff[j]);
-  }
-  // Blocks requested ahead of the one being consumed: one, or two for an FP8 cache in
-  // shared-prefix decode, where a block is half the bytes of an fp16 one and the long
-  // prefix waves end up alone on the GPU (16 more registers: three waves per SIMD
-  // instead of four; slower for plain FP8 decode, which keeps one)
-  constexpr int AHEAD = (kFp8 && Mode == kModeShared) ? 2 : 1;
-  Raw k1[KL], v1[VL];  // with AHEAD == 2: block jb + 1, in flight
-  if constexpr (AHEAD == 2) {
-    if (blk_begin + 1 < blk_end) {
-      const int phys = __builtin_amdgcn_readlane(bt_vec, 1);
-      const bool bad = phys < 0 || phys >= a.num_blocks;
-      bad_table = bad_table || bad;
-      const KV* base = pool + (bad ? 0 : (int64_t)phys * block_elems);
-#pragma unroll
-      for (int j = 0; j < KL; ++j) k1[j] = load_raw(base + koff + KSTEP * j);
-#pragma unroll
-      for (int j = 0; j < VL; ++j) v1[j] = load_raw(base + voff[j]);
-    }
-  }
-
-  for (int jb = blk_begin; jb < blk_end && !bad_table; ++jb) {
-    Raw kn[KL], vn[VL];
-    const int jn = jb + AHEAD;
-    if (jn < blk_end) {
-      const int k64 = (jn - blk_begin) & 63;
-      if (k64 == 0) bt_vec = (lane < blk_end - jn) ? bt[jn + lane] : 0;
-      const int phys = __builtin_amdgcn_readlane(bt_vec, k64);
-      bad_table = phys < 0 || phys >= a.num_blocks;
-      const KV* base = pool + (bad_table ? 0 : (int64_t)phys * block_elems);
-#pragma unroll
-      for (int j = 0; j < KL; ++j) kn[j] = load_raw(base + koff + KSTEP * j);
-#pragma unroll
-      for (int j = 0; j < VL; ++j) vn[j] = load_raw(base + voff[j]);
-    }
+    for (int j = 0; j < VL; ++j) vr[j] = load_raw(base + voff[j]);
+  };
+  // Blocks in flight. fp16: the next block is requested before the current one is used
+  // (two register buffers). FP8: the codes of a block are half the bytes, and two blocks
+  // are kept in flight without a third buffer: block jb + 2 is requested into block jb's
+  // registers as soon as its V is staged and its S^T products have read its K (C4 with
+  // private copies 113.9 -> 102.7 us, shared-prefix decode 64.5 -> 60.3 us; fp16 the
+  // same way took 12 more registers and was no faster)
+  constexpr bool kTwoAhead = kFp8;
+  auto consume = [&](Raw (&kr)[KL], Raw (&vr)[VL], int jb) {
     const int tok0 = jb * kBlockSize;
     const bool tail = tok0 + kBlockSize > L;
     // stage V (tokens past the context end as zeros: their slots may hold anything)
@@ -689,10 +668,10 @@ __global__ __launch_bounds__(kThreads) void decode_gqa_kernel(const DecodeArgs a
       const int t = (lane + kWave * j) / (PIECES / VPL);
       const bool zero = tail && tok0 + t >= L;
       if constexpr (kFp8) {
-        *reinterpret_cast<half8_t*>(vs + vlds[j]) = zero ? half8_t{} : widen_lo(vc[j]);
-        *reinterpret_cast<half8_t*>(vs + vlds[j] + 8) = zero ? half8_t{} : widen_hi(vc[j]);
+        *reinterpret_cast<half8_t*>(vs + vlds[j]) = zero ? half8_t{} : widen_lo(vr[j]);
+        *reinterpret_cast<half8_t*>(vs + vlds[j] + 8) = zero ? half8_t{} : widen_hi(vr[j]);
       } else {
-        *reinterpret_cast<half8_t*>(vs + vlds[j]) = zero ? half8_t{} : vc[j];
+        *reinterpret_cast<half8_t*>(vs + vlds[j]) = zero ? half8_t{} : vr[j];
       }
     }
     // S^T of the block
@@ -701,11 +680,13 @@ __global__ __launch_bounds__(kThreads) void decode_gqa_kernel(const DecodeArgs a
     for (int ks = 0; ks < KS; ++ks) {
       half8_t ka;
       if constexpr (kFp8)
-        ka = (ks & 1) ? widen_hi(kc[ks >> 1]) : widen_lo(kc[ks >> 1]);
+        ka = (ks & 1) ? widen_hi(kr[ks >> 1]) : widen_lo(kr[ks >> 1]);
       else
-        ka = kc[ks];
+        ka = kr[ks];
       sacc = __builtin_amdgcn_mfma_f32_16x16x32_f16(ka, qb[ks], sacc, 0, 0, 0);
     }
+    // the block's registers have been read: with two blocks ahead, block jb + 2 goes there
+    if (kTwoAhead && jb + 2 < blk_end) request(kr, vr, jb + 2);
     // mask, column max over the block's 16 tokens, lazy rescale
     float mloc = neg_inf();
 #pragma unroll
@@ -745,18 +726,23 @@ __global__ __launch_bounds__(kThreads) void decode_gqa_kernel(const DecodeArgs a
     }
     // the next block's V overwrites the stage only after these reads have returned
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-    if constexpr (AHEAD == 2) {
-#pragma unroll
-      for (int j = 0; j < KL; ++j) {
-        kc[j] = k1[j];
-        k1[j] = kn[j];
-      }
-#pragma unroll
-      for (int j = 0; j < VL; ++j) {
-        vc[j] = v1[j];
-        v1[j] = vn[j];
-      }
-    } else {
+  };
+  if constexpr (kTwoAhead) {
+    Raw k0[KL], v0[VL], k1[KL], v1[VL];  // even and odd blocks of the pass
+    request(k0, v0, blk_begin);
+    if (blk_begin + 1 < blk_end) request(k1, v1, blk_begin + 1);
+    for (int jb = blk_begin; jb < blk_end && !bad_table; jb += 2) {
+      consume(k0, v0, jb);
+      if (jb + 1 >= blk_end || bad_table) break;
+      consume(k1, v1, jb + 1);
+    }
+  } else {
+    Raw kc[KL], vc[VL];
+    request(kc, vc, blk_begin);
+    for (int jb = blk_begin; jb < blk_end && !bad_table; ++jb) {
+      Raw kn[KL], vn[VL];
+      if (jb + 1 < blk_end) request(kn, vn, jb + 1);
+      consume(kc, vc, jb);
 #pragma unroll
       for (int j = 0; j < KL; ++j) kc[j] = kn[j];
 #pragma unroll
