@@ -174,6 +174,39 @@ def test_decode_fp8_past_64_blocks_per_partition(D, G):
             check_attention(host(out), want, f"fp8 D{D} G{G} ps{ps} flags{flags}")
 
 
+@pytest.mark.parametrize("G", [2, 4])
+def test_decode_fp8_grouped_bad_entry_at_each_position(G):
+    """The grouped-query kernel keeps two blocks of E4M3 codes in flight, the block after
+    next requested into the registers of the block just read. A table entry outside the pool
+    at any position of a pass (the first block, the second, one requested two ahead, the
+    entries around the reload of the table vector every 64 blocks, the last block) turns
+    exactly its sequence's rows into NaN; every other row matches the oracle, with one
+    partition per sequence and with 32-block partitions."""
+    hkv = 2
+    lens = [16, 32, 48, 112, 2100, 2100, 2100, 2100, 2100, 2100, 40]  # 1, 2, 3, 7 and 132 blocks
+    inp = workloads.decode_case(300 + G, lens, hkv * G, hkv, 128, append=False)
+    ks, vs = 0.03, 0.02
+    pool = quantized_pool(inp, ks, vs)
+    q, bt, L = inp.decode_part()
+    want = oracle_decode_fp8(inp, pool, ks, vs)
+    bad_at = {1: 1, 2: 2, 3: 6, 4: 0, 5: 2, 6: 63, 7: 64, 8: 65, 9: 131}  # sequence: block
+    bt_bad = bt.copy()
+    for b, j in bad_at.items():
+        bt_bad[b, j] = inp.num_blocks + 7 if b % 2 else -1
+    good = [b for b in range(len(lens)) if b not in bad_at]
+    for ps in (4096, 512):
+        note(f"fp8 grouped bad entry G={G} ps={ps}")
+        out = torch.empty(q.shape, dtype=torch.float16, device="cuda")
+        ws = torch.empty(pkv.pa_decode_workspace_bytes(len(L), hkv * G, int(L.max()), ps, 128),
+                         dtype=torch.uint8, device="cuda")
+        pkv.pa_decode_fp8(out, dev(q), dev(pool), dev(bt_bad), dev(L), int(L.max()), inp.scale,
+                          ks, vs, ps, ws, pkv.PA_DECODE_KV_STREAM)
+        got = host(out)
+        for b in bad_at:
+            assert np.isnan(got[b]).all(), (ps, b)
+        check_attention(got[good], want[good], f"fp8 grouped bad entries G{G} ps{ps}")
+
+
 def test_decode_fp8_bad_rows_are_nan():
     inp = workloads.decode_case(96, [40, 50, 60], 4, 4, 64, append=False)
     pool = quantized_pool(inp, 1.0, 1.0)
@@ -266,6 +299,37 @@ def test_shared_prefix_fp8_prefix_groups():
     pairs = [(int(b), int(h)) for b, h in zip(rng.integers(0, 256, 200), rng.integers(0, 32, 200))]
     want = oracle.decode_rows(q, fp8.dequantize_pool(pool, 1.0, 1.0), bt, L, inp.scale, pairs)
     check_attention(np.stack([got[b, h] for b, h in pairs]), want, "shared fp8 prefix-groups")
+
+
+def test_shared_prefix_fp8_bad_entries():
+    """Shared-prefix decode over an E4M3 cache with two blocks in flight per wave: a prefix
+    entry outside the pool in the table of a group's first sequence (the table the prefix
+    pass reads) turns the whole group's rows into NaN; own-token entries outside the pool
+    (first, second and last own block) turn their sequence's rows into NaN; every other row
+    matches the oracle, with one and with several prefix partitions."""
+    priv = [3, 40, 200, 170, 90, 0, 33, 250, 17, 64, 150, 100]
+    inp = workloads.prefix_shared_case(320, 3, 4, 6, priv, 16, 4, 128)
+    ks, vs = 0.03, 0.02
+    pool = quantized_pool(inp, ks, vs)
+    q, bt, L = inp.decode_part()
+    want = oracle_decode_fp8(inp, pool, ks, vs)
+    bt_bad = bt.copy()
+    bt_bad[4, 3] = inp.num_blocks + 1  # group 1's prefix, as its first sequence's table holds it
+    bt_bad[2, 6] = -1                  # first own block (the prefix is 6 blocks)
+    bt_bad[3, 7] = inp.num_blocks      # second own block
+    bt_bad[11, 12] = -5                # last own block (100 own tokens: blocks 6 .. 12)
+    bad = np.zeros(12, bool)
+    bad[[2, 3, 4, 5, 6, 7, 11]] = True
+    gs = dev(np.array([0, 4, 8, 12], np.int32))
+    pl = dev(np.full(3, 96, np.int32))
+    for ps in (512, 32):
+        note(f"shared prefix fp8 bad entries ps={ps}")
+        out = torch.full(q.shape, 0.0, dtype=torch.float16, device="cuda")
+        pkv.pa_decode_shared_prefix_fp8(out, dev(q), dev(pool), dev(bt_bad), dev(L), int(L.max()),
+                                        gs, pl, 4, 96, inp.scale, ks, vs, ps)
+        got = host(out)
+        assert np.isnan(got[bad]).all(), ps
+        check_attention(got[~bad], want[~bad], f"shared fp8 bad entries ps{ps}")
 
 
 @pytest.mark.parametrize("D", [64, 128])
