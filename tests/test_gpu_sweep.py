@@ -1,8 +1,9 @@
 """Seeded random sweep of the attention entry points against the oracle: each case draws its
 own head size, query-group size, KV-head count, lengths and partition size (and for
 prefill the requests' priors and chunks; for shared-prefix decode the groups and their
-declared prefixes), so that combinations the hand-written cases do not list are checked
-too. Every case is small enough for the fp64 oracle to finish in a few seconds at most."""
+declared prefixes; the same over an E4M3 pool), so that combinations the hand-written
+cases do not list are checked too. Every case is small enough for the fp64 oracle to
+finish in a few seconds at most."""
 
 import numpy as np
 import pytest
@@ -116,6 +117,40 @@ def test_shared_prefix_sweep(seed):
     pkv.pa_decode_shared_prefix(out, dev(q), dev(inp.pool), dev(bt), dev(L), int(max(L.max(), mp)),
                                 dev(gs), dev(pl), int(np.diff(gs).max()), mp, inp.scale, ps)
     check_attention(host(out), oracle.decode(q, inp.pool, bt, L, inp.scale), f"shared sweep {seed}")
+
+
+@pytest.mark.parametrize("seed", range(8))
+def test_shared_prefix_fp8_sweep(seed):
+    """Shared-prefix decode over an E4M3 pool (two blocks of codes in flight per wave), drawn
+    as above with longer own tails and random scales, against the oracle on the dequantized
+    pool."""
+    rng = np.random.default_rng(5000 + seed)
+    D, G, hkv = heads(rng)
+    groups = int(rng.integers(1, 5))
+    samples = int(rng.integers(1, 10))
+    pblocks = int(rng.integers(1, 6))
+    priv = rng.integers(0, 150, groups * samples)
+    inp = workloads.prefix_shared_case(5000 + seed, groups, samples, pblocks, priv, hkv * G, hkv, D)
+    starts = [0]
+    for g in range(groups):
+        cuts = sorted(rng.choice(np.arange(1, samples), size=min(int(rng.integers(0, 3)), samples - 1),
+                                 replace=False).tolist()) if samples > 1 else []
+        starts += [g * samples + c for c in cuts] + [(g + 1) * samples]
+    gs = np.asarray(starts, np.int32)
+    pl = (rng.integers(0, pblocks + 1, len(gs) - 1) * 16).astype(np.int32)
+    ps = 16 * int(rng.integers(1, 40))
+    ks, vs = float(rng.uniform(0.005, 0.05)), float(rng.uniform(0.005, 0.05))
+    pool = np.concatenate([fp8.quantize(inp.pool[:, :, 0:1], ks), fp8.quantize(inp.pool[:, :, 1:2], vs)],
+                          axis=2)
+    note(f"shared-prefix fp8 sweep seed={seed} D={D} G={G} Hkv={hkv} groups={groups}x{samples} "
+         f"declared={np.diff(gs).tolist()} prefixes={pl.tolist()} ps={ps}")
+    q, bt, L = inp.decode_part()
+    out = torch.full(q.shape, float("nan"), dtype=torch.float16, device="cuda")
+    mp = int(pl.max())
+    pkv.pa_decode_shared_prefix_fp8(out, dev(q), dev(pool), dev(bt), dev(L), int(max(L.max(), mp)), dev(gs),
+                                    dev(pl), int(np.diff(gs).max()), mp, inp.scale, ks, vs, ps)
+    check_attention(host(out), oracle.decode(q, fp8.dequantize_pool(pool, ks, vs), bt, L, inp.scale),
+                    f"shared fp8 sweep {seed}")
 
 
 @pytest.mark.parametrize("seed", range(12))
