@@ -209,22 +209,27 @@ __device__ __forceinline__ void finish_partition(const DecodeArgs& a, int b, int
     }
     return;
   }
+  // over the wave's rows of lanes (lane L and L ^ o for o = LPT .. 32)
+  auto row_max = [](float x) {
+    if constexpr (LPT <= 4) x = max_xor<4>(x);
+    if constexpr (LPT <= 8) x = max_xor<8>(x);
+    if constexpr (LPT <= 16) x = max_xor<16>(x);
+    return max_xor<32>(x);
+  };
+  auto row_sum = [](float x) {
+    if constexpr (LPT <= 4) x = sum_xor<4>(x);
+    if constexpr (LPT <= 8) x = sum_xor<8>(x);
+    if constexpr (LPT <= 16) x = sum_xor<16>(x);
+    return sum_xor<32>(x);
+  };
+  static_assert(LPT >= 4 && LPT <= 32, "rows of 4 to 32 lanes");
 #pragma unroll
   for (int g = 0; g < G; ++g) {
-    float M = m[g];
-#pragma unroll
-    for (int o = LPT; o < kWave; o <<= 1) M = fmaxf(M, __shfl_xor(M, o, kWave));
+    const float M = row_max(m[g]);
     const float f = (m[g] == neg_inf()) ? 0.0f : fast_exp2(m[g] - M);
-    float lt = l[g] * f;
+    const float lt = row_sum(l[g] * f);
 #pragma unroll
-    for (int o = LPT; o < kWave; o <<= 1) lt += __shfl_xor(lt, o, kWave);
-#pragma unroll
-    for (int d = 0; d < EPL; ++d) {
-      float x = acc[g][d] * f;
-#pragma unroll
-      for (int o = LPT; o < kWave; o <<= 1) x += __shfl_xor(x, o, kWave);
-      acc[g][d] = x;
-    }
+    for (int d = 0; d < EPL; ++d) acc[g][d] = row_sum(acc[g][d] * f);
     if (row == 0) {
       const int64_t h = (int64_t)kvh * G + g;
       const int64_t bh = (int64_t)b * a.num_q_heads + h;

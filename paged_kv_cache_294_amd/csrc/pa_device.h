@@ -122,14 +122,36 @@ __device__ __forceinline__ float dot8(half8_t a, half8_t b, float acc) {
   return acc;
 }
 
-__device__ __forceinline__ float wave_max(float x) {
-  for (int o = 32; o >= 1; o >>= 1) x = fmaxf(x, __shfl_xor(x, o, kWave));
-  return x;
+// Max and sum of x over lanes L and L ^ O of a wave. For O = 16 and 32 gfx950's
+// v_permlane16_swap / v_permlane32_swap exchange rows of 16 lanes (halves of 32 lanes)
+// between two registers inside the vector ALU, without the LDS round trip of ds_bpermute:
+// with x in both operands, the two results hold x of the lane and x of its partner, in an
+// order that depends on the lane, which max and sum do not see (both are commutative, so
+// every lane of a pair gets the same bits as with a shuffle).
+template <int O>
+__device__ __forceinline__ float max_xor(float x) {
+  if constexpr (O == 16) {
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  } else if constexpr (O == 32) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  } else {
+    return fmaxf(x, __shfl_xor(x, O, kWave));
+  }
 }
 
-__device__ __forceinline__ float wave_sum(float x) {
-  for (int o = 32; o >= 1; o >>= 1) x += __shfl_xor(x, o, kWave);
-  return x;
+template <int O>
+__device__ __forceinline__ float sum_xor(float x) {
+  if constexpr (O == 16) {
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+  } else if constexpr (O == 32) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+  } else {
+    return x + __shfl_xor(x, O, kWave);
+  }
 }
 
 __device__ __forceinline__ float neg_inf() { return -__builtin_inff(); }

@@ -547,7 +547,7 @@ __global__ __launch_bounds__(kThreads, 3) void prefill_kernel(const PrefillArgs 
       // them (so both keep the same reference max)
       if (__builtin_amdgcn_ballot_w64(ms > m + kRescaleSlack)) {
         keep_branch();
-        const float mrow = fmaxf(ms, __shfl_xor(ms, 32, kWave));
+        const float mrow = max_xor<32>(ms);
         const float mnew = mrow > m + kRescaleSlack ? mrow : m;
         // 0 when m was -inf; 1 when the row's max did not move, also when it stays at -inf
         // (a row that sees none of this piece's tokens while other rows of the wave do:
@@ -598,7 +598,7 @@ __global__ __launch_bounds__(kThreads, 3) void prefill_kernel(const PrefillArgs 
   if (it < s1) stage(R0{}, it++);
   if (it < s1) stage(R1{}, it++);
 
-  l += __shfl_xor(l, 32, kWave);
+  l = sum_xor<32>(l);
   const bool bad_table = __builtin_amdgcn_ballot_w64(bad_lanes) != 0;
   if (split) {
     // fp32 partials of this piece for the merge kernel, in lane order: o (not normalised),
