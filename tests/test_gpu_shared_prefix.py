@@ -117,3 +117,19 @@ def test_kv_heads_not_a_multiple_of_four(hkv, G):
     for ps in (16, 512):
         note(f"shared prefix Hkv={hkv} G={G} ps={ps}")
         check_attention(run(inp, [0, 4, 8, 12], [48, 48, 48], ps), exp, f"shared Hkv{hkv} G{G} ps{ps}")
+
+
+@pytest.mark.parametrize("G", [1, 4])
+def test_empty_groups_between_groups(G):
+    """group_start is non-decreasing, so a group may be empty (its start equals the next
+    one's); the empty groups, whatever prefix they declare, contribute nothing, and every
+    row equals plain decode's (the oracle's)."""
+    rng = np.random.default_rng(250 + G)
+    priv = rng.integers(0, 90, 12)
+    inp = workloads.prefix_shared_case(250 + G, 3, 4, 3, priv, 4 * G, 4, 128)
+    gs = [0, 0, 4, 4, 4, 8, 12, 12]          # empty groups at 0, 2, 3 and 6
+    pl = [48, 48, 32, 16, 48, 48, 0]
+    exp = oracle_out(inp)
+    for ps in (16, 512):
+        note(f"shared prefix empty groups G={G} ps={ps}")
+        check_attention(run(inp, gs, pl, ps), exp, f"shared empty groups G{G} ps{ps}")
